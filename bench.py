@@ -1,0 +1,204 @@
+"""Benchmark of the low-bit dequant-GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over the DiT attention-projection
+workload (W 3072x3072 bf16 ~ N(0, 0.02^2), 4-bit, group 128):
+  1. quantize + pack W                      (ddg_quantize_pack)
+  2. Y = X W_hat^T for X of 4096 tokens    (ddg_dequant_gemm, bf16 out)
+  3. Y = X W_hat^T for X of 16 tokens      (ddg_dequant_gemm, bf16 out)
+Inputs are resident in HBM before timing.  Each step uses other copies of
+the weights (round robin over enough copies to exceed 1 GiB, 4x the 256 MB
+last-level cache), so the M=16 product streams its packed weights from HBM.
+
+value = dequant-GEMM TFLOP/s at M=4096 (2*M*N*K / mean kernel time, HIP
+events on the launch stream); the JSON line also carries the M=16 packed-
+weight GB/s, the quantize/pack GB/s, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+M_BIG, M_SMALL, N, K, BITS = 4096, 16, 3072, 3072, 4
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the oracle's GEMM sample time")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, budget_s):
+    """The oracle as it stands on the host: quantize + pack + dequantize the
+    whole weight, then the float64 product over row chunks of X until the time
+    budget is used.  Rate = 2 * rows * N * K / product time."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:                                   # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    packed, scales, _ = O.quantize_pack(w, BITS)
+    t_q = time.perf_counter() - t0
+    w16 = O.dequant_from_packed(packed, scales, BITS, N, K)
+    rows, t_g = 0, 0.0
+    chunk = 256
+    while rows < x.shape[0] and t_g < budget_s:
+        t1 = time.perf_counter()
+        O.gemm_ref(x[rows:rows + chunk], w16)
+        t_g += time.perf_counter() - t1
+        rows += chunk
+    q_bytes = 2 * N * K + N * K * BITS // 8 + N * K // 32
+    return {
+        "value": round(2.0 * rows * N * K / t_g / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 product of {rows} of the 4096 token rows with the oracle's "
+                   f"dequantized 3072x3072 weight ({t_g:.1f} s); oracle quantize+pack of the "
+                   f"whole weight {t_q:.2f} s = {q_bytes / t_q / 1e9:.3f} GB/s (1 thread)"),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the product "
+              "shards along the output dimension with no exchange, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    if not os.path.exists(api.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    api.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c = synth.config2(m=M_BIG)
+    w_np, x_np = c["w"], c["x"]
+    w_bytes = N * K * 2
+    p_bytes = N * K * BITS // 8
+    s_bytes = N * K // 128 * 4
+    n_copies = max(2, -(-ROTATE_BYTES // (w_bytes + p_bytes + s_bytes)))
+    w0 = torch.from_numpy(w_np).to(dev, torch.bfloat16)
+    ws = [w0.clone() for _ in range(n_copies)]
+    qws = [api.quantize_pack(wc, BITS) for wc in ws]
+    x_big = torch.from_numpy(x_np).to(dev, torch.bfloat16)
+    x_small = x_big[:M_SMALL].contiguous()
+    y_big = torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev)
+    y_small = torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev)
+
+    def quantize_into(i):
+        q = qws[i]
+        st = api.load_library().ddg_quantize_pack(
+            ws[i].data_ptr(), api.DDG_BF16, N, K, BITS, q.packed.data_ptr(),
+            q.scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise api.DDGError(st, "ddg_quantize_pack")
+
+    ev = {k: [] for k in ("q0", "q1", "g0", "g1", "s0", "s1")}
+
+    def step(i, record):
+        j = i % n_copies
+        far = (i + n_copies // 2) % n_copies        # packed weights not touched for a while
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
+        if record: e[0].record()
+        quantize_into(j)
+        if record: e[1].record(); e[2].record()
+        api.dequant_gemm(x_big, qws[j], out=y_big)
+        if record: e[3].record(); e[4].record()
+        api.dequant_gemm(x_small, qws[far], out=y_small)
+        if record:
+            e[5].record()
+            for k, evt in zip(("q0", "q1", "g0", "g1", "s0", "s1"), e):
+                ev[k].append(evt)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def mean_ms(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+
+    t_q, t_g, t_s = mean_ms("q0", "q1"), mean_ms("g0", "g1"), mean_ms("s0", "s1")
+    flops = 2.0 * M_BIG * N * K
+    tflops = flops / (t_g * 1e-3) / 1e12
+    gbps_small = (p_bytes + s_bytes) / (t_s * 1e-3) / 1e9
+    gbps_q = (w_bytes + p_bytes + s_bytes) / (t_q * 1e-3) / 1e9
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+
+    out = {
+        "metric": "dequant-GEMM TFLOP/s (M=4096) + packed-weight GB/s (M=16), % of roofline",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DiT attention projection: W 3072x3072 bf16 ~N(0,0.02^2), 4-bit per-group(128) "
+                        "fp32 scales, X 4096x3072 bf16 ~N(0,1) (+ its first 16 rows)",
+            "m": M_BIG, "m_small": M_SMALL, "n": N, "k": K, "bits": BITS, "y_dtype": "bf16",
+            "weight_copies_rotated": n_copies,
+        },
+        "kernels_ms": {"quantize_pack": round(t_q, 5), "dequant_gemm_m4096": round(t_g, 5),
+                       "dequant_gemm_m16": round(t_s, 5)},
+        "m16_packed_weight_GBps": round(gbps_small, 2),
+        "m16_frac_of_hbm_peak": round(gbps_small / PEAK_HBM_GBPS, 4),
+        "quantize_pack_GBps": round(gbps_q, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w_np, x_np, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

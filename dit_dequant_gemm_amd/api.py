@@ -1,0 +1,227 @@
+"""Python binding of libddg.so (ctypes).  Argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of
+the computation runs in the library's gfx950 kernels.  When the shared
+library is missing or cannot be loaded every call raises ``RuntimeError``:
+there is no CPU or PyTorch fallback.
+
+The record mirrors the stored format of the Wan-Dancer-14B quantization
+report (§3.3): ``{name}_packed`` (uint8), ``{name}_scales`` (float32 per
+128-group), ``{name}_bw`` (int8 bit width) and ``{name}_nin`` (int32 padded
+input dimension).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+GROUP = 128
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libddg.so")
+_LIB: Optional[ctypes.CDLL] = None
+
+DDG_BF16, DDG_F32 = 0, 1
+
+# entry point -> (restype, argtypes)
+_c_i64, _c_int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "ddg_version": (_c_int, []),
+    "ddg_status_string": (ctypes.c_char_p, [_c_int]),
+    "ddg_packed_bytes": (_c_int, [_c_i64, _c_i64, _c_int, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64)]),
+    "ddg_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
+    "ddg_dequantize": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp]),
+    "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
+    "ddg_lowrank_workspace_bytes": (_c_int, [_c_i64, _c_int, ctypes.POINTER(_sz)]),
+    "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
+                                        _c_int, _vp, _c_int, _vp, _sz, _vp]),
+}
+
+
+class DDGError(RuntimeError):
+    """A libddg entry point returned a negative status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libddg.so (once).  Raises RuntimeError when it is missing."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libddg.so not found at {p}; build it with "
+                           "`python -m dit_dequant_gemm_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ddg_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DDGError(status, where)
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_sizes(n: int, k: int, bits: int):
+    """(packed bytes, number of scales) of an n x k weight at `bits`."""
+    pb, ns = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().ddg_packed_bytes(n, k, bits, ctypes.byref(pb), ctypes.byref(ns)),
+           "ddg_packed_bytes")
+    return pb.value, ns.value
+
+
+@dataclass
+class QWeight:
+    """Quantized weight record: packed codes, per-group scales, bit width,
+    padded input dimension (``k``) and the original input dimension."""
+    packed: torch.Tensor      # uint8, n*k*bits/8
+    scales: torch.Tensor      # float32, (n, k/128)
+    bits: int
+    n: int
+    k: int                    # padded input dimension (multiple of 128)
+    orig_in: int
+
+    def state_dict(self, prefix: str) -> dict:
+        return {
+            f"{prefix}_packed": self.packed,
+            f"{prefix}_scales": self.scales,
+            f"{prefix}_bw": torch.tensor(self.bits, dtype=torch.int8),
+            f"{prefix}_nin": torch.tensor(self.k, dtype=torch.int32),
+        }
+
+    @classmethod
+    def from_state_dict(cls, sd: dict, prefix: str, orig_in: Optional[int] = None,
+                        device="cuda") -> "QWeight":
+        bits = int(sd[f"{prefix}_bw"])
+        k = int(sd[f"{prefix}_nin"])
+        scales = sd[f"{prefix}_scales"].to(device=device, dtype=torch.float32).contiguous()
+        n = scales.numel() // (k // GROUP)
+        packed = sd[f"{prefix}_packed"].to(device=device, dtype=torch.uint8).contiguous()
+        return cls(packed, scales.view(n, k // GROUP), bits, n, k, orig_in or k)
+
+
+def quantize_pack(w: torch.Tensor, bits: int) -> QWeight:
+    """Quantize an (out x in) bf16/float32 GPU weight per 128-group and pack it."""
+    _require_cuda(w, "w")
+    if w.dim() != 2 or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be a 2-D bf16 or float32 tensor")
+    n, orig_in = w.shape
+    k = -(-orig_in // GROUP) * GROUP
+    if k != orig_in:                      # zero-pad the input dimension (record's _nin)
+        w = torch.nn.functional.pad(w, (0, k - orig_in)).contiguous()
+    pb, ns = packed_sizes(n, k, bits)
+    packed = torch.empty(pb, dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // GROUP), dtype=torch.float32, device=w.device)
+    lib = load_library()
+    _check(lib.ddg_quantize_pack(w.data_ptr(), DDG_F32 if w.dtype == torch.float32 else DDG_BF16,
+                                 n, k, bits, packed.data_ptr(), scales.data_ptr(),
+                                 _stream_ptr(w.device)), "ddg_quantize_pack")
+    return QWeight(packed, scales, bits, n, k, orig_in)
+
+
+def dequantize(qw: QWeight) -> torch.Tensor:
+    """Dense bf16 w_hat (n x padded in)."""
+    out = torch.empty((qw.n, qw.k), dtype=torch.bfloat16, device=qw.packed.device)
+    _check(load_library().ddg_dequantize(qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
+                                         qw.n, qw.k, out.data_ptr(),
+                                         _stream_ptr(qw.packed.device)), "ddg_dequantize")
+    return out
+
+
+def _prep_x(x: torch.Tensor, qw: QWeight) -> torch.Tensor:
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    if x.shape[1] == qw.k:
+        return x
+    if x.shape[1] != qw.orig_in:
+        raise ValueError(f"x has {x.shape[1]} inputs, weight expects {qw.orig_in}")
+    return torch.nn.functional.pad(x, (0, qw.k - qw.orig_in)).contiguous()
+
+
+def _out(x: torch.Tensor, n: int, out_dtype, out):
+    if out is None:
+        return torch.empty((x.shape[0], n), dtype=out_dtype, device=x.device)
+    _require_cuda(out, "out")
+    if out.shape != (x.shape[0], n) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out has the wrong shape or dtype")
+    return out
+
+
+def dequant_gemm(x: torch.Tensor, qw: QWeight, out_dtype=torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X @ w_hat^T with on-the-fly dequantization."""
+    x = _prep_x(x, qw)
+    y = _out(x, qw.n, out_dtype, out)
+    _check(load_library().ddg_dequant_gemm(
+        x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
+        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
+        _stream_ptr(x.device)), "ddg_dequant_gemm")
+    return y
+
+
+def lowrank_workspace_bytes(m: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load_library().ddg_lowrank_workspace_bytes(m, r, ctypes.byref(b)),
+           "ddg_lowrank_workspace_bytes")
+    return b.value
+
+
+def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
+                       lora_up: torch.Tensor, out_dtype=torch.bfloat16,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X @ w_hat^T + bf16(X @ L1) @ L2 with lora_down = L1^T (r x in) and
+    lora_up = L2^T (out x r), both bf16."""
+    x = _prep_x(x, qw)
+    for t, name in ((lora_down, "lora_down"), (lora_up, "lora_up")):
+        _require_cuda(t, name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    r = lora_down.shape[0]
+    if lora_down.shape[1] != qw.k:
+        if lora_down.shape[1] != qw.orig_in:
+            raise ValueError("lora_down has the wrong input dimension")
+        lora_down = torch.nn.functional.pad(lora_down, (0, qw.k - qw.orig_in)).contiguous()
+    if lora_up.shape != (qw.n, r):
+        raise ValueError("lora_up must be (out x r)")
+    y = _out(x, qw.n, out_dtype, out)
+    need = lowrank_workspace_bytes(x.shape[0], r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(load_library().ddg_lowrank_fused_gemm(
+        x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
+        qw.n, lora_down.data_ptr(), lora_up.data_ptr(), r, y.data_ptr(),
+        DDG_F32 if y.dtype == torch.float32 else DDG_BF16, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(x.device)),
+        "ddg_lowrank_fused_gemm")
+    return y

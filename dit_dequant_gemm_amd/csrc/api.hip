@@ -1,0 +1,235 @@
+// C ABI of libddg (declared in include/ddg.h): argument validation on the
+// host, kernel choice, launch.  No allocation, no synchronization.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/ddg.h"
+#include "ddg_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647;     // M, N, K fit a signed 32-bit int
+constexpr int kMaxDevices = 64;
+
+// Per-device facts cached on first use: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_dev_ok[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool bits_ok(int bits) { return bits >= 3 && bits <= 7; }
+
+bool k_ok(int64_t k) { return k > 0 && k <= kMaxDim && k % DDG_GROUP == 0; }
+
+// a * b without overflow past 2^62 (byte counts stay well inside int64).
+bool mul_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && (a == 0 || b <= (INT64_C(1) << 62) / a); }
+
+// Current device: gfx950 check and compute-unit count.
+int device_info(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DDG_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DDG_ERR_UNSUPPORTED;
+  int ok = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (ok == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DDG_ERR_HIP;
+    const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    ok = is950 ? 1 : -1;
+    g_dev_ok[dev].store(ok, std::memory_order_release);
+  }
+  if (ok < 0) return DDG_ERR_UNSUPPORTED;
+  *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return DDG_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DDG_OK : DDG_ERR_HIP; }
+
+template <template <int> class F, typename... A>
+hipError_t by_bits(int bits, A&&... args) {
+  switch (bits) {
+    case 3: return F<3>::run(args...);
+    case 4: return F<4>::run(args...);
+    case 5: return F<5>::run(args...);
+    case 6: return F<6>::run(args...);
+    case 7: return F<7>::run(args...);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int B>
+struct QuantizeF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_quantize_pack<B>(a...); }
+};
+template <int B>
+struct DequantizeF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_dequantize<B>(a...); }
+};
+template <int B>
+struct LargeF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_large<B>(a...); }
+};
+template <int B>
+struct SmallF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_small<B>(a...); }
+};
+
+// Validation shared by the two GEMM entry points.
+int check_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed, const float* scales,
+               int bits, int64_t n, const void* y, int y_dtype) {
+  if (!bits_ok(bits) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32)) return DDG_ERR_ARG;
+  if (m < 0 || m > kMaxDim || !k_ok(k) || n <= 0 || n > kMaxDim || n % 16) return DDG_ERR_SHAPE;
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!x || !packed || !scales || !y) return DDG_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || !aligned(scales, 4))
+    return DDG_ERR_ALIGN;
+  return DDG_OK;
+}
+
+// Kernel choice for the product; fills a.tiles_* for the large kernel.
+hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t stream) {
+  if (a.m <= 64) {
+    const int rb = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
+    // widest column tile that still gives every compute unit a workgroup
+    int cb = 1;
+    if ((int64_t)a.n / 64 >= cus) cb = 4;
+    else if ((int64_t)a.n / 32 >= cus) cb = 2;
+    return by_bits<SmallF>(bits, a, rb, cb, stream);
+  }
+  // large kernel: 256-row tiles, 4 waves x (16*cb) columns; pick cb by the
+  // estimated time (rounds of workgroups x relative tile time).
+  const int64_t tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
+  int best_cb = 4;
+  double best = 1e300;
+  for (int cb : {4, 3, 2}) {
+    const int64_t tiles_n = (a.n + 64 * cb - 1) / (64 * cb);
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const double eff = cb == 4 ? 1.0 : (cb == 3 ? 0.97 : 0.9);
+    const double t = (double)rounds * cb / eff;
+    if (t < best - 1e-9) { best = t; best_cb = cb; }
+  }
+  a.tiles_m = (int)tiles_m;
+  a.tiles_n = (a.n + 64 * best_cb - 1) / (64 * best_cb);
+  if ((int64_t)a.tiles_m * a.tiles_n > kMaxDim) return hipErrorInvalidValue;
+  return by_bits<LargeF>(bits, a, best_cb, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ddg_version(void) { return DDG_VERSION; }
+
+const char* ddg_status_string(int status) {
+  switch (status) {
+    case DDG_OK: return "ok";
+    case DDG_ERR_ARG: return "invalid argument (null pointer, dtype or bit width)";
+    case DDG_ERR_SHAPE: return "invalid shape";
+    case DDG_ERR_ALIGN: return "misaligned pointer";
+    case DDG_ERR_WORKSPACE: return "workspace too small";
+    case DDG_ERR_HIP: return "HIP launch or query failed";
+    case DDG_ERR_UNSUPPORTED: return "current device is not gfx950";
+  }
+  return "unknown status";
+}
+
+int ddg_packed_bytes(int64_t n, int64_t k, int bits, int64_t* packed_bytes, int64_t* n_scales) {
+  if (!packed_bytes || !n_scales || !bits_ok(bits)) return DDG_ERR_ARG;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, bits)) return DDG_ERR_SHAPE;
+  *packed_bytes = n * k / 8 * bits;
+  *n_scales = n * (k / DDG_GROUP);
+  return DDG_OK;
+}
+
+int ddg_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int bits, uint8_t* packed,
+                      float* scales, hipStream_t stream) {
+  if (!bits_ok(bits) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32)) return DDG_ERR_ARG;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4)) return DDG_ERR_SHAPE;
+  if (n == 0) return DDG_OK;
+  if (!w || !packed || !scales) return DDG_ERR_ARG;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  const int64_t n_chunks = n * k / 32;
+  return hip_status(by_bits<QuantizeF>(bits, w, w_dtype == DDG_F32, n_chunks,
+                                       reinterpret_cast<uint32_t*>(packed), scales, stream));
+}
+
+int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t n, int64_t k,
+                   void* w_out, hipStream_t stream) {
+  if (!bits_ok(bits)) return DDG_ERR_ARG;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 2)) return DDG_ERR_SHAPE;
+  if (n == 0) return DDG_OK;
+  if (!packed || !scales || !w_out) return DDG_ERR_ARG;
+  if (!aligned(packed, 16) || !aligned(w_out, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(by_bits<DequantizeF>(bits, packed, scales, n * k / 32, w_out, stream));
+}
+
+int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                     const float* scales, int bits, int64_t n, void* y, int y_dtype,
+                     hipStream_t stream) {
+  if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
+  if (m == 0) return DDG_OK;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  ddg::GemmArgs a{};
+  a.x = static_cast<const __bf16*>(x);
+  a.packed = packed;
+  a.scales = scales;
+  a.y = y;
+  a.t = nullptr;
+  a.lora_up = nullptr;
+  a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = 0;
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return hip_status(launch_product(a, bits, cus, stream));
+}
+
+int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes) {
+  if (!bytes) return DDG_ERR_ARG;
+  if (m < 0 || m > kMaxDim || r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  const int64_t raw = m * r * 2;
+  *bytes = (size_t)((raw + 255) / 256 * 256);
+  return DDG_OK;
+}
+
+int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                           const float* scales, int bits, int64_t n, const void* lora_down,
+                           const void* lora_up, int r, void* y, int y_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
+  if (r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!lora_down || !lora_up || !workspace) return DDG_ERR_ARG;
+  if (!aligned(lora_down, 16) || !aligned(lora_up, 16) || !aligned(workspace, 16))
+    return DDG_ERR_ALIGN;
+  size_t need = 0;
+  ddg_lowrank_workspace_bytes(m, r, &need);
+  if (workspace_bytes < need) return DDG_ERR_WORKSPACE;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  __bf16* t = static_cast<__bf16*>(workspace);
+  if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
+                                           static_cast<const __bf16*>(lora_down), t, (int)m,
+                                           (int)k, r, stream))
+    return hip_status(e);
+  ddg::GemmArgs a{};
+  a.x = static_cast<const __bf16*>(x);
+  a.packed = packed;
+  a.scales = scales;
+  a.y = y;
+  a.t = t;
+  a.lora_up = static_cast<const __bf16*>(lora_up);
+  a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = r;
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return hip_status(launch_product(a, bits, cus, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Device-side building blocks for the gfx950 kernels of libddg.
+//
+// Packed-code unpacking and dequantization (the Wan-Dancer-14B quantization
+// report, §3.3 packed layout and §3.4 dequantize):
+//   w_hat = bf16_rne(fl32((q_u - n_half) * scale)).
+//
+// A "chunk" is 32 consecutive codes of one row inside one 128-group.  With
+// the MSB-first bitstream a chunk occupies exactly `B` dwords and starts on a
+// dword boundary, for every bit width B in 3..7.  The GEMM kernels give each
+// lane one chunk per (column, group) so that all 32 codes share one scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ddg {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr int kGroup = 128;
+
+template <int B>
+struct Bits {
+  static constexpr int n_half = (1 << (B - 1)) - 1;     // largest |q|
+  static constexpr uint32_t mask = (1u << B) - 1;
+  // q + 64 = q_u + (64 - n_half): a byte in [1, 127] for every B <= 7, so that
+  // fma(q + 64, s, -64 s) = fl32(q * s) with one rounding (64 s is exact).
+  static constexpr uint32_t bias64 = 64u - (uint32_t)n_half;
+};
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fl32(q * s) given v = q + 64 as a float and ns64 = -64 * s.
+__device__ __forceinline__ float scale_code(float v, float s, float ns64) {
+  return __builtin_fmaf(v, s, ns64);
+}
+
+// Code I (0..31) of a chunk whose dwords were byte-swapped into `be`
+// (big-endian words: stream bit 32*j is the MSB of be[j]).
+template <int B>
+__device__ __forceinline__ uint32_t chunk_code(const uint32_t* be, int i) {
+  const int o = i * B, j = o >> 5, off = o & 31;
+  if (off + B <= 32) return (be[j] >> (32 - off - B)) & Bits<B>::mask;
+  return __builtin_amdgcn_alignbit(be[j], be[j + 1], 64 - off - B) & Bits<B>::mask;
+}
+
+// Dequantize codes 8*S .. 8*S+7 of a chunk into one MFMA operand (8 bf16,
+// element e = code 8*S+e).  `raw` holds the chunk's dwords as loaded
+// (little-endian), `be` the same dwords byte-swapped (unused for B == 4).
+template <int B, int S>
+__device__ __forceinline__ bf16x8 dequant8(const uint32_t* raw, const uint32_t* be, float s,
+                                           float ns64) {
+  u32x4 out;
+  if constexpr (B == 4) {
+    // Dword S holds codes 8S..8S+7; byte p holds code 8S+2p in its high
+    // nibble and 8S+2p+1 in its low nibble.
+    const uint32_t x = raw[S];
+    const uint32_t ev = ((x >> 4) & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
+    const uint32_t od = (x & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = (float)((ev >> (8 * p)) & 0xFFu);
+      const float b = (float)((od >> (8 * p)) & 0xFFu);
+      out[p] = pack_bf16x2(scale_code(a, s, ns64), scale_code(b, s, ns64));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t c0 = chunk_code<B>(be, 8 * S + 2 * p) + Bits<B>::bias64;
+      const uint32_t c1 = chunk_code<B>(be, 8 * S + 2 * p + 1) + Bits<B>::bias64;
+      out[p] = pack_bf16x2(scale_code((float)c0, s, ns64), scale_code((float)c1, s, ns64));
+    }
+  }
+  return __builtin_bit_cast(bf16x8, out);
+}
+
+template <int B>
+__device__ __forceinline__ void byteswap_chunk(const uint32_t* raw, uint32_t* be) {
+  if constexpr (B != 4) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) be[j] = __builtin_bswap32(raw[j]);
+  }
+}
+
+// Load the B dwords of one chunk (4-byte aligned; 16-byte aligned for B == 4).
+template <int B>
+__device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t* raw) {
+  if constexpr (B == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    raw[0] = v[0]; raw[1] = v[1]; raw[2] = v[2]; raw[3] = v[3];
+  } else if constexpr (B == 6) {
+    const u32x2* q = reinterpret_cast<const u32x2*>(p);   // chunk offsets are 8-byte aligned
+#pragma unroll
+    for (int j = 0; j < 3; ++j) { const u32x2 v = q[j]; raw[2 * j] = v[0]; raw[2 * j + 1] = v[1]; }
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+    for (int j = 0; j < B; ++j) raw[j] = q[j];
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+}  // namespace ddg

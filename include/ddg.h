@@ -1,0 +1,164 @@
+/*
+ * ddg.h -- C ABI of libddg.so: low-bit (3..7 bit) per-group weight
+ * quantization and the dequantize-on-the-fly GEMM of a diffusion-transformer
+ * linear layer, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [WDQ]  The Wan-Dancer-14B mixed-precision quantization report (mtrt.cn):
+ *          §3.1 per-group(128) symmetric quantization, §3.3 multi-bit packed
+ *          storage and the stored record (packed / scales / bit width / padded
+ *          input dimension), §3.4 GPU-native dequantize, §5.4 dequantize then
+ *          bf16 matmul.
+ *   [SVDQ] "SVDQuant：4-bit量化让扩散模型在消费级GPU上高效运行" (kongchang.com):
+ *          section "技术原理详解" (16-bit low-rank branch plus quantized residual).
+ *
+ * Conventions shared by every entry point:
+ *   - W is out x in = N x K, row-major; groups are 128 consecutive inputs of a
+ *     row ([WDQ] §3.1).  K must be a positive multiple of 128; a caller with
+ *     another input size zero-pads W and X to the next multiple of 128 (the
+ *     record's padded input dimension, [WDQ] §3.3).
+ *   - Quantizer ([WDQ] §3.1), all in IEEE float32:
+ *       a = max |w| over the group;  step = (2 * fl(a * 1.01f)) / (2^bits - 1);
+ *       q = clamp(round_half_even(fl(w / step)), -n_half, n_half),
+ *       n_half = 2^(bits-1) - 1;  code q_u = q + n_half in [0, 2^bits - 2];
+ *       scale = step.  An all-zero group gets q = 0 and scale 0.
+ *   - Packed layout ([WDQ] §3.3): the row-major codes form one continuous
+ *     bitstream, each code written with `bits` bits, most significant bit
+ *     first; stream bit 0 is the MSB of byte 0.  A row takes K*bits/8 bytes,
+ *     a group 16*bits bytes.  For bits = 4 the even-index code is the high
+ *     nibble.  Total N*K*bits/8 bytes.
+ *   - Scales: float32, N x (K/128), row-major.
+ *   - Dequantized weight fed to the matmul ([WDQ] §3.4, §5.4):
+ *       w_hat = bf16_round_nearest_even(fl32((q_u - n_half) * scale)).
+ *   - X is M x K bf16 row-major; Y is M x N row-major, bf16 or float32;
+ *     products accumulate in float32.  Y is overwritten, never accumulated.
+ *
+ * Memory, streams, errors:
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or synchronizes.  Buffers must not
+ *     overlap, except as stated.
+ *   - Every launch is asynchronous on `stream` (0 = the default stream).
+ *     Calls keep no mutable state between calls and may come from any thread.
+ *   - Return value: DDG_OK (0) or a negative ddg_status.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     launched and no memory is touched.  DDG_ERR_HIP means a launch failed
+ *     (the HIP error is left for hipGetLastError).
+ *   - Alignment: x, w, packed, y, lora_* and workspace must be 16-byte
+ *     aligned; scales 4-byte aligned.
+ */
+#ifndef DDG_H
+#define DDG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDG_GROUP 128      /* weights per scale ([WDQ] §3.1) */
+#define DDG_VERSION 1
+
+typedef enum ddg_dtype {
+  DDG_BF16 = 0,
+  DDG_F32 = 1
+} ddg_dtype;
+
+typedef enum ddg_status {
+  DDG_OK = 0,
+  DDG_ERR_ARG = -1,          /* null pointer, bad enum, bits outside 3..7   */
+  DDG_ERR_SHAPE = -2,        /* sizes not allowed (see each call)           */
+  DDG_ERR_ALIGN = -3,        /* pointer misaligned                          */
+  DDG_ERR_WORKSPACE = -4,    /* workspace smaller than required             */
+  DDG_ERR_HIP = -5,          /* a HIP launch or query failed                */
+  DDG_ERR_UNSUPPORTED = -6   /* no gfx950 device current                    */
+} ddg_status;
+
+/* Library version (DDG_VERSION). */
+int ddg_version(void);
+
+/* Text for a status code (static string, never NULL). */
+const char* ddg_status_string(int status);
+
+/*
+ * Sizes of the packed record for an N x K weight at `bits` ([WDQ] §3.3 table:
+ * 3 bit 8 weights -> 3 bytes, 4 bit 2 -> 1, 5 bit 8 -> 5, 6 bit 4 -> 3,
+ * 7 bit 8 -> 7).  Host-only, no device access.
+ *   packed_bytes <- N*K*bits/8,  n_scales <- N*K/128.
+ * Errors: DDG_ERR_ARG (null output, bits), DDG_ERR_SHAPE (n < 0, k not a
+ * positive multiple of 128, overflow).
+ */
+int ddg_packed_bytes(int64_t n, int64_t k, int bits, int64_t* packed_bytes,
+                     int64_t* n_scales);
+
+/*
+ * Quantize and pack ([WDQ] §3.1 quantizer, §3.3 packing).
+ *   w       N x K weights, bf16 or float32 (w_dtype), finite values.
+ *   packed  out: N*K*bits/8 bytes (layout above), fully written.
+ *   scales  out: N*(K/128) float32, fully written.
+ * Results are bit-exact: the arithmetic is the IEEE float32 sequence above
+ * (correctly rounded multiply and divide, no fused operations, subnormals
+ * kept).  n == 0 is a no-op.
+ * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (n < 0; k not a positive multiple of
+ * 128), DDG_ERR_ALIGN, DDG_ERR_HIP.
+ */
+int ddg_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
+                      uint8_t* packed, float* scales, hipStream_t stream);
+
+/*
+ * Dense dequantization ([WDQ] §3.4): w_out (N x K bf16) = w_hat for every
+ * weight.  For checking and for callers that want a dense copy; the GEMM
+ * below never materializes it.  n == 0 is a no-op.
+ * Errors: as ddg_quantize_pack.
+ */
+int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t n,
+                   int64_t k, void* w_out, hipStream_t stream);
+
+/*
+ * Y = X * w_hat^T ([WDQ] §3.4 + §5.4, dequantizing inside the GEMM).
+ *   x       M x K bf16.       packed/scales: the record of an N x K weight.
+ *   y       M x N, y_dtype (DDG_BF16 or DDG_F32), fully overwritten.
+ * Requirements: M >= 0 (M == 0 is a no-op), N a positive multiple of 16,
+ * K a positive multiple of 128, M, N <= 2^31 - 1.
+ * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP.
+ */
+int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                     const float* scales, int bits, int64_t n, void* y, int y_dtype,
+                     hipStream_t stream);
+
+/*
+ * Workspace bytes ddg_lowrank_fused_gemm needs for M rows and rank r
+ * (the M x r bf16 intermediate T, rounded up to 256 bytes).  Host-only.
+ * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m < 0, r outside 8..128 or not a
+ * multiple of 8).
+ */
+int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes);
+
+/*
+ * Y = X * w_hat^T + T * L2 with T = bf16(X * L1)  ([SVDQ] 技术原理详解: a
+ * 16-bit low-rank branch beside the quantized residual; the residual's record
+ * is packed/scales).  The low-rank factors are passed in the layout of linear
+ * weights (out x in):
+ *   lora_down  r x K bf16  = L1^T   (row j: the j-th input projection)
+ *   lora_up    N x r bf16  = L2^T   (row n: output n's branch weights)
+ * T is computed in float32 and rounded to bf16 once (the branch is a bf16
+ * product); the branch term T * L2 is summed into the same float32
+ * accumulator as the main product before y is written.
+ *   workspace  device scratch of at least ddg_lowrank_workspace_bytes(M, r)
+ *              bytes; its contents are scratch (no initial state needed).
+ * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0.
+ * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_WORKSPACE,
+ * DDG_ERR_HIP.
+ */
+int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                           const float* scales, int bits, int64_t n,
+                           const void* lora_down, const void* lora_up, int r,
+                           void* y, int y_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDG_H */

@@ -1,0 +1,156 @@
+"""The C ABI on the host (CPU only): the library loads, exports every entry
+point declared in include/ddg.h, and rejects bad arguments before any HIP
+call.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dit_dequant_gemm_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddg.h")
+
+OK, E_ARG, E_SHAPE, E_ALIGN, E_WS = 0, -1, -2, -3, -4
+FAKE = 0x10000          # aligned non-null address; never dereferenced by these calls
+MISALIGNED = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return api.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("ddg_quantize_pack", "ddg_dequant_gemm", "ddg_lowrank_fused_gemm",
+              "ddg_dequantize", "ddg_packed_bytes", "ddg_lowrank_workspace_bytes",
+              "ddg_status_string", "ddg_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(api.SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ddg_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.ddg_status_string(st)
+    assert lib.ddg_status_string(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("bits,ratio", [(3, 3 / 8), (4, 1 / 2), (5, 5 / 8), (6, 6 / 8), (7, 7 / 8)])
+def test_packed_bytes(lib, bits, ratio):
+    pb, ns = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.ddg_packed_bytes(5120, 5120, bits, ctypes.byref(pb), ctypes.byref(ns)) == OK
+    assert pb.value == int(5120 * 5120 * ratio) and ns.value == 204_800
+    assert lib.ddg_packed_bytes(16, 100, bits, ctypes.byref(pb), ctypes.byref(ns)) == E_SHAPE
+    assert lib.ddg_packed_bytes(16, 0, bits, ctypes.byref(pb), ctypes.byref(ns)) == E_SHAPE
+    assert lib.ddg_packed_bytes(-1, 128, bits, ctypes.byref(pb), ctypes.byref(ns)) == E_SHAPE
+    assert lib.ddg_packed_bytes(16, 128, bits, None, ctypes.byref(ns)) == E_ARG
+    assert lib.ddg_packed_bytes(0, 128, bits, ctypes.byref(pb), ctypes.byref(ns)) == OK
+    assert pb.value == 0
+
+
+def test_packed_bytes_bad_bits(lib):
+    pb, ns = ctypes.c_int64(), ctypes.c_int64()
+    for b in (0, 1, 2, 8, 16, -4):
+        assert lib.ddg_packed_bytes(16, 128, b, ctypes.byref(pb), ctypes.byref(ns)) == E_ARG
+
+
+def test_workspace_bytes(lib):
+    b = ctypes.c_size_t()
+    assert lib.ddg_lowrank_workspace_bytes(4096, 32, ctypes.byref(b)) == OK and b.value == 4096 * 64
+    assert lib.ddg_lowrank_workspace_bytes(3, 8, ctypes.byref(b)) == OK and b.value == 256
+    assert lib.ddg_lowrank_workspace_bytes(0, 32, ctypes.byref(b)) == OK and b.value == 0
+    for r in (0, 4, 12, 136, -8):
+        assert lib.ddg_lowrank_workspace_bytes(64, r, ctypes.byref(b)) == E_SHAPE
+    assert lib.ddg_lowrank_workspace_bytes(64, 32, None) == E_ARG
+
+
+def test_quantize_pack_rejects_bad_arguments(lib):
+    q = lib.ddg_quantize_pack
+    assert q(FAKE, 0, 16, 128, 9, FAKE, FAKE, None) == E_ARG         # bits
+    assert q(FAKE, 7, 16, 128, 4, FAKE, FAKE, None) == E_ARG         # dtype
+    assert q(FAKE, 0, 16, 100, 4, FAKE, FAKE, None) == E_SHAPE       # k % 128
+    assert q(FAKE, 0, -2, 128, 4, FAKE, FAKE, None) == E_SHAPE
+    assert q(None, 0, 16, 128, 4, FAKE, FAKE, None) == E_ARG         # null
+    assert q(FAKE, 0, 16, 128, 4, None, FAKE, None) == E_ARG
+    assert q(FAKE, 0, 16, 128, 4, FAKE, None, None) == E_ARG
+    assert q(MISALIGNED, 0, 16, 128, 4, FAKE, FAKE, None) == E_ALIGN
+    assert q(FAKE, 0, 16, 128, 4, FAKE + 8, FAKE, None) == E_ALIGN
+    assert q(FAKE, 0, 16, 128, 4, FAKE, FAKE + 2, None) == E_ALIGN
+    assert q(None, 0, 0, 128, 4, None, None, None) == OK              # empty: no-op
+
+
+def test_dequantize_rejects_bad_arguments(lib):
+    d = lib.ddg_dequantize
+    assert d(FAKE, FAKE, 2, 16, 128, FAKE, None) == E_ARG
+    assert d(FAKE, FAKE, 4, 16, 64, FAKE, None) == E_SHAPE
+    assert d(None, FAKE, 4, 16, 128, FAKE, None) == E_ARG
+    assert d(FAKE, FAKE, 4, 16, 128, MISALIGNED, None) == E_ALIGN
+    assert d(None, None, 4, 0, 128, None, None) == OK
+
+
+def test_dequant_gemm_rejects_bad_arguments(lib):
+    g = lib.ddg_dequant_gemm
+    assert g(FAKE, 4, 128, FAKE, FAKE, 8, 32, FAKE, 0, None) == E_ARG      # bits
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE, 5, None) == E_ARG      # y dtype
+    assert g(FAKE, 4, 130, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE    # k
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 24, FAKE, 0, None) == E_SHAPE    # n % 16
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 0, FAKE, 0, None) == E_SHAPE     # n == 0
+    assert g(FAKE, -1, 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE   # m < 0
+    assert g(FAKE, 2 ** 31, 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE
+    assert g(None, 4, 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_ARG
+    assert g(FAKE, 4, 128, None, FAKE, 4, 32, FAKE, 0, None) == E_ARG
+    assert g(FAKE, 4, 128, FAKE, None, 4, 32, FAKE, 0, None) == E_ARG
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, None, 0, None) == E_ARG
+    assert g(MISALIGNED, 4, 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_ALIGN
+    assert g(FAKE, 4, 128, FAKE + 4, FAKE, 4, 32, FAKE, 0, None) == E_ALIGN
+    assert g(FAKE, 4, 128, FAKE, FAKE + 1, 4, 32, FAKE, 0, None) == E_ALIGN
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE + 8, 1, None) == E_ALIGN
+    assert g(None, 0, 128, None, None, 4, 32, None, 0, None) == OK          # M == 0
+
+
+def test_lowrank_fused_gemm_rejects_bad_arguments(lib):
+    f = lib.ddg_lowrank_fused_gemm
+    base = [FAKE, 64, 256, FAKE, FAKE, 4, 64, FAKE, FAKE, 32, FAKE, 0, FAKE, 64 * 64, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = {"x": 0, "m": 1, "k": 2, "bits": 5, "n": 6, "down": 7, "up": 8, "r": 9, "y": 10,
+               "ydt": 11, "ws": 12, "wsb": 13}
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return f(*a)
+
+    assert call(r=12) == E_SHAPE
+    assert call(r=0) == E_SHAPE
+    assert call(r=256) == E_SHAPE
+    assert call(down=None) == E_ARG
+    assert call(up=None) == E_ARG
+    assert call(ws=None) == E_ARG
+    assert call(down=MISALIGNED) == E_ALIGN
+    assert call(ws=MISALIGNED) == E_ALIGN
+    assert call(wsb=64 * 64 - 1) == E_WS
+    assert call(bits=1) == E_ARG
+    assert call(k=100) == E_SHAPE
+    assert call(m=0, x=None, down=None, up=None, ws=None, y=None) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        api.load_library(str(tmp_path / "missing.so"))

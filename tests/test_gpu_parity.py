@@ -1,0 +1,219 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: packed bytes, scales, dense dequantized bf16 weights.
+Tolerance (products): relative Frobenius <= 1e-3 and per-row max-abs
+<= 2e-2 * max|row| of the oracle on the same dequantized weights.
+Full-size workloads compare sampled rows that the oracle computes one by one
+(first rows, random rows, the ragged last rows); small shapes compare every
+element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dit_dequant_gemm_amd import synth
+from parity_util import (check_product, dev_bf16, dev_f32, f32_bits, host, sample_rows,
+                         sample_weight_rows)
+
+pytestmark = pytest.mark.gpu
+BITS = (3, 4, 5, 6, 7)
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _quant_exact(api, w, bits, rows=None, f32_input=False):
+    """GPU quantize_pack of the whole tensor; oracle on `rows` (all if None)."""
+    wt = dev_f32(w) if f32_input else dev_bf16(w)
+    qw = api.quantize_pack(wt, bits)
+    n, k = w.shape
+    packed = host(qw.packed).reshape(n, k * bits // 8)
+    scales = host(qw.scales)
+    rows = np.arange(n) if rows is None else rows
+    p_ref, s_ref, q_ref = O.quantize_pack(w[rows], bits)
+    assert np.array_equal(packed[rows].reshape(-1), p_ref), "packed bytes differ"
+    assert np.array_equal(f32_bits(scales[rows]), f32_bits(s_ref)), "scales differ"
+    return qw, q_ref, s_ref
+
+
+# ------------------------------------------------------------------ quantize + pack
+@pytest.mark.parametrize("bits", BITS)
+def test_quantize_pack_small_edge_cases(gpu_lib, bits):
+    _case(f"quantize_pack edge cases bits={bits}")
+    rng = np.random.default_rng(bits)
+    w = rng.normal(0, 0.02, (24, 384)).astype(np.float32)
+    w[1, :128] = 0.0                                   # all-zero group
+    w[2, 128:256] = rng.normal(0, 1e-39, 128)          # subnormal group (f32 input)
+    w[3, :] = rng.standard_t(2, 384) * 3.0             # heavy tails
+    w[4, 5] = 100.0                                    # single outlier
+    w[5, :] = np.round(rng.normal(0, 3, 384))          # many exact ties
+    w[6, 256:] = -w[6, 256:]
+    w[7, :128] = 1e30
+    wb = synth.to_bf16(w)
+    _quant_exact(gpu_lib, wb, bits)                    # bf16 input
+    _quant_exact(gpu_lib, w, bits, f32_input=True)     # float32 input
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (17, 1152), (64, 512)])
+def test_quantize_pack_random_shapes(gpu_lib, bits, n, k):
+    _case(f"quantize_pack n={n} k={k} bits={bits}")
+    w = synth.random_case(n * 1000 + k + bits, 1, n, k)["w"]
+    _quant_exact(gpu_lib, w, bits)
+
+
+def test_quantize_pack_config1(gpu_lib):
+    _case("quantize_pack workload 1")
+    c = synth.config1()
+    _quant_exact(gpu_lib, c["w"], c["bits"])
+
+
+def test_quantize_pack_config2_full(gpu_lib):
+    _case("quantize_pack workload 2 (3072x3072, every row)")
+    c = synth.config2(m=1)
+    _quant_exact(gpu_lib, c["w"], 4)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+@pytest.mark.parametrize("bits", (3, 5, 6, 7))
+def test_quantize_pack_config3(gpu_lib, which, bits):
+    _case(f"quantize_pack workload 3 {which} bits={bits}")
+    c = synth.config3(which, m=1)
+    rows = sample_weight_rows(c["w"].shape[0], bits)
+    _quant_exact(gpu_lib, c["w"], bits, rows)
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "up", "down"])
+def test_quantize_pack_config5_all_bits(gpu_lib, name):
+    w = synth.config5_weights(name)
+    for bits in BITS:
+        _case(f"quantize_pack workload 5 {name} bits={bits}")
+        _quant_exact(gpu_lib, w, bits, sample_weight_rows(w.shape[0], bits))
+
+
+# ------------------------------------------------------------------ dense dequantize
+@pytest.mark.parametrize("bits", BITS)
+def test_dequantize_bit_exact(gpu_lib, bits):
+    _case(f"dequantize bits={bits}")
+    w = synth.random_case(7 + bits, 1, 48, 640, wstd=0.05)["w"]
+    qw = gpu_lib.quantize_pack(dev_bf16(w), bits)
+    d = host(gpu_lib.dequantize(qw))
+    q_u, s = O.quantize_groups(w, bits)
+    assert np.array_equal(f32_bits(d), f32_bits(O.dequant_bf16(q_u, s, bits)))
+
+
+# ------------------------------------------------------------------ products
+def _oracle_w16(w, bits):
+    q_u, s = O.quantize_groups(w, bits)
+    return O.dequant_bf16(q_u, s, bits)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m", [1, 15, 16, 17, 33, 64, 65, 130, 257])
+def test_gemm_ragged_shapes(gpu_lib, bits, m):
+    for n, k in ((16, 128), (48, 384), (272, 256)):
+        _case(f"dequant_gemm m={m} n={n} k={k} bits={bits}")
+        c = synth.random_case(m * 7 + n + k + bits, m, n, k)
+        qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+        y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], bits))
+        xd = dev_bf16(c["x"])
+        check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32)), y_ref, False, "f32")
+        check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
+
+
+def test_gemm_empty_batch_leaves_output(gpu_lib):
+    _case("dequant_gemm m=0")
+    c = synth.random_case(1, 4, 32, 128)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), 4)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    y = gpu_lib.dequant_gemm(x, qw, torch.float32)
+    assert y.shape == (0, 32)
+
+
+def test_gemm_config1(gpu_lib):
+    _case("dequant_gemm workload 1 (M=64)")
+    c = synth.config1()
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), 4)
+    y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], 4))
+    xd = dev_bf16(c["x"])
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32)), y_ref, False)
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True)
+
+
+@pytest.mark.parametrize("m", [16, 4096])
+def test_gemm_config2(gpu_lib, m):
+    _case(f"dequant_gemm workload 2 M={m}")
+    c = synth.config2(m=m)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), 4)
+    w16 = _oracle_w16(c["w"], 4)
+    rows = sample_rows(m, 2) if m > 64 else np.arange(m)
+    y_ref = O.gemm_ref(c["x"][rows], w16)
+    xd = dev_bf16(c["x"])
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32))[rows], y_ref, False)
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16))[rows], y_ref, True)
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_gemm_config3(gpu_lib, which):
+    c = synth.config3(which)
+    xd = dev_bf16(c["x"])
+    rows = sample_rows(4096, 3, count=64)
+    for bits in c["bits_sweep"]:
+        _case(f"dequant_gemm workload 3 {which} bits={bits}")
+        qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+        y_ref = O.gemm_ref(c["x"][rows], _oracle_w16(c["w"], bits))
+        check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16))[rows], y_ref, True)
+        check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32))[rows], y_ref, False)
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "up", "down"])
+def test_gemm_config5(gpu_lib, name):
+    w = synth.config5_weights(name)
+    drawn = synth.config5_bits()[name]
+    x16 = synth.config5_x(name, 16)
+    xd16 = dev_bf16(x16)
+    wd = dev_bf16(w)
+    for bits in BITS:                      # every width at M = 16
+        _case(f"dequant_gemm workload 5 {name} M=16 bits={bits}")
+        qw = gpu_lib.quantize_pack(wd, bits)
+        w16 = _oracle_w16(w, bits)
+        check_product(host(gpu_lib.dequant_gemm(xd16, qw, torch.bfloat16)), O.gemm_ref(x16, w16), True)
+        if bits == drawn:                  # the drawn width at M = 32760 (ragged last tile)
+            _case(f"dequant_gemm workload 5 {name} M=32760 bits={bits}")
+            x = synth.config5_x(name, 32760)
+            rows = sample_rows(32760, 5, count=48, tail=248)
+            y = host(gpu_lib.dequant_gemm(dev_bf16(x), qw, torch.bfloat16))
+            check_product(y[rows], O.gemm_ref(x[rows], w16), True)
+            del x, y
+
+
+# ------------------------------------------------------------------ low-rank branch
+def _lowrank_case(api, x, w, bits, r, rows=None, out=torch.float32):
+    l1, l2, res = O.svd_split(w, r)
+    qr, q_ref, s_ref = _quant_exact(api, res, bits, f32_input=True,
+                                    rows=None if w.shape[0] <= 512 else sample_weight_rows(w.shape[0], r))
+    w16 = O.dequant_bf16(*O.quantize_groups(res, bits), bits)
+    rows = np.arange(x.shape[0]) if rows is None else rows
+    y_ref, _ = O.lowrank_fused_ref(x[rows], w16, l1, l2)
+    ld = dev_bf16(np.ascontiguousarray(l1.T))
+    lu = dev_bf16(np.ascontiguousarray(l2.T))
+    y = host(api.lowrank_fused_gemm(dev_bf16(x), qr, ld, lu, out))
+    return check_product(y[rows], y_ref, out == torch.bfloat16)
+
+
+@pytest.mark.parametrize("r", [8, 16, 40, 64, 128])
+@pytest.mark.parametrize("m", [5, 16, 48, 100])
+def test_lowrank_small_shapes(gpu_lib, r, m):
+    _case(f"lowrank_fused_gemm m={m} r={r}")
+    c = synth.random_case(r * 100 + m, m, 144, 384, wstd=0.05)
+    _lowrank_case(gpu_lib, c["x"], c["w"], 4, r)
+    _lowrank_case(gpu_lib, c["x"], c["w"], 5, r, out=torch.bfloat16)
+
+
+def test_lowrank_config4(gpu_lib):
+    _case("lowrank_fused_gemm workload 4 (M=4096, r=32)")
+    c = synth.config4()
+    _lowrank_case(gpu_lib, c["x"], c["w"], 4, 32, rows=sample_rows(4096, 4))
+    _lowrank_case(gpu_lib, c["x"][:16], c["w"], 4, 32, out=torch.bfloat16)
