@@ -42,9 +42,49 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the oracle's GEMM sample time")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
+                                                      "dequant_gemm_attnproj3072_traffic.md"),
+                    help="profile summary holding the measured HBM bytes per launch of the "
+                         "dominant kernel (used only while the kernel sources are unchanged)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times), to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) over the HIP sources, in name order."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dit_dequant_gemm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path: str):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("source_hash") == kernel_source_hash():
+                return int(rec["bytes_per_launch"])
+    return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, three times: counter reference."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, x, budget_s):
@@ -63,11 +103,14 @@ def cpu_baseline(w, x, budget_s):
     packed, scales, _ = O.quantize_pack(w, BITS)
     t_q = time.perf_counter() - t0
     w16 = O.dequant_from_packed(packed, scales, BITS, N, K)
+    # the float64 product over row chunks of X, cycling through the 4096 rows
+    # until the budget is used (at least one full pass)
     rows, t_g = 0, 0.0
     chunk = 256
-    while rows < x.shape[0] and t_g < budget_s:
+    while rows < x.shape[0] or t_g < budget_s:
+        r0 = rows % x.shape[0]
         t1 = time.perf_counter()
-        O.gemm_ref(x[rows:rows + chunk], w16)
+        O.gemm_ref(x[r0:r0 + chunk], w16)
         t_g += time.perf_counter() - t1
         rows += chunk
     q_bytes = 2 * N * K + N * K * BITS // 8 + N * K // 32
@@ -76,8 +119,8 @@ def cpu_baseline(w, x, budget_s):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 product of {rows} of the 4096 token rows with the oracle's "
-                   f"dequantized 3072x3072 weight ({t_g:.1f} s); oracle quantize+pack of the "
+        "sample": (f"float64 product of {rows} token rows (the 4096 rows of X, cycled) with the "
+                   f"oracle's dequantized 3072x3072 weight ({t_g:.1f} s); oracle quantize+pack of the "
                    f"whole weight {t_q:.2f} s = {q_bytes / t_q / 1e9:.3f} GB/s (1 thread)"),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
@@ -85,6 +128,9 @@ def cpu_baseline(w, x, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the product "
               "shards along the output dimension with no exchange, see the design notes",
@@ -158,9 +204,7 @@ def main():
     gbps_small = (p_bytes + s_bytes) / (t_s * 1e-3) / 1e9
     gbps_q = (w_bytes + p_bytes + s_bytes) / (t_q * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic)
 
     out = {
         "metric": "dequant-GEMM TFLOP/s (M=4096) + packed-weight GB/s (M=16), % of roofline",
