@@ -26,7 +26,7 @@ BITS = (3, 4, 5, 6, 7)
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # IEEE float32 for the bit-exact quantizer: correctly rounded division,
     # subnormals kept, no contraction into fused multiply-adds.
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",

@@ -8,7 +8,8 @@
 
 namespace {
 
-constexpr int64_t kMaxDim = 2147483647;     // M, N, K fit a signed 32-bit int
+constexpr int64_t kMaxDim = 2147483647;     // M, N fit a signed 32-bit int
+constexpr int64_t kMaxK = INT64_C(1) << 20; // per-tile buffer ranges stay below 4 GiB
 constexpr int kMaxDevices = 64;
 
 // Per-device facts cached on first use: 0 unknown, 1 gfx950, -1 other.
@@ -82,7 +83,8 @@ struct SmallF {
 int check_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed, const float* scales,
                int bits, int64_t n, const void* y, int y_dtype) {
   if (!bits_ok(bits) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32)) return DDG_ERR_ARG;
-  if (m < 0 || m > kMaxDim || !k_ok(k) || n <= 0 || n > kMaxDim || n % 16) return DDG_ERR_SHAPE;
+  if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || n % 16)
+    return DDG_ERR_SHAPE;
   if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return DDG_ERR_SHAPE;
   if (m == 0) return DDG_OK;
   if (!x || !packed || !scales || !y) return DDG_ERR_ARG;
@@ -104,13 +106,13 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t strea
   // large kernel: 256-row tiles, 4 waves x (16*cb) columns; pick cb by the
   // estimated time (rounds of workgroups x relative tile time).
   const int64_t tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
-  int best_cb = 4;
+  int best_cb = 3;
   double best = 1e300;
-  for (int cb : {4, 3, 2}) {
+  for (int cb : {3, 2}) {
     const int64_t tiles_n = (a.n + 64 * cb - 1) / (64 * cb);
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t rounds = (tiles + cus - 1) / cus;
-    const double eff = cb == 4 ? 1.0 : (cb == 3 ? 0.97 : 0.9);
+    const double eff = cb == 3 ? 1.0 : 0.85;
     const double t = (double)rounds * cb / eff;
     if (t < best - 1e-9) { best = t; best_cb = cb; }
   }

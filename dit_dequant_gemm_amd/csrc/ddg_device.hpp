@@ -55,9 +55,10 @@ __device__ __forceinline__ uint32_t chunk_code(const uint32_t* be, int i) {
 // Dequantize codes 8*S .. 8*S+7 of a chunk into one MFMA operand (8 bf16,
 // element e = code 8*S+e).  `raw` holds the chunk's dwords as loaded
 // (little-endian), `be` the same dwords byte-swapped (unused for B == 4).
-template <int B, int S>
-__device__ __forceinline__ bf16x8 dequant8(const uint32_t* raw, const uint32_t* be, float s,
-                                           float ns64) {
+// S must fold to a constant after inlining and unrolling.
+template <int B>
+__device__ __forceinline__ bf16x8 dequant8(const uint32_t* raw, const uint32_t* be, int S,
+                                           float s, float ns64) {
   u32x4 out;
   if constexpr (B == 4) {
     // Dword S holds codes 8S..8S+7; byte p holds code 8S+2p in its high
@@ -82,6 +83,30 @@ __device__ __forceinline__ bf16x8 dequant8(const uint32_t* raw, const uint32_t* 
   return __builtin_bit_cast(bf16x8, out);
 }
 
+// Pair P (codes 8*S+2P, 8*S+2P+1) of a chunk as one packed bf16 pair.  For
+// B == 4, `nib` holds the two nibble-spread words of dword S (see
+// spread_nibbles); otherwise `be` holds the byte-swapped dwords.  S and P must
+// fold to constants after inlining.
+template <int B>
+__device__ __forceinline__ uint32_t dequant_pair(const uint32_t* be, const uint32_t* nib, int S,
+                                                 int P, float s, float ns64) {
+  if constexpr (B == 4) {
+    const float a = (float)((nib[0] >> (8 * P)) & 0xFFu);
+    const float b = (float)((nib[1] >> (8 * P)) & 0xFFu);
+    return pack_bf16x2(scale_code(a, s, ns64), scale_code(b, s, ns64));
+  } else {
+    const uint32_t c0 = chunk_code<B>(be, 8 * S + 2 * P) + Bits<B>::bias64;
+    const uint32_t c1 = chunk_code<B>(be, 8 * S + 2 * P + 1) + Bits<B>::bias64;
+    return pack_bf16x2(scale_code((float)c0, s, ns64), scale_code((float)c1, s, ns64));
+  }
+}
+
+// 4-bit only: dword x -> {even codes, odd codes} as bytes q + 64.
+__device__ __forceinline__ void spread_nibbles(uint32_t x, uint32_t* nib) {
+  nib[0] = ((x >> 4) & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
+  nib[1] = (x & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
+}
+
 template <int B>
 __device__ __forceinline__ void byteswap_chunk(const uint32_t* raw, uint32_t* be) {
   if constexpr (B != 4) {
@@ -104,6 +129,42 @@ __device__ __forceinline__ void load_chunk(const uint8_t* p, uint32_t* raw) {
     const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
 #pragma unroll
     for (int j = 0; j < B; ++j) raw[j] = q[j];
+  }
+}
+
+// Buffer resources (gfx9 family descriptor word 3).  Loads past num_records
+// return zeros, so tiles that hang over the M or N edge need no clamping.
+constexpr int kBufferFlags = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+// The B dwords of one chunk through a buffer resource (dword-aligned offsets).
+template <int B>
+__device__ __forceinline__ void load_chunk_buf(rsrc_t r, uint32_t voff, uint32_t soff,
+                                               uint32_t* raw) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t v3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+  if constexpr (B == 3) {
+    const v3 a = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    raw[0] = a.x; raw[1] = a.y; raw[2] = a.z;
+  } else {
+    const v4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
+    if constexpr (B == 5) {
+      raw[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, 0);
+    } else if constexpr (B == 6) {
+      const v2 b = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16, soff, 0);
+      raw[4] = b.x; raw[5] = b.y;
+    } else if constexpr (B == 7) {
+      const v3 b = __builtin_amdgcn_raw_buffer_load_b96(r, voff + 16, soff, 0);
+      raw[4] = b.x; raw[5] = b.y; raw[6] = b.z;
+    }
   }
 }
 

@@ -12,6 +12,9 @@
 //                         article, section "技术原理详解")
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "ddg_device.hpp"
 
 namespace ddg {
@@ -106,10 +109,10 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
   const float s = scales[c >> 2];
   const float ns64 = -64.0f * s;
   u32x4* dst = out + c * 4;
-  dst[0] = __builtin_bit_cast(u32x4, dequant8<B, 0>(raw, be, s, ns64));
-  dst[1] = __builtin_bit_cast(u32x4, dequant8<B, 1>(raw, be, s, ns64));
-  dst[2] = __builtin_bit_cast(u32x4, dequant8<B, 2>(raw, be, s, ns64));
-  dst[3] = __builtin_bit_cast(u32x4, dequant8<B, 3>(raw, be, s, ns64));
+  dst[0] = __builtin_bit_cast(u32x4, dequant8<B>(raw, be, 0, s, ns64));
+  dst[1] = __builtin_bit_cast(u32x4, dequant8<B>(raw, be, 1, s, ns64));
+  dst[2] = __builtin_bit_cast(u32x4, dequant8<B>(raw, be, 2, s, ns64));
+  dst[3] = __builtin_bit_cast(u32x4, dequant8<B>(raw, be, 3, s, ns64));
 }
 
 // ---------------------------------------------------------------------------
@@ -193,47 +196,76 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 template <int B, int CB>
 __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs args) {
+  constexpr int RB = kBM / 16;          // 16 row blocks of 16
+  constexpr int LA = 6;                 // A-operand look-ahead, in MFMA steps
+  constexpr int RING = 8;               // A-operand ring (64 steps per group = 8 laps)
   constexpr int WN = 16 * CB;
   constexpr int BN = 4 * WN;
-  constexpr int RB = kBM / 16;
+  constexpr int HAND = 64 - LA;         // step of the group hand-over (barrier)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lq = lane >> 4;
   int tm, tn;
   tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
   const int m0 = tm * kBM;
-  const int n0 = tn * BN + wave * WN;
+  const int nw0 = tn * BN;
   const int K = args.k;
   const int G = K / kGroup;
-  const int64_t row_bytes = (int64_t)K * B / 8;
+  const uint32_t row_bytes = (uint32_t)K * B / 8;
+  const uint32_t xrow_bytes = (uint32_t)K * 2;
+  const int m_valid = min(kBM, args.m - m0);
+  const int n_valid = min(BN, args.n - nw0);
+  // Rows past M / columns past N read as zeros (their results are not stored).
+  const rsrc_t rx = make_rsrc(args.x + (int64_t)m0 * K, (uint32_t)m_valid * xrow_bytes);
+  const rsrc_t rw = make_rsrc(args.packed + (int64_t)nw0 * row_bytes, (uint32_t)n_valid * row_bytes);
+  const rsrc_t rs = make_rsrc(args.scales + (int64_t)nw0 * G, (uint32_t)n_valid * G * 4);
 
-  // This lane's weight rows (one per column block), clamped for the N tail.
-  const uint8_t* wptr[CB];
-  const float* sptr[CB];
+  // X -> LDS.  DMA instruction i of this wave fills 1 KB block wave*16+i: rows
+  // 4*(wave*16+i) + lane/16, slot lane%16, holding logical chunk slot^(row&15).
+  uint32_t xoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 64 + 4 * j + lq;
+    const int c = (lane & 15) ^ (r & 15);
+    xoff[j] = (uint32_t)r * xrow_bytes + (uint32_t)c * 16;
+  }
+  auto issue_x_one = [&](int g, int stage, int i) {
+    uint8_t* base = lds + stage * kLdsStage + wave * 16 * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + i * 1024), 16,
+                                             xoff[i & 3] + (uint32_t)(i >> 2) * 16 * xrow_bytes,
+                                             (uint32_t)g * kGroup * 2, 0, 0);
+  };
+  auto issue_x_all = [&](int g, int stage) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_x_one(g, stage, i);
+  };
+
+  // Packed chunks and scales of this lane's columns.
+  uint32_t woff[CB], soffs[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int n = min(n0 + cb * 16 + lr, args.n - 1);
-    wptr[cb] = args.packed + (int64_t)n * row_bytes + lq * 4 * B;
-    sptr[cb] = args.scales + (int64_t)n * G;
+    const uint32_t nl = (uint32_t)(wave * WN + cb * 16 + lr);
+    woff[cb] = nl * row_bytes + (uint32_t)lq * 4 * B;
+    soffs[cb] = nl * (uint32_t)G * 4;
   }
-
-  // X -> LDS: wave issues 16 x 1 KB per stage; lane -> (row, slot).
-  const int x_row_local = lane >> 4;     // + 4 * instruction
-  const int x_slot = lane & 15;
-  auto issue_x = [&](int g, int stage) {
-    uint8_t* base = lds + stage * kLdsStage;
+  auto load_w = [&](int g, uint32_t (&w)[CB][B], float (&sc)[CB]) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int blk = wave * 16 + i;                 // 1 KB block = 4 rows
-      const int r = blk * 4 + x_row_local;
-      const int c = x_slot ^ (r & 15);
-      const int gm = min(m0 + r, args.m - 1);
-      const __bf16* src = args.x + (int64_t)gm * K + g * kGroup + c * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0, 0);
+    for (int cb = 0; cb < CB; ++cb) {
+      load_chunk_buf<B>(rw, woff[cb], (uint32_t)g * 16 * B, w[cb]);
+      sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soffs[cb],
+                                                                            (uint32_t)g * 4, 0));
     }
+  };
+
+  // A operand of step u (sub-step u/16, row block u%16) from an LDS stage.
+  uint32_t aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = (uint32_t)(lr * 256 + (((4 * lq + s) ^ lr) * 16));
+  auto read_a = [&](int stage, int u) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(lds + stage * kLdsStage + (u & 15) * 4096 +
+                                            aoff[u >> 4]);
   };
 
   f32x4 acc[RB][CB];
@@ -243,101 +275,152 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs args) {
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (args.t != nullptr) {
-    // acc = T * lora_up^T over the rank dimension (steps of 32).
+    // acc = T * lora_up^T over the rank dimension, 32 at a time (zero-padded).
     const int R = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     for (int j0 = 0; j0 < R; j0 += 32) {
       const int kk = j0 + 8 * lq;
       const bool kok = kk < R;
+      const int kc = min(kk, R - 8);
       bf16x8 bl[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const int n = min(n0 + cb * 16 + lr, args.n - 1);
-        bl[cb] = load_bf16x8_or_zero(args.lora_up + (int64_t)n * R + kk, kok);
+        const int n = min(nw0 + wave * WN + cb * 16 + lr, args.n - 1);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
+        bl[cb] = kok ? v : zero;
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int m = min(m0 + rb * 16 + lr, args.m - 1);
-        const bf16x8 al = load_bf16x8_or_zero(args.t + (int64_t)m * R + kk, kok);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
+        const bf16x8 al = kok ? v : zero;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16x16x32(al, bl[cb], acc[rb][cb]);
       }
     }
   }
 
-  uint32_t wcur[CB][B], wnext[CB][B];
-  float scur[CB], snext[CB];
-  issue_x(0, 0);
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    load_chunk<B>(wptr[cb], wcur[cb]);
-    scur[cb] = sptr[cb][0];
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  uint32_t wc[CB][B], wn[CB][B], be[CB][B];
+  float sc[CB], sn[CB], ns64[CB];
+  bf16x8 ring[RING];
+  u32x4 bc[CB], bnx[CB];
+  uint32_t nib[CB][2];                  // 4-bit: spread nibbles of the current dword
 
-  for (int g = 0; g < G; ++g) {
-    const int stage = g & 1;
-    const bool more = (g + 1) < G;
-    if (more) {
-      issue_x(g + 1, stage ^ 1);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        load_chunk<B>(wptr[cb] + (int64_t)(g + 1) * 16 * B, wnext[cb]);
-        snext[cb] = sptr[cb][g + 1];
-      }
-    }
-    uint32_t be[CB][B];
-    float ns64[CB];
+  auto take_next_weights = [&]() {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      byteswap_chunk<B>(wcur[cb], be[cb]);
-      ns64[cb] = -64.0f * scur[cb];
-    }
-    const uint8_t* xs = lds + stage * kLdsStage;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 bfrag[CB];
+      for (int j = 0; j < B; ++j) wc[cb][j] = wn[cb][j];
+      sc[cb] = sn[cb];
+      byteswap_chunk<B>(wc[cb], be[cb]);
+      ns64[cb] = -64.0f * sc[cb];
+    }
+  };
+  // dequantization job j of a sub-step: column block j / 4, bf16 pair j % 4
+  auto dq_job = [&](int j, int S) {
+    const int cb = j >> 2, p = j & 3;
+    if constexpr (B == 4) {
+      if (p == 0) spread_nibbles(wc[cb][S], nib[cb]);
+    }
+    bnx[cb][p] = dequant_pair<B>(be[cb], nib[cb], S, p, sc[cb], ns64[cb]);
+  };
+
+  // Group g uses LDS stage (g + G) % 2, so that after an optional lone first
+  // group (odd G) the loop runs in (stage 0, stage 1) pairs.
+  const int st0 = G & 1;
+  issue_x_all(0, st0);
+  load_w(0, wn, sn);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  take_next_weights();
+#pragma unroll
+  for (int u = 0; u < LA; ++u) ring[u % RING] = read_a(st0, u);
+#pragma unroll
+  for (int j = 0; j < 4 * CB; ++j) dq_job(j, 0);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) bc[cb] = bnx[cb];
+
+  // One 128-group: 64 steps (4 sub-steps x 16 row blocks), CB MFMAs each.
+  // Every step index is a compile-time constant (fold over an index sequence),
+  // so the operand ring and the dequantization schedule are fully static:
+  //   steps 0..15   one X DMA instruction each (next group -> idle stage)
+  //   step 16       packed chunks + scales of the next group
+  //   every step    one LDS read LA steps ahead, at most one dequantization
+  //                 job (2 codes) for the next sub-step, CB MFMAs
+  //   end of s = 2  switch to the next group's weights (their loads landed)
+  //   step HAND     barrier: the next group's X is in LDS, this stage is free
+  // The last group runs the same code: its "next group" is itself again
+  // (clamped), fetched into the idle stage and never used.
+  constexpr int JOBS = 4 * CB;
+  auto group = [&](int g, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const int gn = min(g + 1, G - 1);
+    auto step = [&]<int T>(std::integral_constant<int, T>) {
+      constexpr int s = T >> 4, rb = T & 15;
+      if constexpr (T < 16) issue_x_one(gn, ST ^ 1, T);
+      if constexpr (T == 16) load_w(gn, wn, sn);
+      if constexpr (T == HAND) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      constexpr int u = T + LA;
+      if constexpr (u < 64) {
+        ring[u % RING] = read_a(ST, u);
+      } else {
+        ring[u % RING] = read_a(ST ^ 1, u - 64);
+      }
+      // jobs of the next sub-step (the next group's sub-step 0 during s = 3)
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        ([&] {
+          if constexpr (J * 16 / JOBS == rb) dq_job(J, (s + 1) & 3);
+        }(), ...);
+      }(std::make_integer_sequence<int, JOBS>{});
+      [&]<int... C>(std::integer_sequence<int, C...>) {
+        ((acc[rb][C] = mfma16x16x32(ring[T % RING], __builtin_bit_cast(bf16x8, bc[C]),
+                                    acc[rb][C])), ...);
+      }(std::make_integer_sequence<int, CB>{});
+      if constexpr (rb == 15) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) bc[cb] = bnx[cb];
+        if constexpr (s == 2) take_next_weights();
+      }
+      // interleave: MFMA, a few VALU, MFMA, ... (one wave per SIMD: the
+      // dequantization must ride in the shadow of the matrix pipe)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        if (s == 0) bfrag[cb] = dequant8<B, 0>(wcur[cb], be[cb], scur[cb], ns64[cb]);
-        if (s == 1) bfrag[cb] = dequant8<B, 1>(wcur[cb], be[cb], scur[cb], ns64[cb]);
-        if (s == 2) bfrag[cb] = dequant8<B, 2>(wcur[cb], be[cb], scur[cb], ns64[cb]);
-        if (s == 3) bfrag[cb] = dequant8<B, 3>(wcur[cb], be[cb], scur[cb], ns64[cb]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
-      const int slot = (4 * lq + s) ^ lr;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 16 + lr;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(xs + row * 256 + slot * 16);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16x16x32(a, bfrag[cb], acc[rb][cb]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-        for (int j = 0; j < B; ++j) wcur[cb][j] = wnext[cb][j];
-        scur[cb] = snext[cb];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... T>(std::integer_sequence<int, T...>) {
+      (step(std::integral_constant<int, T>{}), ...);
+    }(std::make_integer_sequence<int, 64>{});
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int g = 0;
+  if (st0 == 1) group(g++, I1{});
+  for (; g < G; g += 2) {
+    group(g, I0{});
+    group(g + 1, I1{});
   }
 
+  const int ncol0 = nw0 + wave * WN;
   if (args.out_bf16) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        store_tile<true>(args.y, args.n, m0 + rb * 16 + 4 * lq, n0 + cb * 16 + lr, args.m,
+        store_tile<true>(args.y, args.n, m0 + rb * 16 + 4 * lq, ncol0 + cb * 16 + lr, args.m,
                          args.n, acc[rb][cb]);
   } else {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        store_tile<false>(args.y, args.n, m0 + rb * 16 + 4 * lq, n0 + cb * 16 + lr, args.m,
+        store_tile<false>(args.y, args.n, m0 + rb * 16 + 4 * lq, ncol0 + cb * 16 + lr, args.m,
                           args.n, acc[rb][cb]);
   }
 }
@@ -401,10 +484,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs args) {
     for (int cb = 0; cb < CB; ++cb) {
       byteswap_chunk<B>(raw[cb], be[cb]);
       ns64[cb] = -64.0f * sc[cb];
-      const bf16x8 b0 = dequant8<B, 0>(raw[cb], be[cb], sc[cb], ns64[cb]);
-      const bf16x8 b1 = dequant8<B, 1>(raw[cb], be[cb], sc[cb], ns64[cb]);
-      const bf16x8 b2 = dequant8<B, 2>(raw[cb], be[cb], sc[cb], ns64[cb]);
-      const bf16x8 b3 = dequant8<B, 3>(raw[cb], be[cb], sc[cb], ns64[cb]);
+      const bf16x8 b0 = dequant8<B>(raw[cb], be[cb], 0, sc[cb], ns64[cb]);
+      const bf16x8 b1 = dequant8<B>(raw[cb], be[cb], 1, sc[cb], ns64[cb]);
+      const bf16x8 b2 = dequant8<B>(raw[cb], be[cb], 2, sc[cb], ns64[cb]);
+      const bf16x8 b3 = dequant8<B>(raw[cb], be[cb], 3, sc[cb], ns64[cb]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         acc[rb][cb] = mfma16x16x32(a[rb][0], b0, acc[rb][cb]);

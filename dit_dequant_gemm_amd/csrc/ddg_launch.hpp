@@ -15,7 +15,7 @@ hipError_t launch_quantize_pack(const void* w, bool f32_in, int64_t n_chunks, ui
 template <int B>
 hipError_t launch_dequantize(const uint8_t* packed, const float* scales, int64_t n_chunks,
                              void* out, hipStream_t stream);
-// cb: column blocks (of 16) per wave, one of 2, 3, 4
+// cb: column blocks (of 16) per wave, 2 or 3
 template <int B>
 hipError_t launch_gemm_large(const GemmArgs& a, int cb, hipStream_t stream);
 // rb: row blocks (of 16) in 1, 2, 4; cb: column blocks per workgroup in 1, 2, 4

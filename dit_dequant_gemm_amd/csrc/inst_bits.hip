@@ -39,7 +39,6 @@ hipError_t launch_gemm_large<DDG_BITS>(const GemmArgs& a, int cb, hipStream_t st
   switch (cb) {
     case 2: gemm_large_kernel<DDG_BITS, 2><<<grid, block, 0, stream>>>(a); break;
     case 3: gemm_large_kernel<DDG_BITS, 3><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_large_kernel<DDG_BITS, 4><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -120,7 +120,7 @@ int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t
  *   x       M x K bf16.       packed/scales: the record of an N x K weight.
  *   y       M x N, y_dtype (DDG_BF16 or DDG_F32), fully overwritten.
  * Requirements: M >= 0 (M == 0 is a no-op), N a positive multiple of 16,
- * K a positive multiple of 128, M, N <= 2^31 - 1.
+ * K a positive multiple of 128 and at most 2^20, M, N <= 2^31 - 1.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP.
  */
 int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,

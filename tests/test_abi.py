@@ -110,6 +110,7 @@ def test_dequant_gemm_rejects_bad_arguments(lib):
     assert g(FAKE, 4, 128, FAKE, FAKE, 8, 32, FAKE, 0, None) == E_ARG      # bits
     assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE, 5, None) == E_ARG      # y dtype
     assert g(FAKE, 4, 130, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE    # k
+    assert g(FAKE, 4, 2 ** 20 + 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE
     assert g(FAKE, 4, 128, FAKE, FAKE, 4, 24, FAKE, 0, None) == E_SHAPE    # n % 16
     assert g(FAKE, 4, 128, FAKE, FAKE, 4, 0, FAKE, 0, None) == E_SHAPE     # n == 0
     assert g(FAKE, -1, 128, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE   # m < 0
