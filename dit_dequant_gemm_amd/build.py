@@ -54,6 +54,10 @@ def _compile(unit, asm: bool):
     if asm:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=udir)
+    if r.returncode != 0 and asm:
+        # keeping intermediates can trip the compiler on some template
+        # instantiations; the object itself builds without them
+        r = subprocess.run(cmd[:-1], capture_output=True, text=True, cwd=udir)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {name}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj, r.stderr

@@ -3,7 +3,7 @@
 #include <atomic>
 #include <cstring>
 
-#include "../../include/ddg.h"
+#include "ddg.h"
 #include "ddg_launch.hpp"
 
 namespace {
@@ -97,29 +97,25 @@ int check_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed, const
 hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t stream) {
   if (a.m <= 64) {
     const int rb = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
-    // widest column tile that still gives every compute unit a workgroup
-    int cb = 1;
-    if ((int64_t)a.n / 64 >= cus) cb = 4;
-    else if ((int64_t)a.n / 32 >= cus) cb = 2;
-    return by_bits<SmallF>(bits, a, rb, cb, stream);
+    // Column waves x K-split waves per workgroup, from timings of the
+    // 16-token products: four column waves where that still leaves about 200+
+    // workgroups (wide outputs), two where 128+ remain, else one column wave
+    // and an 8-way K split.
+    const int64_t nb = ((int64_t)a.n + 15) / 16;
+    int nc = 1, nk = rb == 1 ? 8 : 4;
+    if (rb == 1) {
+      if (nb / 4 >= 200) { nc = 4; nk = 2; }
+      else if (nb / 2 >= 128) { nc = 2; nk = 2; }
+    } else if ((nb + 1) / 2 >= cus) {
+      nc = 2; nk = 2;
+    }
+    return by_bits<SmallF>(bits, a, rb, nc, nk, stream);
   }
-  // large kernel: 256-row tiles, 4 waves x (16*cb) columns; pick cb by the
-  // estimated time (rounds of workgroups x relative tile time).
-  const int64_t tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
-  int best_cb = 3;
-  double best = 1e300;
-  for (int cb : {3, 2}) {
-    const int64_t tiles_n = (a.n + 64 * cb - 1) / (64 * cb);
-    const int64_t tiles = tiles_m * tiles_n;
-    const int64_t rounds = (tiles + cus - 1) / cus;
-    const double eff = cb == 3 ? 1.0 : 0.85;
-    const double t = (double)rounds * cb / eff;
-    if (t < best - 1e-9) { best = t; best_cb = cb; }
-  }
-  a.tiles_m = (int)tiles_m;
-  a.tiles_n = (a.n + 64 * best_cb - 1) / (64 * best_cb);
+  // large kernel: 256 x 256 tiles
+  a.tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
+  a.tiles_n = (a.n + ddg::kBN - 1) / ddg::kBN;
   if ((int64_t)a.tiles_m * a.tiles_n > kMaxDim) return hipErrorInvalidValue;
-  return by_bits<LargeF>(bits, a, best_cb, stream);
+  return by_bits<LargeF>(bits, a, stream);
 }
 
 }  // namespace

@@ -145,20 +145,22 @@ __device__ __forceinline__ bf16x8 load_bf16x8_or_zero(const __bf16* p, bool ok) 
 }
 
 // ---------------------------------------------------------------------------
-// K2: large-M GEMM.  Workgroup = 4 waves (256 threads), tile BM = 256 rows x
-// BN = 4*WN columns; wave w owns columns [w*WN, (w+1)*WN) for all 256 rows,
-// so every packed weight is dequantized exactly once per workgroup.
-// K advances one 128-group per step:
-//   * X[256 x 128] bf16 (64 KB) goes HBM -> LDS with global_load_lds_dwordx4,
+// K2: large-M GEMM.  Workgroup = 8 waves (512 threads, two per SIMD: one wave
+// per SIMD cannot keep the matrix pipe busy), tile 256 rows x 256 columns.
+// Wave w owns columns [32w, 32w + 32) for all 256 rows, so every packed
+// weight is dequantized exactly once per workgroup and each wave needs only
+// 128 accumulators.  MFMA v_mfma_f32_32x32x16_bf16: A = X rows (from LDS),
+// B = dequantized weights (registers).
+// K advances one 128-group per step of the outer loop:
+//   * X[256 x 128] bf16 (64 KB) goes HBM -> LDS with buffer_load ... lds,
 //     double-buffered (2 x 64 KB).  LDS row r holds 16 chunks of 16 bytes;
-//     logical chunk c sits in slot c ^ (r & 15) so that MFMA A-operand reads
-//     are free of bank conflicts.
-//   * each lane streams its packed chunk (B dwords) + scale for each of its
-//     WN/16 columns straight to registers, one step ahead.
-// MFMA v_mfma_f32_16x16x32_bf16.  The K index inside a group is permuted so
-// that MFMA sub-step s, lane quarter lq, element e uses input
-// 32*lq + 8*s + e: the A operand (X from LDS) and the B operand (dequantized
-// codes) use the same permutation, so the dot products are unchanged.
+//     logical chunk c sits in slot c ^ (r & 15), which keeps the A-operand
+//     ds_read_b128 free of bank conflicts.
+//   * each lane streams its packed chunk (64 codes = 2B dwords) and scale one
+//     group ahead into registers.
+// The K index inside a group is permuted: MFMA k-step j (0..7), lane half h,
+// element e uses input 64h + 8j + e, for the A operand and the dequantized B
+// operand alike, so the dot products are unchanged.
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const __bf16* x;          // M x K
@@ -173,6 +175,7 @@ struct GemmArgs {
 };
 
 constexpr int kBM = 256;
+constexpr int kBN = 256;
 constexpr int kLdsStage = kBM * kGroup * 2;   // 64 KB
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -194,141 +197,129 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gm;
 }
 
-template <int B, int CB>
-__global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs args) {
-  constexpr int RB = kBM / 16;          // 16 row blocks of 16
-  constexpr int LA = 6;                 // A-operand look-ahead, in MFMA steps
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int B>
+__global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
+  constexpr int RB = kBM / 32;          // 8 row blocks of 32
+  constexpr int LA = 4;                 // A-operand look-ahead, in MFMA steps
   constexpr int RING = 8;               // A-operand ring (64 steps per group = 8 laps)
-  constexpr int WN = 16 * CB;
-  constexpr int BN = 4 * WN;
-  constexpr int HAND = 64 - LA;         // step of the group hand-over (barrier)
+  constexpr int STEPS = 8 * RB;         // 8 k-steps x 8 row blocks
+  constexpr int HAND = STEPS - LA;      // step of the group hand-over (barrier)
+  constexpr int CW = 2 * B;             // packed dwords per lane per group
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int lr = lane & 15, lq = lane >> 4;
+  const int lr = lane & 31, lh = lane >> 5;
   int tm, tn;
   tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
   const int m0 = tm * kBM;
-  const int nw0 = tn * BN;
+  const int nw0 = tn * kBN;
   const int K = args.k;
   const int G = K / kGroup;
   const uint32_t row_bytes = (uint32_t)K * B / 8;
   const uint32_t xrow_bytes = (uint32_t)K * 2;
   const int m_valid = min(kBM, args.m - m0);
-  const int n_valid = min(BN, args.n - nw0);
+  const int n_valid = min(kBN, args.n - nw0);
   // Rows past M / columns past N read as zeros (their results are not stored).
   const rsrc_t rx = make_rsrc(args.x + (int64_t)m0 * K, (uint32_t)m_valid * xrow_bytes);
   const rsrc_t rw = make_rsrc(args.packed + (int64_t)nw0 * row_bytes, (uint32_t)n_valid * row_bytes);
   const rsrc_t rs = make_rsrc(args.scales + (int64_t)nw0 * G, (uint32_t)n_valid * G * 4);
 
-  // X -> LDS.  DMA instruction i of this wave fills 1 KB block wave*16+i: rows
-  // 4*(wave*16+i) + lane/16, slot lane%16, holding logical chunk slot^(row&15).
+  // X -> LDS.  DMA instruction i (0..7) of wave w fills 1 KB block 8w+i: rows
+  // 32w + 4i + lane/16, slot lane%16, holding logical chunk slot ^ (row & 15).
   uint32_t xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = wave * 64 + 4 * j + lq;
+    const int r = wave * 32 + 4 * j + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     xoff[j] = (uint32_t)r * xrow_bytes + (uint32_t)c * 16;
   }
   auto issue_x_one = [&](int g, int stage, int i) {
-    uint8_t* base = lds + stage * kLdsStage + wave * 16 * 1024;
+    uint8_t* base = lds + stage * kLdsStage + wave * 8 * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + i * 1024), 16,
                                              xoff[i & 3] + (uint32_t)(i >> 2) * 16 * xrow_bytes,
                                              (uint32_t)g * kGroup * 2, 0, 0);
   };
-  auto issue_x_all = [&](int g, int stage) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) issue_x_one(g, stage, i);
+
+  // Packed chunk (codes 64h .. 64h+63 of column 32w + lane%32) and its scale.
+  const uint32_t nl = (uint32_t)(wave * 32 + lr);
+  const uint32_t woff = nl * row_bytes + (uint32_t)lh * 8 * B;
+  const uint32_t soffs = nl * (uint32_t)G * 4;
+  auto load_w = [&](int g, uint32_t (&w)[CW], float& sc) {
+    load_chunk_buf<B>(rw, woff, (uint32_t)g * 16 * B, w);
+    load_chunk_buf<B>(rw, woff + 4 * B, (uint32_t)g * 16 * B, w + B);
+    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soffs,
+                                                                      (uint32_t)g * 4, 0));
   };
 
-  // Packed chunks and scales of this lane's columns.
-  uint32_t woff[CB], soffs[CB];
+  // A operand of step u (k-step u/8, row block u%8) from an LDS stage.
+  uint32_t aoff[8];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const uint32_t nl = (uint32_t)(wave * WN + cb * 16 + lr);
-    woff[cb] = nl * row_bytes + (uint32_t)lq * 4 * B;
-    soffs[cb] = nl * (uint32_t)G * 4;
-  }
-  auto load_w = [&](int g, uint32_t (&w)[CB][B], float (&sc)[CB]) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      load_chunk_buf<B>(rw, woff[cb], (uint32_t)g * 16 * B, w[cb]);
-      sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soffs[cb],
-                                                                            (uint32_t)g * 4, 0));
-    }
-  };
-
-  // A operand of step u (sub-step u/16, row block u%16) from an LDS stage.
-  uint32_t aoff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = (uint32_t)(lr * 256 + (((4 * lq + s) ^ lr) * 16));
+  for (int ks = 0; ks < 8; ++ks) aoff[ks] = (uint32_t)(lr * 256 + (((8 * lh + ks) ^ (lr & 15)) * 16));
   auto read_a = [&](int stage, int u) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(lds + stage * kLdsStage + (u & 15) * 4096 +
-                                            aoff[u >> 4]);
+    return *reinterpret_cast<const bf16x8*>(lds + stage * kLdsStage + (u & 7) * 8192 +
+                                            aoff[u >> 3]);
   };
 
-  f32x4 acc[RB][CB];
+  f32x16 acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
 
   if (args.t != nullptr) {
-    // acc = T * lora_up^T over the rank dimension, 32 at a time (zero-padded).
+    // acc = T * lora_up^T over the rank dimension, 16 at a time (zero-padded).
     const int R = args.r;
     const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    for (int j0 = 0; j0 < R; j0 += 32) {
-      const int kk = j0 + 8 * lq;
+    const int n = min(nw0 + wave * 32 + lr, args.n - 1);
+    for (int j0 = 0; j0 < R; j0 += 16) {
+      const int kk = j0 + 8 * lh;
       const bool kok = kk < R;
       const int kc = min(kk, R - 8);
-      bf16x8 bl[CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int n = min(nw0 + wave * WN + cb * 16 + lr, args.n - 1);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
-        bl[cb] = kok ? v : zero;
-      }
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
+      const bf16x8 bl = kok ? v : zero;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int m = min(m0 + rb * 16 + lr, args.m - 1);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
-        const bf16x8 al = kok ? v : zero;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16x16x32(al, bl[cb], acc[rb][cb]);
+        const int m = min(m0 + rb * 32 + lr, args.m - 1);
+        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
+        acc[rb] = mfma32x32x16(kok ? tv : zero, bl, acc[rb]);
       }
     }
   }
 
-  uint32_t wc[CB][B], wn[CB][B], be[CB][B];
-  float sc[CB], sn[CB], ns64[CB];
+  uint32_t wc[CW], wn[CW], be[CW];
+  float sc = 0.f, sn = 0.f, ns64 = 0.f;
   bf16x8 ring[RING];
-  u32x4 bc[CB], bnx[CB];
-  uint32_t nib[CB][2];                  // 4-bit: spread nibbles of the current dword
+  u32x4 bc, bnx;
+  uint32_t nib[2];                      // 4-bit: spread nibbles of the current dword
 
   auto take_next_weights = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int j = 0; j < CW; ++j) wc[j] = wn[j];
+    sc = sn;
+    if constexpr (B != 4) {
 #pragma unroll
-      for (int j = 0; j < B; ++j) wc[cb][j] = wn[cb][j];
-      sc[cb] = sn[cb];
-      byteswap_chunk<B>(wc[cb], be[cb]);
-      ns64[cb] = -64.0f * sc[cb];
+      for (int j = 0; j < CW; ++j) be[j] = __builtin_bswap32(wc[j]);
     }
+    ns64 = -64.0f * sc;
   };
-  // dequantization job j of a sub-step: column block j / 4, bf16 pair j % 4
-  auto dq_job = [&](int j, int S) {
-    const int cb = j >> 2, p = j & 3;
+  // dequantization job p (bf16 pair p, 0..3) of k-step ks
+  auto dq_job = [&](int p, int ks) {
     if constexpr (B == 4) {
-      if (p == 0) spread_nibbles(wc[cb][S], nib[cb]);
+      if (p == 0) spread_nibbles(wc[ks], nib);
     }
-    bnx[cb][p] = dequant_pair<B>(be[cb], nib[cb], S, p, sc[cb], ns64[cb]);
+    bnx[p] = dequant_pair<B>(be, nib, ks, p, sc, ns64);
   };
 
   // Group g uses LDS stage (g + G) % 2, so that after an optional lone first
   // group (odd G) the loop runs in (stage 0, stage 1) pairs.
   const int st0 = G & 1;
-  issue_x_all(0, st0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue_x_one(0, st0, i);
   load_w(0, wn, sn);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -336,66 +327,51 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs args) {
 #pragma unroll
   for (int u = 0; u < LA; ++u) ring[u % RING] = read_a(st0, u);
 #pragma unroll
-  for (int j = 0; j < 4 * CB; ++j) dq_job(j, 0);
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) bc[cb] = bnx[cb];
+  for (int p = 0; p < 4; ++p) dq_job(p, 0);
+  bc = bnx;
 
-  // One 128-group: 64 steps (4 sub-steps x 16 row blocks), CB MFMAs each.
-  // Every step index is a compile-time constant (fold over an index sequence),
-  // so the operand ring and the dequantization schedule are fully static:
-  //   steps 0..15   one X DMA instruction each (next group -> idle stage)
-  //   step 16       packed chunks + scales of the next group
-  //   every step    one LDS read LA steps ahead, at most one dequantization
-  //                 job (2 codes) for the next sub-step, CB MFMAs
-  //   end of s = 2  switch to the next group's weights (their loads landed)
+  // One 128-group: 64 steps (8 k-steps x 8 row blocks), one MFMA each.  Every
+  // step index is a compile-time constant (fold over an index sequence), so the
+  // operand ring and the dequantization schedule are fully static:
+  //   steps 0..7    one X DMA instruction each (next group -> idle stage)
+  //   step 8        packed chunk + scale of the next group
+  //   every step    one LDS read LA steps ahead; on even row blocks one
+  //                 dequantization job (2 codes) for the next k-step; 1 MFMA
+  //   end of ks = 6 switch to the next group's weights (their loads landed)
   //   step HAND     barrier: the next group's X is in LDS, this stage is free
   // The last group runs the same code: its "next group" is itself again
   // (clamped), fetched into the idle stage and never used.
-  constexpr int JOBS = 4 * CB;
   auto group = [&](int g, auto stage_tag) {
     constexpr int ST = decltype(stage_tag)::value;
     const int gn = min(g + 1, G - 1);
     auto step = [&]<int T>(std::integral_constant<int, T>) {
-      constexpr int s = T >> 4, rb = T & 15;
-      if constexpr (T < 16) issue_x_one(gn, ST ^ 1, T);
-      if constexpr (T == 16) load_w(gn, wn, sn);
+      constexpr int ks = T >> 3, rb = T & 7;
+      if constexpr (T < 8) issue_x_one(gn, ST ^ 1, T);
+      if constexpr (T == 8) load_w(gn, wn, sn);
       if constexpr (T == HAND) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
       constexpr int u = T + LA;
-      if constexpr (u < 64) {
+      if constexpr (u < STEPS) {
         ring[u % RING] = read_a(ST, u);
       } else {
-        ring[u % RING] = read_a(ST ^ 1, u - 64);
+        ring[u % RING] = read_a(ST ^ 1, u - STEPS);
       }
-      // jobs of the next sub-step (the next group's sub-step 0 during s = 3)
-      [&]<int... J>(std::integer_sequence<int, J...>) {
-        ([&] {
-          if constexpr (J * 16 / JOBS == rb) dq_job(J, (s + 1) & 3);
-        }(), ...);
-      }(std::make_integer_sequence<int, JOBS>{});
-      [&]<int... C>(std::integer_sequence<int, C...>) {
-        ((acc[rb][C] = mfma16x16x32(ring[T % RING], __builtin_bit_cast(bf16x8, bc[C]),
-                                    acc[rb][C])), ...);
-      }(std::make_integer_sequence<int, CB>{});
-      if constexpr (rb == 15) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) bc[cb] = bnx[cb];
-        if constexpr (s == 2) take_next_weights();
+      if constexpr ((rb & 1) == 0) dq_job(rb >> 1, (ks + 1) & 7);
+      acc[rb] = mfma32x32x16(ring[T % RING], __builtin_bit_cast(bf16x8, bc), acc[rb]);
+      if constexpr (rb == 7) {
+        bc = bnx;
+        if constexpr (ks == 6) take_next_weights();
       }
-      // interleave: MFMA, a few VALU, MFMA, ... (one wave per SIMD: the
-      // dequantization must ride in the shadow of the matrix pipe)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
+      // one MFMA, then the VALU work rides in its shadow
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
     [&]<int... T>(std::integer_sequence<int, T...>) {
       (step(std::integral_constant<int, T>{}), ...);
-    }(std::make_integer_sequence<int, 64>{});
+    }(std::make_integer_sequence<int, STEPS>{});
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -407,139 +383,230 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs args) {
     group(g + 1, I1{});
   }
 
-  const int ncol0 = nw0 + wave * WN;
-  if (args.out_bf16) {
+  // Epilogue: lane holds rows 8(r/4) + 4h + r%4 of column lane%32, r = 0..15.
+  const int col = nw0 + wave * 32 + lr;
+  if (col < args.n) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        store_tile<true>(args.y, args.n, m0 + rb * 16 + 4 * lq, ncol0 + cb * 16 + lr, args.m,
-                         args.n, acc[rb][cb]);
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        store_tile<false>(args.y, args.n, m0 + rb * 16 + 4 * lq, ncol0 + cb * 16 + lr, args.m,
-                          args.n, acc[rb][cb]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// K3: small-M GEMM (M <= 16*RB <= 64).  Workgroup = NW waves; it owns CB
-// column blocks (16*CB columns) and the whole K range; wave w takes the
-// groups g = w, w + NW, ...  Per group each lane loads its X row slice (the
-// A operands, reused across the CB column blocks) and, per column block, its
-// packed chunk + scale.  The NW partial tiles are summed through LDS.
-// ---------------------------------------------------------------------------
-template <int B, int RB, int CB, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_small_kernel(GemmArgs args) {
-  __shared__ f32x4 red[NW][RB * CB][64];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 15, lq = lane >> 4;
-  const int n0 = blockIdx.x * 16 * CB;
-  const int K = args.k;
-  const int G = K / kGroup;
-  const int64_t row_bytes = (int64_t)K * B / 8;
-
-  const uint8_t* wptr[CB];
-  const float* sptr[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int n = min(n0 + cb * 16 + lr, args.n - 1);
-    wptr[cb] = args.packed + (int64_t)n * row_bytes + lq * 4 * B;
-    sptr[cb] = args.scales + (int64_t)n * G;
-  }
-  const __bf16* xptr[RB];
-  bool xok[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int m = rb * 16 + lr;
-    xok[rb] = m < args.m;
-    xptr[rb] = args.x + (int64_t)min(m, args.m - 1) * K + 32 * lq;
-  }
-
-  f32x4 acc[RB][CB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int g = wave; g < G; g += NW) {
-    bf16x8 a[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[rb][s] = load_bf16x8_or_zero(xptr[rb] + g * kGroup + 8 * s, xok[rb]);
-    uint32_t raw[CB][B], be[CB][B];
-    float sc[CB], ns64[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      load_chunk<B>(wptr[cb] + (int64_t)g * 16 * B, raw[cb]);
-      sc[cb] = sptr[cb][g];
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      byteswap_chunk<B>(raw[cb], be[cb]);
-      ns64[cb] = -64.0f * sc[cb];
-      const bf16x8 b0 = dequant8<B>(raw[cb], be[cb], 0, sc[cb], ns64[cb]);
-      const bf16x8 b1 = dequant8<B>(raw[cb], be[cb], 1, sc[cb], ns64[cb]);
-      const bf16x8 b2 = dequant8<B>(raw[cb], be[cb], 2, sc[cb], ns64[cb]);
-      const bf16x8 b3 = dequant8<B>(raw[cb], be[cb], 3, sc[cb], ns64[cb]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][cb] = mfma16x16x32(a[rb][0], b0, acc[rb][cb]);
-        acc[rb][cb] = mfma16x16x32(a[rb][1], b1, acc[rb][cb]);
-        acc[rb][cb] = mfma16x16x32(a[rb][2], b2, acc[rb][cb]);
-        acc[rb][cb] = mfma16x16x32(a[rb][3], b3, acc[rb][cb]);
-      }
-    }
-  }
-
-  if (args.t != nullptr) {
-    if (wave == 0) {
-      const int R = args.r;
-      for (int j0 = 0; j0 < R; j0 += 32) {
-        const int kk = j0 + 8 * lq;
-        const bool kok = kk < R;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int n = min(n0 + cb * 16 + lr, args.n - 1);
-          const bf16x8 bl = load_bf16x8_or_zero(args.lora_up + (int64_t)n * R + kk, kok);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int m = min(rb * 16 + lr, args.m - 1);
-            const bf16x8 al = load_bf16x8_or_zero(args.t + (int64_t)m * R + kk, kok);
-            acc[rb][cb] = mfma16x16x32(al, bl, acc[rb][cb]);
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < args.m) {
+          if (args.out_bf16)
+            static_cast<__bf16*>(args.y)[(int64_t)row * args.n + col] = (__bf16)acc[rb][r];
+          else
+            static_cast<float*>(args.y)[(int64_t)row * args.n + col] = acc[rb][r];
         }
       }
     }
   }
+}
 
+// ---------------------------------------------------------------------------
+// K3: small-M GEMM (M <= 16*RB <= 64): a bandwidth kernel.
+// Workgroup = NC x NK waves.  Wave (c, h) owns column block c (16 columns of
+// the workgroup's 16*NC) and K split h (a contiguous range of 128-groups).
+//   * X: for each group, the 16*RB x 128 bf16 slice of a K split is staged
+//     once into an LDS ring (R slots) with coalesced buffer_load ... lds (1 KB
+//     per instruction, shared out among the NC waves of that split) and read
+//     back as MFMA A operands by all NC waves.  Rows past M read as zeros.
+//   * packed weights: each lane's chunk (B dwords) + scale PW groups ahead in
+//     a register ring (they come from HBM; this is what must stay in flight).
+//   * the NK partial tiles of a column block are summed through LDS.
+// All ring slots are static (the step loop is unrolled by lcm(R, PW)); group
+// indices past a wave's range are clamped, loaded and never used.
+// ---------------------------------------------------------------------------
+template <int B, int RB, int NC, int NK>
+__global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args) {
+  // X slices and packed weights of step j + D are issued together at step j
+  // (ring of S = D + 1 slots each).  Loads finish in issue order, so waiting
+  // for the X of step j never waits for a later step's packed weights.
+  constexpr int XSLOT = RB * 16 * 256;        // one group's X slice: 16*RB rows x 256 bytes
+  constexpr int RED_BYTES = (NK > 1 ? NK - 1 : 1) * NC * RB * 64 * 16;
+  // ring slots: up to 6, as many as fit in the 160 KB of LDS
+  constexpr int S_FIT = (160 * 1024 - RED_BYTES) / (NK * XSLOT);
+  constexpr int S = S_FIT > 6 ? 6 : S_FIT;
+  static_assert(S >= 2, "X ring needs two slots");
+  constexpr int D = S - 1;                    // steps in flight
+  constexpr int DMA_SLOT = XSLOT / 1024;      // 1 KB DMA instructions per slice
+  static_assert(DMA_SLOT % NC == 0, "slice DMA must split evenly over the column waves");
+  constexpr int ND = DMA_SLOT / NC;           // DMA instructions per wave per group
+  constexpr int NWL = (B == 3 || B == 4) ? 2 : 3;   // buffer loads per group: chunk + scale
+  // issued after X(j) (at step j - D): W(j), then D - 1 steps of X + W
+  constexpr int VM_AHEAD = NWL + (D - 1) * (ND + NWL);
+  static_assert(VM_AHEAD < 64, "vmcnt field");
+  constexpr int WAIT_IMM = (VM_AHEAD & 15) | ((VM_AHEAD >> 4) << 14) | (7 << 4) | (15 << 8);
+  // One LDS array per ring slot: the compiler can then see that a DMA into
+  // one slot does not alias reads of another, and does not make the reads
+  // wait for it.
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[NK][XSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs1[NK][XSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[S > 2 ? NK : 1][S > 2 ? XSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs3[S > 3 ? NK : 1][S > 3 ? XSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs4[S > 4 ? NK : 1][S > 4 ? XSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs5[S > 5 ? NK : 1][S > 5 ? XSLOT : 16];
+  __shared__ f32x4 red[NK > 1 ? NK - 1 : 1][NC][RB][64];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = wave % NC, h = wave / NC;
+  auto xslot = [&]<int SL>(std::integral_constant<int, SL>) -> uint8_t* {
+    if constexpr (SL == 0) return &xs0[h][0];
+    else if constexpr (SL == 1) return &xs1[h][0];
+    else if constexpr (SL == 2) return &xs2[h][0];
+    else if constexpr (SL == 3) return &xs3[h][0];
+    else if constexpr (SL == 4) return &xs4[h][0];
+    else return &xs5[h][0];
+  };
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NC;
+  const int K = args.k;
+  const int G = K / kGroup;
+  const int g_begin = h * G / NK, g_end = (h + 1) * G / NK;
+  const int cnt = g_end - g_begin;
+  const int steps = (G + NK - 1) / NK;        // the same for every wave (barriers)
+  const int g_last = cnt > 0 ? g_end - 1 : G - 1;
+  const uint32_t row_bytes = (uint32_t)K * B / 8;
+
+  // this wave's column (rows past N read as zeros through the resource bounds)
+  const int n = min(n0 + c * 16 + lr, args.n - 1);
+  const int n_valid = min(16 * NC, args.n - n0);
+  const rsrc_t rw = make_rsrc(args.packed + (int64_t)n0 * row_bytes, (uint32_t)n_valid * row_bytes);
+  const rsrc_t rs = make_rsrc(args.scales + (int64_t)n0 * G, (uint32_t)n_valid * G * 4);
+  const uint32_t woff = (uint32_t)(c * 16 + lr) * row_bytes + (uint32_t)lq * 4 * B;
+  const uint32_t soffs = (uint32_t)(c * 16 + lr) * (uint32_t)G * 4;
+
+  // X DMA: instruction d of this wave fills 1 KB block c*ND + d of the slice:
+  // rows 4*(c*ND+d) + lane/16, slot lane%16 = logical chunk ^ (row & 15).
+  const rsrc_t rx = make_rsrc(args.x, (uint32_t)args.m * (uint32_t)K * 2);
+  auto issue_x = [&](uint8_t* slot_base, int j) {
+    const int g = min(g_begin + j, g_last);
+    uint8_t* base = slot_base + (c * ND) * 1024;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int row = 4 * (c * ND + d) + (lane >> 4);
+      const uint32_t voff = (uint32_t)row * (uint32_t)K * 2 + (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + d * 1024), 16, voff,
+                                               (uint32_t)g * kGroup * 2, 0, 0);
+    }
+  };
+  uint32_t aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = (uint32_t)(lr * 256 + (((4 * lq + s) ^ lr) * 16));
+
+  uint32_t raw[S][B];
+  float sc[S];
+  auto load_w = [&](int slot, int j) {
+    const int g = min(g_begin + j, g_last);
+    load_chunk_buf<B>(rw, woff, (uint32_t)g * 16 * B, raw[slot]);
+    sc[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soffs,
+                                                                            (uint32_t)g * 4, 0));
+  };
+
+  // one accumulator per sub-step: the four MFMAs of a group are independent
+  // (a single chain would wait out the MFMA latency four times per group)
+  f32x4 acc4[4][RB];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc4[s][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* base, int ws) {
+    uint32_t be[B];
+    byteswap_chunk<B>(raw[ws], be);
+    const float ns64 = -64.0f * sc[ws];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 bf = dequant8<B>(raw[ws], be, s, sc[ws], ns64);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + rb * 4096 + aoff[s]);
+        acc4[s][rb] = mfma16x16x32(a, bf, acc4[s][rb]);
+      }
+    }
+  };
+
+  // Step j (ring slot j % S for both rings): wait for X(j), barrier, issue
+  // X(j+D) and W(j+D) into slot (j-1) % S, compute step j.
+  using std::integral_constant;
+  auto step = [&]<int U>(integral_constant<int, U>, int j) {
+    // own X DMA of step j landed; then every wave's has, and every wave is
+    // done with slot (j-1) % S.  A bare s_barrier: a fenced barrier would
+    // also wait for the loads of later steps still in flight.
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    asm volatile("s_barrier" ::: "memory");
+    issue_x(xslot(integral_constant<int, (U + D) % S>{}), j + D);
+    load_w((U + D) % S, j + D);
+    if (j < cnt) compute(xslot(integral_constant<int, U % S>{}), U % S);
+  };
+  // prologue: steps 0..D-1, X then W per step (the order of the steady state)
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    // (sched_barrier: the scheduler would otherwise sink the scale loads to
+    // the end, and the wait counts merged at the loop head would follow them)
+    ((issue_x(xslot(integral_constant<int, J>{}), J), load_w(J, J),
+      __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, D>{});
+  // main loop: whole blocks of S steps, every load unconditional (so the
+  // compiler's wait counts stay exact across the loop)
+  const int full = steps / S * S;
+  for (int j0 = 0; j0 < full; j0 += S) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (step(integral_constant<int, U>{}, j0 + U), ...);
+    }(std::make_integer_sequence<int, S>{});
+  }
+  // tail: the remaining steps (fewer than S)
+  [&]<int... U>(std::integer_sequence<int, U...>) {
+    ([&] { if (full + U < steps) step(integral_constant<int, U>{}, full + U); }(), ...);
+  }(std::make_integer_sequence<int, S>{});
+  __syncthreads();
+
+  f32x4 acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) red[wave][rb * CB + cb][lane] = acc[rb][cb];
-  __syncthreads();
-  // Sum the NW partial tiles; thread t handles tile entries t, t + 64*NW, ...
-  for (int e = threadIdx.x; e < RB * CB * 64; e += 64 * NW) {
-    const int tile = e / 64, ln = e % 64;
-    f32x4 s = red[0][tile][ln];
+    for (int i = 0; i < 4; ++i)
+      acc[rb][i] = (acc4[0][rb][i] + acc4[1][rb][i]) + (acc4[2][rb][i] + acc4[3][rb][i]);
+
+  if constexpr (NK > 1) {
+    if (h > 0) {
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const f32x4 v = red[w][tile][ln];
-      s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+      for (int rb = 0; rb < RB; ++rb) red[h - 1][c][rb][lane] = acc[rb];
     }
-    const int rb = tile / CB, cb = tile % CB;
+    __syncthreads();
+    if (h > 0) return;
+#pragma unroll
+    for (int k = 0; k < NK - 1; ++k)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x4 v = red[k][c][rb][lane];
+        acc[rb][0] += v[0]; acc[rb][1] += v[1]; acc[rb][2] += v[2]; acc[rb][3] += v[3];
+      }
+  }
+
+  if (args.t != nullptr) {
+    const int R_ = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int j0 = 0; j0 < R_; j0 += 32) {
+      const int kk = j0 + 8 * lq;
+      const bool kok = kk < R_;
+      const int kc = min(kk, R_ - 8);
+      const bf16x8 vl = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R_ + kc);
+      const bf16x8 bl = kok ? vl : zero;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int m = min(rb * 16 + lr, args.m - 1);
+        const bf16x8 vt = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R_ + kc);
+        acc[rb] = mfma16x16x32(kok ? vt : zero, bl, acc[rb]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     if (args.out_bf16)
-      store_tile<true>(args.y, args.n, rb * 16 + 4 * (ln >> 4), n0 + cb * 16 + (ln & 15),
-                       args.m, args.n, s);
+      store_tile<true>(args.y, args.n, rb * 16 + 4 * lq, n0 + c * 16 + lr, args.m, args.n, acc[rb]);
     else
-      store_tile<false>(args.y, args.n, rb * 16 + 4 * (ln >> 4), n0 + cb * 16 + (ln & 15),
-                        args.m, args.n, s);
+      store_tile<false>(args.y, args.n, rb * 16 + 4 * lq, n0 + c * 16 + lr, args.m, args.n, acc[rb]);
   }
 }
 

@@ -15,12 +15,13 @@ hipError_t launch_quantize_pack(const void* w, bool f32_in, int64_t n_chunks, ui
 template <int B>
 hipError_t launch_dequantize(const uint8_t* packed, const float* scales, int64_t n_chunks,
                              void* out, hipStream_t stream);
-// cb: column blocks (of 16) per wave, 2 or 3
+// a.tiles_m / a.tiles_n: 256 x 256 tiles
 template <int B>
-hipError_t launch_gemm_large(const GemmArgs& a, int cb, hipStream_t stream);
-// rb: row blocks (of 16) in 1, 2, 4; cb: column blocks per workgroup in 1, 2, 4
+hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t stream);
+// rb: row blocks (of 16) in 1, 2, 4; nc column waves x nk K-split waves per
+// workgroup: (2,2) (1,4) (1,8) (2,4) (4,2) for rb = 1, (1,4) (2,2) otherwise
 template <int B>
-hipError_t launch_gemm_small(const GemmArgs& a, int rb, int cb, hipStream_t stream);
+hipError_t launch_gemm_small(const GemmArgs& a, int rb, int nc, int nk, hipStream_t stream);
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);

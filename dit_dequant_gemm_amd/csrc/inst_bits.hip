@@ -34,27 +34,23 @@ hipError_t launch_dequantize<DDG_BITS>(const uint8_t* packed, const float* scale
 }
 
 template <>
-hipError_t launch_gemm_large<DDG_BITS>(const GemmArgs& a, int cb, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(256);
-  switch (cb) {
-    case 2: gemm_large_kernel<DDG_BITS, 2><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_large_kernel<DDG_BITS, 3><<<grid, block, 0, stream>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_gemm_large<DDG_BITS>(const GemmArgs& a, hipStream_t stream) {
+  gemm_large_kernel<DDG_BITS><<<dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <>
-hipError_t launch_gemm_small<DDG_BITS>(const GemmArgs& a, int rb, int cb, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.n + 16 * cb - 1) / (16 * cb)));
-#define DDG_SMALL(RB, CB, NW)                                                          \
-  if (rb == RB && cb == CB) {                                                          \
-    gemm_small_kernel<DDG_BITS, RB, CB, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);    \
-    return hipGetLastError();                                                          \
+hipError_t launch_gemm_small<DDG_BITS>(const GemmArgs& a, int rb, int nc, int nk,
+                                       hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n + 16 * nc - 1) / (16 * nc)));
+#define DDG_SMALL(RB, NC, NK)                                                             \
+  if (rb == RB && nc == NC && nk == NK) {                                                 \
+    gemm_small_kernel<DDG_BITS, RB, NC, NK><<<grid, dim3(64 * NC * NK), 0, stream>>>(a); \
+    return hipGetLastError();                                                             \
   }
-  DDG_SMALL(1, 1, 8) DDG_SMALL(1, 2, 8) DDG_SMALL(1, 4, 8)
-  DDG_SMALL(2, 1, 8) DDG_SMALL(2, 2, 8) DDG_SMALL(2, 4, 8)
-  DDG_SMALL(4, 1, 8) DDG_SMALL(4, 2, 8) DDG_SMALL(4, 4, 4)
+  DDG_SMALL(1, 2, 2) DDG_SMALL(1, 1, 4) DDG_SMALL(1, 1, 8) DDG_SMALL(1, 2, 4) DDG_SMALL(1, 4, 2)
+  DDG_SMALL(2, 1, 4) DDG_SMALL(2, 2, 2)
+  DDG_SMALL(4, 1, 4) DDG_SMALL(4, 2, 2)
 #undef DDG_SMALL
   return hipErrorInvalidValue;
 }
