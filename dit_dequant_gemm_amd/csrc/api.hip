@@ -74,6 +74,11 @@ struct LargeF {
   static hipError_t run(A... a) { return ddg::launch_gemm_large<B>(a...); }
 };
 template <int B>
+struct SkinnyF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_skinny<B>(a...); }
+};
+template <int B>
 struct SmallF {
   template <typename... A>
   static hipError_t run(A... a) { return ddg::launch_gemm_small<B>(a...); }
@@ -95,6 +100,31 @@ int check_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed, const
 
 // Kernel choice for the product; fills a.tiles_* for the large kernel.
 hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t stream) {
+  if (a.m <= 16) {
+    // Wide outputs (at least 200 workgroups of 64 columns): the
+    // weight-streaming kernel with an 8-way K split and X in registers.  Below
+    // that it would either leave compute units idle or reload X (16 K bf16)
+    // into too many workgroups; the LDS-ring kernel below is faster there.
+    const int64_t nb = ((int64_t)a.n + 15) / 16;
+    const int g = a.k / DDG_GROUP;
+    if (nb / 4 >= 200) {
+      int ncb = 4;
+      // groups per wave chunk: the size (5, 4 or 3) that pads the busiest
+      // wave's share of K (ceil(G / 8) groups) with the fewest empty groups
+      const int per_wave = (g + 7) / 8;
+      int kc = 5, waste = 1 << 30;
+      for (int c = 5; c >= 3; --c) {
+        const int w = (per_wave + c - 1) / c * c - per_wave;
+        if (w < waste) { waste = w; kc = c; }
+      }
+      // shrink until the weight buffers and the scale areas fit in LDS
+      auto lds = [&] { return ddg::skinny_static_lds(bits, kc, ncb) + ddg::skinny_scale_lds(kc); };
+      while (lds() > ddg::kLdsLimit && (ncb > 1 || kc > 3)) {
+        if (ncb > 1) ncb /= 2; else --kc;
+      }
+      if (lds() <= ddg::kLdsLimit) return by_bits<SkinnyF>(bits, a, kc, ncb, stream);
+    }
+  }
   if (a.m <= 64) {
     const int rb = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
     // Column waves x K-split waves per workgroup, from timings of the

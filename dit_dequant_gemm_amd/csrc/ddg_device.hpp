@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ddg {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -100,6 +102,76 @@ __device__ __forceinline__ uint32_t dequant_pair(const uint32_t* be, const uint3
     const uint32_t c1 = chunk_code<B>(be, 8 * S + 2 * P + 1) + Bits<B>::bias64;
     return pack_bf16x2(scale_code((float)c0, s, ns64), scale_code((float)c1, s, ns64));
   }
+}
+
+// ---------------------------------------------------------------------------
+// "Plus-one" form, used by the M <= 16 kernel.  Every code q_u is at most
+// 2^B - 2, so q_u + 1 still fits its B-bit field: one 32-bit add of a
+// constant with a 1 at the lowest bit of every field that lies wholly in a
+// word adds 1 to all of them at once, with no carry between fields.  Then
+// fl32((q_u - n_half) * s) = fma(q_u + 1, s, -2^(B-1) s), the constant being
+// exact (a power-of-two multiple of s), so the product is rounded once.
+// ---------------------------------------------------------------------------
+template <int B>
+struct PlusOne {
+  // the add constant for big-endian word j of a 32-code chunk
+  static constexpr uint32_t word_add(int j) {
+    uint32_t a = 0;
+    for (int c = 0; c < 32; ++c) {
+      const int o = c * B - 32 * j;
+      if (o >= 0 && o + B <= 32) a |= 1u << (32 - o - B);
+    }
+    return a;
+  }
+};
+
+// Byte-swapped chunk words with 1 added to every whole field (B != 4).
+template <int B>
+__device__ __forceinline__ void plus_one_words(const uint32_t* raw, uint32_t* be1) {
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    ((be1[J] = __builtin_bswap32(raw[J]) + PlusOne<B>::word_add(J)), ...);
+  }(std::make_integer_sequence<int, B>{});
+}
+
+// Code I of the chunk plus one, from plus_one_words output.
+template <int B>
+__device__ __forceinline__ uint32_t chunk_code_p1(const uint32_t* be1, int i) {
+  const int o = i * B, j = o >> 5, off = o & 31;
+  if (off + B <= 32) return (be1[j] >> (32 - off - B)) & Bits<B>::mask;
+  // a field across two words was not incremented by the word adds
+  return (__builtin_amdgcn_alignbit(be1[j], be1[j + 1], 64 - off - B) & Bits<B>::mask) + 1u;
+}
+
+// Codes 8S .. 8S+7 of a chunk as one MFMA operand, plus-one form.  For
+// B == 4, x1 = dword S of the chunk plus 0x11111111 (byte p holds codes
+// 8S+2p, 8S+2p+1 in its high, low nibble); otherwise be1 from plus_one_words.
+// nsh = -2^(B-1) * s.  S must fold to a constant.
+template <int B>
+__device__ __forceinline__ bf16x8 dequant8_p1(const uint32_t* be1, uint32_t x1, int S, float s,
+                                              float nsh) {
+  u32x4 out;
+  if constexpr (B == 4) {
+    uint32_t ev = (x1 >> 4) & 0x0F0F0F0Fu;
+    uint32_t od = x1 & 0x0F0F0F0Fu;
+    // keep the two masked words: each byte then converts with one
+    // v_cvt_f32_ubyteN (the compiler would otherwise extract every nibble
+    // with its own bit-field extract)
+    asm("" : "+v"(ev), "+v"(od));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = (float)((ev >> (8 * p)) & 0xFFu);
+      const float b = (float)((od >> (8 * p)) & 0xFFu);
+      out[p] = pack_bf16x2(__builtin_fmaf(a, s, nsh), __builtin_fmaf(b, s, nsh));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = (float)chunk_code_p1<B>(be1, 8 * S + 2 * p);
+      const float b = (float)chunk_code_p1<B>(be1, 8 * S + 2 * p + 1);
+      out[p] = pack_bf16x2(__builtin_fmaf(a, s, nsh), __builtin_fmaf(b, s, nsh));
+    }
+  }
+  return __builtin_bit_cast(bf16x8, out);
 }
 
 // 4-bit only: dword x -> {even codes, odd codes} as bytes q + 64.

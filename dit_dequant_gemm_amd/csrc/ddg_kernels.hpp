@@ -403,17 +403,19 @@ __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// K3: small-M GEMM (M <= 16*RB <= 64): a bandwidth kernel.
+// K3: small-M GEMM (16 < M <= 64; M <= 16 when the skinny kernel below
+// does not apply): a bandwidth kernel.
 // Workgroup = NC x NK waves.  Wave (c, h) owns column block c (16 columns of
 // the workgroup's 16*NC) and K split h (a contiguous range of 128-groups).
 //   * X: for each group, the 16*RB x 128 bf16 slice of a K split is staged
-//     once into an LDS ring (R slots) with coalesced buffer_load ... lds (1 KB
-//     per instruction, shared out among the NC waves of that split) and read
-//     back as MFMA A operands by all NC waves.  Rows past M read as zeros.
-//   * packed weights: each lane's chunk (B dwords) + scale PW groups ahead in
-//     a register ring (they come from HBM; this is what must stay in flight).
+//     into an LDS ring with coalesced buffer_load ... lds (1 KB per
+//     instruction, shared out among the NC waves of that split) and read back
+//     as MFMA A operands by all NC waves.  Rows past M read as zeros.
+//   * packed weights: each lane's chunk (B dwords) and scale in a register
+//     ring; the X slice and the weights of step j + D are issued together at
+//     step j.
 //   * the NK partial tiles of a column block are summed through LDS.
-// All ring slots are static (the step loop is unrolled by lcm(R, PW)); group
+// Ring slots are static (the step loop is unrolled by the ring size); group
 // indices past a wave's range are clamped, loaded and never used.
 // ---------------------------------------------------------------------------
 template <int B, int RB, int NC, int NK>
@@ -608,6 +610,230 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
     else
       store_tile<false>(args.y, args.n, rb * 16 + 4 * lq, n0 + c * 16 + lr, args.m, args.n, acc[rb]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// K3s: product for M <= 16 tokens that streams the packed weights.
+// Workgroup = 8 waves = an 8-way split of the K groups; it owns NCB blocks of
+// 16 output columns.  Wave h works through its share of K in chunks of
+// kc <= KC groups: the chunk's X slice is loaded once into registers and run
+// against the packed rows of every column block, so the weights are read
+// once and X once per workgroup.
+//   * scales: the workgroup's rows of the scale matrix are one contiguous
+//     range; it is copied to LDS once (dynamic LDS, 16 NCB G floats).
+//   * packed weights of a (column block, chunk) -- 16 rows x kc*16*B bytes,
+//     each row's part contiguous -- go to the wave's own LDS buffer with 1 KB
+//     buffer_load ... lds instructions whose lanes take consecutive 16-byte
+//     pieces (whole cache lines, rows end to end); lane (lr, lq) then reads
+//     its B dwords per group: inputs 32 lq .. 32 lq + 31 of the group, the
+//     input order of the other kernels (the X operand uses it too).
+//   * dequantization in the plus-one form (see dequant8_p1).
+// The next column block (or block 0 of the next chunk) streams into the other
+// buffer while this one is dequantized and multiplied.  A load with nothing
+// to fetch goes to an offset past the end of its buffer resource (in the
+// offset register: that is what the range check sees) and returns zeros
+// without a memory access.
+// ---------------------------------------------------------------------------
+// LDS bytes of gemm_skinny_kernel<B, KC, NCB>: the weight buffers (the first
+// one also holds the final reduction) plus the per-wave scale areas.
+__host__ __device__ constexpr size_t skinny_static_lds(int b, int kc, int ncb) {
+  return (size_t)8 * ((kc * b + 3) / 4) * 1024 * 2 >= (size_t)8 * ((kc * b + 3) / 4) * 1024 + (size_t)8 * ncb * 1024
+             ? (size_t)8 * ((kc * b + 3) / 4) * 1024 * 2
+             : (size_t)8 * ((kc * b + 3) / 4) * 1024 + (size_t)8 * ncb * 1024;
+}
+__host__ __device__ constexpr size_t skinny_scale_lds(int kc) { return (size_t)8 * kc * 64 * 4; }
+constexpr size_t kLdsLimit = 160 * 1024;
+
+template <int B, int KC, int NCB>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs args) {
+  constexpr int NW = 8;                  // waves = K splits
+  constexpr uint32_t kNoLoad = 0x80000000u;
+  constexpr int NDMA = (KC * B + 3) / 4; // 1 KB DMA instructions per wave per block
+  constexpr int WBUF = NDMA * 1024;
+  constexpr int RED = NW * NCB * 64 * 16;
+  // Two weight buffers as two arrays: the compiler can then tell that a DMA
+  // into one does not feed reads of the other, and does not wait for it.
+  __shared__ __attribute__((aligned(1024))) uint8_t wl0[NW * WBUF >= RED ? NW * WBUF : RED];
+  __shared__ __attribute__((aligned(1024))) uint8_t wl1[NW * WBUF];
+  // this wave's scales for the current chunk: [group j][row of the workgroup]
+  __shared__ __attribute__((aligned(256))) float scw[NW][KC][64];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int K = args.k, G = K / kGroup;
+  const int n0 = blockIdx.x * 16 * NCB;
+  // (wave-uniform: kept in scalar registers)
+  const int gs = __builtin_amdgcn_readfirstlane(wave * G / NW);
+  const int cnt = __builtin_amdgcn_readfirstlane((wave + 1) * G / NW) - gs;
+  const int nch = __builtin_amdgcn_readfirstlane((cnt + KC - 1) / KC);
+  const int kc_lo = __builtin_amdgcn_readfirstlane(cnt / max(nch, 1));
+  const int kc_rem = cnt - kc_lo * nch;
+  const uint32_t row_bytes = (uint32_t)K * B / 8;
+  const int n_valid = min(16 * NCB, args.n - n0);
+  const rsrc_t rw = make_rsrc(args.packed + (int64_t)n0 * row_bytes, (uint32_t)n_valid * row_bytes);
+  const rsrc_t rs = make_rsrc(args.scales + (int64_t)n0 * G, (uint32_t)n_valid * G * 4);
+  const rsrc_t rx = make_rsrc(args.x, (uint32_t)args.m * (uint32_t)K * 2);
+
+  // chunk c of this wave: groups [g0, g0 + kc), balanced, kc <= KC
+  auto chunk_g0 = [&](int c) __attribute__((always_inline)) { return gs + c * kc_lo + min(c, kc_rem); };
+  auto chunk_kc = [&](int c) __attribute__((always_inline)) { return kc_lo + (c < kc_rem ? 1 : 0); };
+
+  // Per-chunk DMA offsets: DMA d, lane i fetches piece f = 64 d + i of the
+  // block (row f / (kc B), 16-byte piece f % (kc B) of that row's part);
+  // pieces past the block, and every piece of a chunk past the last, get the
+  // no-load offset.  f / (kc B) = f * inv >> 16 for f < 64 NDMA <= 576.
+  auto chunk_offsets = [&](int c, uint32_t* off) __attribute__((always_inline)) {
+    const bool valid = c < nch;
+    const int g0 = chunk_g0(c), kc = chunk_kc(c);
+    const uint32_t per_row = (uint32_t)(kc * B);
+    const uint32_t inv = (65536u + per_row - 1) / per_row;
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) {
+      const uint32_t f = 64 * d + lane;
+      const uint32_t row = __umul24(f, inv) >> 16;
+      const uint32_t piece = f - __umul24(row, per_row);
+      off[d] = valid && f < 16u * per_row
+                   ? __umul24(row, row_bytes) + (uint32_t)g0 * 16 * B + piece * 16
+                   : kNoLoad;
+    }
+  };
+  auto load_w = [&]<int BUF>(std::integral_constant<int, BUF>, int cb, const uint32_t* off)
+      __attribute__((always_inline)) {
+    uint8_t* dst = (BUF == 0 ? wl0 : wl1) + wave * WBUF;
+    const uint32_t blk = (uint32_t)(cb * 16) * row_bytes;
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(dst + d * 1024), 16, off[d] + blk, 0, 0, 0);
+  };
+
+  // scales of chunk c for the workgroup's rows -> scw[wave]: one 256-byte
+  // DMA per group, lane i = row i (4 bytes per lane: no load straddles the
+  // end of the resource)
+  auto load_scales = [&](int c) __attribute__((always_inline)) {
+    const int g0 = chunk_g0(c), kc = chunk_kc(c);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const bool ok = c < nch && j < kc && lane < 16 * NCB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&scw[wave][j][0], 4,
+                                               ok ? ((uint32_t)lane * G + g0 + j) * 4 : kNoLoad, 0, 0, 0);
+    }
+  };
+
+  bf16x8 xa[KC][4];
+  auto load_x = [&](int c) __attribute__((always_inline)) {
+    const int g0 = chunk_g0(c), kc = chunk_kc(c);
+    const uint32_t base = (uint32_t)lr * K * 2 + (uint32_t)(g0 * kGroup + 32 * lq) * 2;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const bool ok = c < nch && j < kc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        xa[j][t] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? base + (j * kGroup + 8 * t) * 2 : kNoLoad, 0, 0));
+    }
+  };
+
+  f32x4 acc[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // groups j >= kc (a short chunk) have zero X, so they add exact zeros
+  auto compute = [&]<int BUF>(std::integral_constant<int, BUF>, int cb, int c) __attribute__((always_inline)) {
+    const int kc = chunk_kc(c);
+    const uint8_t* src = (BUF == 0 ? wl0 : wl1) + wave * WBUF + lr * (kc * B * 16) + lq * 4 * B;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      uint32_t r[B];
+#pragma unroll
+      for (int e = 0; e < B; ++e) r[e] = reinterpret_cast<const uint32_t*>(src + j * 16 * B)[e];
+      const float s = scw[wave][min(j, kc - 1)][cb * 16 + lr];
+      const float nsh = -(float)(1 << (B - 1)) * s;
+      uint32_t be1[B];
+      if constexpr (B != 4) plus_one_words<B>(r, be1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t x1 = B == 4 ? r[t] + 0x11111111u : 0u;
+        acc[cb][t & 1] = mfma16x16x32(xa[j][t], dequant8_p1<B>(be1, x1, t, s, nsh), acc[cb][t & 1]);
+      }
+    }
+  };
+
+  // Block (c, cb) uses weight buffer (c * NCB + cb) & 1; with NCB odd the
+  // chunk loop is unrolled by two so that every buffer index is static.
+  constexpr int CU = (NCB & 1) ? 2 : 1;
+  using std::integral_constant;
+  uint32_t off_cur[NDMA], off_next[NDMA];
+  chunk_offsets(0, off_cur);
+  load_w(integral_constant<int, 0>{}, 0, off_cur);
+  auto block = [&]<int U, int CB>(integral_constant<int, U>, integral_constant<int, CB>, int c)
+      __attribute__((always_inline)) {
+    constexpr int cur = (U * NCB + CB) & 1;
+    if constexpr (CB + 1 < NCB) {
+      load_w(integral_constant<int, cur ^ 1>{}, CB + 1, off_cur);
+    } else {
+      chunk_offsets(c + 1, off_next);
+      load_w(integral_constant<int, cur ^ 1>{}, 0, off_next);
+    }
+    // the scheduler would otherwise mix blocks (and their register reuse)
+    __builtin_amdgcn_sched_barrier(0);
+    if (c < nch) compute(integral_constant<int, cur>{}, CB, c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto chunk_body = [&]<int U>(integral_constant<int, U> u, int c) __attribute__((always_inline)) {
+    load_scales(c);
+    load_x(c);
+    __builtin_amdgcn_sched_barrier(0);
+    [&]<int... CB>(std::integer_sequence<int, CB...>) __attribute__((always_inline)) {
+      (block(u, integral_constant<int, CB>{}, c), ...);
+    }(std::make_integer_sequence<int, NCB>{});
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) off_cur[d] = off_next[d];
+  };
+  for (int c0 = 0; c0 < nch; c0 += CU) {
+    [&]<int... U>(std::integer_sequence<int, U...>) __attribute__((always_inline)) {
+      (chunk_body(integral_constant<int, U>{}, c0 + U), ...);
+    }(std::make_integer_sequence<int, CU>{});
+  }
+
+  // sum the 8 partial tiles of each column block; wave cb finishes block cb
+  // (the reduction reuses the first weight buffer: every DMA must have landed)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(wl0);     // [NW][NCB][64]
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    f32x4 v = acc[cb][0];
+    v[0] += acc[cb][1][0]; v[1] += acc[cb][1][1]; v[2] += acc[cb][1][2]; v[3] += acc[cb][1][3];
+    red[(wave * NCB + cb) * 64 + lane] = v;
+  }
+  __syncthreads();
+  if (wave >= NCB) return;
+  const int cb = wave;
+  f32x4 tot = red[cb * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    const f32x4 v = red[(w * NCB + cb) * 64 + lane];
+    tot[0] += v[0]; tot[1] += v[1]; tot[2] += v[2]; tot[3] += v[3];
+  }
+  const int n = min(n0 + cb * 16 + lr, args.n - 1);
+  if (args.t != nullptr) {
+    const int R_ = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int j0 = 0; j0 < R_; j0 += 32) {
+      const int kk = j0 + 8 * lq;
+      const bool kok = kk < R_;
+      const int kc = min(kk, R_ - 8);
+      const bf16x8 bl = kok ? *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R_ + kc) : zero;
+      const int m = min(lr, args.m - 1);
+      const bf16x8 vt = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R_ + kc);
+      tot = mfma16x16x32(kok ? vt : zero, bl, tot);
+    }
+  }
+  if (args.out_bf16)
+    store_tile<true>(args.y, args.n, 4 * lq, n0 + cb * 16 + lr, args.m, args.n, tot);
+  else
+    store_tile<false>(args.y, args.n, 4 * lq, n0 + cb * 16 + lr, args.m, args.n, tot);
 }
 
 // ---------------------------------------------------------------------------

@@ -23,6 +23,9 @@ hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t stream);
 template <int B>
 hipError_t launch_gemm_small(const GemmArgs& a, int rb, int nc, int nk, hipStream_t stream);
 
+template <int B>
+hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t stream);
+
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
 

@@ -55,4 +55,20 @@ hipError_t launch_gemm_small<DDG_BITS>(const GemmArgs& a, int rb, int nc, int nk
   return hipErrorInvalidValue;
 }
 
+template <>
+hipError_t launch_gemm_skinny<DDG_BITS>(const GemmArgs& a, int kc, int ncb, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n + 16 * ncb - 1) / (16 * ncb)));
+  if (skinny_static_lds(DDG_BITS, kc, ncb) + skinny_scale_lds(kc) > kLdsLimit) return hipErrorInvalidValue;
+#define DDG_SKINNY(KC, NCB)                                                       \
+  if (kc == KC && ncb == NCB) {                                                   \
+    gemm_skinny_kernel<DDG_BITS, KC, NCB><<<grid, dim3(512), 0, stream>>>(a);    \
+    return hipGetLastError();                                                     \
+  }
+  DDG_SKINNY(3, 1) DDG_SKINNY(3, 2) DDG_SKINNY(3, 4)
+  DDG_SKINNY(4, 1) DDG_SKINNY(4, 2) DDG_SKINNY(4, 4)
+  DDG_SKINNY(5, 1) DDG_SKINNY(5, 2) DDG_SKINNY(5, 4)
+#undef DDG_SKINNY
+  return hipErrorInvalidValue;
+}
+
 }  // namespace ddg

@@ -123,6 +123,24 @@ def test_gemm_ragged_shapes(gpu_lib, bits, m):
         check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
 
 
+# M <= 16 with a wide output (N >= 12800) runs the weight-streaming kernel:
+# K from one group (7 of 8 K-split waves idle) to 108 groups (several chunks
+# per wave, a short last chunk), N with a partial last workgroup, M < 16.
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m,n,k", [(16, 12800, 128), (1, 12816, 640), (7, 12816, 3328),
+                                   (16, 12864, 5120), (16, 12816, 13824)])
+def test_gemm_wide_small_m(gpu_lib, bits, m, n, k):
+    if k == 13824 and bits not in (3, 7):
+        pytest.skip("the 108-group case runs at the narrowest and widest code")
+    _case(f"dequant_gemm wide small-M m={m} n={n} k={k} bits={bits}")
+    c = synth.random_case(m * 131 + n + k + bits, m, n, k)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+    y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], bits))
+    xd = dev_bf16(c["x"])
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32)), y_ref, False, "f32")
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
+
+
 def test_gemm_empty_batch_leaves_output(gpu_lib):
     _case("dequant_gemm m=0")
     c = synth.random_case(1, 4, 32, 128)
@@ -210,6 +228,13 @@ def test_lowrank_small_shapes(gpu_lib, r, m):
     c = synth.random_case(r * 100 + m, m, 144, 384, wstd=0.05)
     _lowrank_case(gpu_lib, c["x"], c["w"], 4, r)
     _lowrank_case(gpu_lib, c["x"], c["w"], 5, r, out=torch.bfloat16)
+
+
+def test_lowrank_wide_small_m(gpu_lib):
+    _case("lowrank_fused_gemm wide small-M m=16 n=12816 k=640 r=32")
+    c = synth.random_case(4242, 16, 12816, 640, wstd=0.05)
+    _lowrank_case(gpu_lib, c["x"], c["w"], 5, 32)
+    _lowrank_case(gpu_lib, c["x"][:3], c["w"], 4, 32, out=torch.bfloat16)
 
 
 def test_lowrank_config4(gpu_lib):
