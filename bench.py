@@ -9,16 +9,25 @@ Inputs are resident in HBM before timing.  Each step uses other copies of
 the weights (round robin over enough copies to exceed 1 GiB, 4x the 256 MB
 last-level cache), so the M=16 product streams its packed weights from HBM.
 
-value = dequant-GEMM TFLOP/s at M=4096 (2*M*N*K / mean kernel time, HIP
-events on the launch stream); the JSON line also carries the M=16 packed-
-weight GB/s, the quantize/pack GB/s, the roofline of the dominant kernel and
-the CPU oracle timed on a bounded sample.
+Timing, all with HIP events on the stream the kernels are launched on:
+  * ms_per_step: K whole steps back to back between two events (plus a
+    device synchronize on both sides);
+  * per-kernel averages: for each of the three launches, K launches of that
+    kernel alone back to back between two events, divided by K.  This is the
+    kernel's own duration (what rocprofv3 --kernel-trace reports per launch),
+    without the dispatch gap an event pair around a single launch includes.
+value = dequant-GEMM TFLOP/s at M=4096 (2*M*N*K / its average duration); the
+JSON line also carries the M=16 packed-weight GB/s, the quantize/pack GB/s,
+the roofline of the dominant kernel and the CPU oracle timed on a bounded
+sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --suite block16     (the four linears of a DiT block at M=16)
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -46,6 +55,10 @@ def parse():
                                                       "dequant_gemm_attnproj3072_traffic.md"),
                     help="profile summary holding the measured HBM bytes per launch of the "
                          "dominant kernel (used only while the kernel sources are unchanged)")
+    ap.add_argument("--suite", choices=["block16"], default=None,
+                    help="block16: instead of the bench line, time the four linears of a "
+                         "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
+                         "one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -85,6 +98,47 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 3}), flush=True)
+
+
+def block16_suite(steps, warmup):
+    """The four linears of one DiT block at M = 16 tokens: packed-weight GB/s
+    of each product, K back-to-back launches over >= 1 GiB of weight copies."""
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    bits_of = synth.config5_bits()
+    for name in ("qkv", "o", "up", "down"):
+        bits = bits_of[name]
+        n, k = synth.C5_SHAPES[name]
+        w = torch.from_numpy(synth.config5_weights(name)).to(dev, torch.bfloat16)
+        x = torch.from_numpy(synth.config5_x(name, 16)).to(dev, torch.bfloat16)
+        q0 = api.quantize_pack(w, bits)
+        del w
+        nbytes = q0.packed.numel() + q0.scales.numel() * 4
+        copies = max(2, -(-ROTATE_BYTES // nbytes))
+        qs = [q0] + [dataclasses.replace(q0, packed=q0.packed.clone(), scales=q0.scales.clone())
+                     for _ in range(copies - 1)]
+        y = torch.empty((16, n), dtype=torch.bfloat16, device=dev)
+        for i in range(warmup):
+            api.dequant_gemm(x, qs[i % copies], out=y)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            api.dequant_gemm(x, qs[(warmup + i) % copies], out=y)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({"suite": "dit-block-m16", "linear": name, "n": n, "k": k, "bits": bits,
+                          "m": 16, "us": round(ms * 1e3, 2), "packed_weight_GBps": round(gbps, 1),
+                          "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                          "weight_copies_rotated": copies, "steps": steps}), flush=True)
+        del qs, q0, x, y
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(w, x, budget_s):
@@ -146,6 +200,9 @@ def main():
     api.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.suite == "block16":
+        block16_suite(args.steps, args.warmup)
+        return
 
     c = synth.config2(m=M_BIG)
     w_np, x_np = c["w"], c["x"]
@@ -169,36 +226,51 @@ def main():
         if st:
             raise api.DDGError(st, "ddg_quantize_pack")
 
-    ev = {k: [] for k in ("q0", "q1", "g0", "g1", "s0", "s1")}
+    stream = torch.cuda.current_stream()
 
-    def step(i, record):
-        j = i % n_copies
-        far = (i + n_copies // 2) % n_copies        # packed weights not touched for a while
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
-        if record: e[0].record()
-        quantize_into(j)
-        if record: e[1].record(); e[2].record()
-        api.dequant_gemm(x_big, qws[j], out=y_big)
-        if record: e[3].record(); e[4].record()
-        api.dequant_gemm(x_small, qws[far], out=y_small)
-        if record:
-            e[5].record()
-            for k, evt in zip(("q0", "q1", "g0", "g1", "s0", "s1"), e):
-                ev[k].append(evt)
+    def gemm_big(i):
+        api.dequant_gemm(x_big, qws[i % n_copies], out=y_big)
+
+    def gemm_small(i):
+        # packed weights not touched for a while (the big product of step i
+        # reads copy i): M=16 streams them from HBM
+        api.dequant_gemm(x_small, qws[(i + n_copies // 2) % n_copies], out=y_small)
+
+    def step(i):
+        quantize_into(i % n_copies)
+        gemm_big(i)
+        gemm_small(i)
+
+    def burst_ms(fn, count, offset):
+        """Average duration of `count` back-to-back launches of fn."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(count):
+            fn(offset + i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / count
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        step(args.warmup + i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
 
-    def mean_ms(a, b):
-        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+    base = args.warmup + args.steps
+    t_q = burst_ms(lambda i: quantize_into(i % n_copies), args.steps, base)
+    t_g = burst_ms(gemm_big, args.steps, base)
+    t_s = burst_ms(gemm_small, args.steps, base)
 
-    t_q, t_g, t_s = mean_ms("q0", "q1"), mean_ms("g0", "g1"), mean_ms("s0", "s1")
     flops = 2.0 * M_BIG * N * K
     tflops = flops / (t_g * 1e-3) / 1e12
     gbps_small = (p_bytes + s_bytes) / (t_s * 1e-3) / 1e9
@@ -213,7 +285,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -227,6 +299,7 @@ def main():
         },
         "kernels_ms": {"quantize_pack": round(t_q, 5), "dequant_gemm_m4096": round(t_g, 5),
                        "dequant_gemm_m16": round(t_s, 5)},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "m16_packed_weight_GBps": round(gbps_small, 2),
         "m16_frac_of_hbm_peak": round(gbps_small / PEAK_HBM_GBPS, 4),
         "quantize_pack_GBps": round(gbps_q, 2),
