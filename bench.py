@@ -13,9 +13,10 @@ Timing, all with HIP events on the stream the kernels are launched on:
   * ms_per_step: K whole steps back to back between two events (plus a
     device synchronize on both sides);
   * per-kernel averages: for each of the three launches, K launches of that
-    kernel alone back to back between two events, divided by K.  This is the
-    kernel's own duration (what rocprofv3 --kernel-trace reports per launch),
-    without the dispatch gap an event pair around a single launch includes.
+    kernel alone back to back between two events, divided by K, the median
+    of 5 such bursts.  This is the kernel's own duration (what rocprofv3
+    --kernel-trace reports per launch), without the dispatch gap an event
+    pair around a single launch includes.
 value = dequant-GEMM TFLOP/s at M=4096 (2*M*N*K / its average duration); the
 JSON line also carries the M=16 packed-weight GB/s, the quantize/pack GB/s,
 the roofline of the dominant kernel and the CPU oracle timed on a bounded
@@ -40,6 +41,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 M_BIG, M_SMALL, N, K, BITS = 4096, 16, 3072, 3072, 4
+REPEATS = 5
 ROTATE_BYTES = 1 << 30
 
 
@@ -141,6 +143,35 @@ def block16_suite(steps, warmup):
         torch.cuda.empty_cache()
 
 
+def system_info(torch):
+    """GPU name, clock and ROCm build; host CPU model."""
+    info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+            "torch": torch.__version__}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        info["gcn_arch"] = props.gcnArchName
+        info["compute_units"] = props.multi_processor_count
+        rate = getattr(props, "clock_rate", None)
+        if rate:
+            info["max_clock_mhz"] = round(rate / 1000.0)
+    except Exception:                                   # pragma: no cover
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            info["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(w, x, budget_s):
     """The oracle as it stands on the host: quantize + pack + dequantize the
     whole weight, then the float64 product over row chunks of X until the time
@@ -148,9 +179,13 @@ def cpu_baseline(w, x, budget_s):
     import numpy as np
 
     import oracle as O
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        pools = threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in pools] + [1])
+        blas = [f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)"
+                for d in pools if d.get("user_api") == "blas"]
     except Exception:                                   # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
@@ -177,6 +212,7 @@ def cpu_baseline(w, x, budget_s):
                    f"oracle's dequantized 3072x3072 weight ({t_g:.1f} s); oracle quantize+pack of the "
                    f"whole weight {t_q:.2f} s = {q_bytes / t_q / 1e9:.3f} GB/s (1 thread)"),
         "affinity_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas,
     }
 
 
@@ -266,10 +302,23 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # per-kernel averages: median over REPEATS bursts of `steps` launches each
     base = args.warmup + args.steps
-    t_q = burst_ms(lambda i: quantize_into(i % n_copies), args.steps, base)
-    t_g = burst_ms(gemm_big, args.steps, base)
-    t_s = burst_ms(gemm_small, args.steps, base)
+    reps = {"q": [], "g": [], "s": []}
+    for r in range(REPEATS):
+        off = base + r * args.steps
+        reps["q"].append(burst_ms(lambda i: quantize_into(i % n_copies), args.steps, off))
+        reps["g"].append(burst_ms(gemm_big, args.steps, off))
+        reps["s"].append(burst_ms(gemm_small, args.steps, off))
+    t_q, t_g, t_s = (float(np.median(reps[k])) for k in ("q", "g", "s"))
+
+    # context, not a target: torch's dense bf16 product of the same shape on
+    # the dequantized weight (no dequantization inside)
+    w_t = api.dequantize(qws[0]).t().contiguous()       # K x N, a plain row-major operand
+    for _ in range(3):
+        torch.matmul(x_big, w_t)
+    t_dense = burst_ms(lambda i: torch.matmul(x_big, w_t), args.steps, 0)
+    del w_t
 
     flops = 2.0 * M_BIG * N * K
     tflops = flops / (t_g * 1e-3) / 1e12
@@ -299,6 +348,11 @@ def main():
         },
         "kernels_ms": {"quantize_pack": round(t_q, 5), "dequant_gemm_m4096": round(t_g, 5),
                        "dequant_gemm_m16": round(t_s, 5)},
+        "kernels_ms_repeats": {k: [round(v, 5) for v in reps[k2]]
+                               for k, k2 in (("quantize_pack", "q"), ("dequant_gemm_m4096", "g"),
+                                             ("dequant_gemm_m16", "s"))},
+        "context_torch_matmul_bf16_dense_TFLOPs": round(flops / (t_dense * 1e-3) / 1e12, 1),
+        "system": system_info(torch),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "m16_packed_weight_GBps": round(gbps_small, 2),
         "m16_frac_of_hbm_peak": round(gbps_small / PEAK_HBM_GBPS, 4),
