@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--suite", choices=["block16"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
-                         "one JSON line each")
+                         "one by one and grouped, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -104,43 +104,77 @@ def copy_calibration():
 
 def block16_suite(steps, warmup):
     """The four linears of one DiT block at M = 16 tokens: packed-weight GB/s
-    of each product, K back-to-back launches over >= 1 GiB of weight copies."""
+    of each product (K back-to-back launches over >= 1 GiB of weight copies),
+    then the same four as one grouped call, and q, k, v as three 5120x5120
+    tensors of different widths, one by one and grouped."""
     import torch
 
     from dit_dequant_gemm_amd import api, synth
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    bits_of = synth.config5_bits()
-    for name in ("qkv", "o", "up", "down"):
-        bits = bits_of[name]
-        n, k = synth.C5_SHAPES[name]
-        w = torch.from_numpy(synth.config5_weights(name)).to(dev, torch.bfloat16)
-        x = torch.from_numpy(synth.config5_x(name, 16)).to(dev, torch.bfloat16)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def resident(w_np, x_np, bits):
+        """Weight copies totalling >= 1 GiB, X, Y for one linear."""
+        w = torch.from_numpy(w_np).to(dev, torch.bfloat16)
         q0 = api.quantize_pack(w, bits)
         del w
         nbytes = q0.packed.numel() + q0.scales.numel() * 4
         copies = max(2, -(-ROTATE_BYTES // nbytes))
         qs = [q0] + [dataclasses.replace(q0, packed=q0.packed.clone(), scales=q0.scales.clone())
                      for _ in range(copies - 1)]
-        y = torch.empty((16, n), dtype=torch.bfloat16, device=dev)
-        for i in range(warmup):
-            api.dequant_gemm(x, qs[i % copies], out=y)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            api.dequant_gemm(x, qs[(warmup + i) % copies], out=y)
-        e1.record(stream)
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        print(json.dumps({"suite": "dit-block-m16", "linear": name, "n": n, "k": k, "bits": bits,
-                          "m": 16, "us": round(ms * 1e3, 2), "packed_weight_GBps": round(gbps, 1),
-                          "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                          "weight_copies_rotated": copies, "steps": steps}), flush=True)
-        del qs, q0, x, y
-        torch.cuda.empty_cache()
+        x = torch.from_numpy(x_np).to(dev, torch.bfloat16)
+        y = torch.empty((16, q0.n), dtype=torch.bfloat16, device=dev)
+        return {"qs": qs, "x": x, "y": y, "bytes": nbytes, "bits": bits, "n": q0.n, "k": q0.k}
+
+    def line(name, lins, us):
+        nbytes = sum(L["bytes"] for L in lins)
+        gbps = nbytes / (us * 1e-3) / 1e9
+        print(json.dumps({"suite": "dit-block-m16", "linear": name,
+                          "shapes": [f"{L['n']}x{L['k']}@{L['bits']}b" for L in lins], "m": 16,
+                          "us": round(us * 1e3, 2), "packed_weight_GBps": round(gbps, 1),
+                          "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "steps": steps}),
+              flush=True)
+
+    def seq(lins):
+        def fn(i):
+            for L in lins:
+                api.dequant_gemm(L["x"], L["qs"][i % len(L["qs"])], out=L["y"])
+        return fn
+
+    def grouped(lins):
+        def fn(i):
+            api.dequant_gemm_grouped([(L["x"], L["qs"][i % len(L["qs"])], L["y"]) for L in lins])
+        return fn
+
+    bits_of = synth.config5_bits()
+    block = []
+    for name in ("qkv", "o", "up", "down"):
+        L = resident(synth.config5_weights(name), synth.config5_x(name, 16), bits_of[name])
+        line(name, [L], timed(seq([L])))
+        block.append(L)
+    line("qkv+o+up+down one by one", block, timed(seq(block)))
+    line("qkv+o+up+down grouped", block, timed(grouped(block)))
+    del block
+    torch.cuda.empty_cache()
+    # q, k, v as separate tensors (rows of the fused qkv weight) at 5, 6, 4 bits
+    w = synth.config5_weights("qkv")
+    x = synth.config5_x("qkv", 16)
+    qkv = [resident(w[5120 * i:5120 * (i + 1)], x, b) for i, b in enumerate((5, 6, 4))]
+    line("q,k,v (5,6,4 bits) one by one", qkv, timed(seq(qkv)))
+    line("q,k,v (5,6,4 bits) grouped", qkv, timed(grouped(qkv)))
 
 
 def system_info(torch):

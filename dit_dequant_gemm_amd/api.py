@@ -27,6 +27,15 @@ DDG_BF16, DDG_F32 = 0, 1
 
 # entry point -> (restype, argtypes)
 _c_i64, _c_int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
+class GemmDesc(ctypes.Structure):
+    """ddg_gemm_desc: one product of a grouped call."""
+    _fields_ = [("x", _vp), ("packed", _vp), ("scales", _vp), ("y", _vp),
+                ("m", _c_i64), ("k", _c_i64), ("n", _c_i64), ("bits", _c_int), ("y_dtype", _c_int)]
+
+
+MAX_GROUPED = 256
 SIGNATURES = {
     "ddg_version": (_c_int, []),
     "ddg_status_string": (ctypes.c_char_p, [_c_int]),
@@ -34,6 +43,7 @@ SIGNATURES = {
     "ddg_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
     "ddg_dequantize": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp]),
     "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
+    "ddg_dequant_gemm_grouped": (_c_int, [ctypes.POINTER(GemmDesc), _c_int, _vp]),
     "ddg_lowrank_workspace_bytes": (_c_int, [_c_i64, _c_int, ctypes.POINTER(_sz)]),
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
@@ -187,6 +197,30 @@ def dequant_gemm(x: torch.Tensor, qw: QWeight, out_dtype=torch.bfloat16,
         qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
         _stream_ptr(x.device)), "ddg_dequant_gemm")
     return y
+
+
+def dequant_gemm_grouped(items, out_dtype=torch.bfloat16):
+    """Several independent products Y_i = X_i @ w_hat_i^T in as few launches
+    as possible.  items: sequence of (x, qw) or (x, qw, out); returns the
+    list of outputs.  All tensors on the same device; the current stream."""
+    items = list(items)
+    if not items:
+        return []
+    descs = (GemmDesc * len(items))()
+    outs, keep = [], []
+    for i, it in enumerate(items):
+        x, qw = it[0], it[1]
+        out = it[2] if len(it) > 2 else None
+        x = _prep_x(x, qw)
+        y = _out(x, qw.n, out_dtype, out)
+        keep.append(x)
+        outs.append(y)
+        descs[i] = GemmDesc(x.data_ptr(), qw.packed.data_ptr(), qw.scales.data_ptr(), y.data_ptr(),
+                            x.shape[0], qw.k, qw.n, qw.bits,
+                            DDG_F32 if y.dtype == torch.float32 else DDG_BF16)
+    _check(load_library().ddg_dequant_gemm_grouped(descs, len(items), _stream_ptr(outs[0].device)),
+           "ddg_dequant_gemm_grouped")
+    return outs
 
 
 def lowrank_workspace_bytes(m: int, r: int) -> int:

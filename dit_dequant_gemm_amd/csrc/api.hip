@@ -1,5 +1,6 @@
 // C ABI of libddg (declared in include/ddg.h): argument validation on the
 // host, kernel choice, launch.  No allocation, no synchronization.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -98,6 +99,19 @@ int check_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed, const
   return DDG_OK;
 }
 
+// Groups per wave chunk of the M <= 16 weight-streaming kernels for K = 128 g:
+// the size (5, 4 or 3) that pads the busiest wave's share of K (ceil(g / 8)
+// groups) with the fewest empty groups.
+int skinny_chunk(int g) {
+  const int per_wave = (g + 7) / 8;
+  int kc = 5, waste = 1 << 30;
+  for (int c = 5; c >= 3; --c) {
+    const int w = (per_wave + c - 1) / c * c - per_wave;
+    if (w < waste) { waste = w; kc = c; }
+  }
+  return kc;
+}
+
 // Kernel choice for the product; fills a.tiles_* for the large kernel.
 hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t stream) {
   if (a.m <= 16) {
@@ -109,14 +123,7 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t strea
     const int g = a.k / DDG_GROUP;
     if (nb / 4 >= 200) {
       int ncb = 4;
-      // groups per wave chunk: the size (5, 4 or 3) that pads the busiest
-      // wave's share of K (ceil(G / 8) groups) with the fewest empty groups
-      const int per_wave = (g + 7) / 8;
-      int kc = 5, waste = 1 << 30;
-      for (int c = 5; c >= 3; --c) {
-        const int w = (per_wave + c - 1) / c * c - per_wave;
-        if (w < waste) { waste = w; kc = c; }
-      }
+      int kc = skinny_chunk(g);
       // shrink until the weight buffers and the scale areas fit in LDS
       auto lds = [&] { return ddg::skinny_static_lds(bits, kc, ncb) + ddg::skinny_scale_lds(kc); };
       while (lds() > ddg::kLdsLimit && (ncb > 1 || kc > 3)) {
@@ -218,6 +225,66 @@ int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
   a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = 0;
   a.out_bf16 = y_dtype == DDG_BF16;
   return hip_status(launch_product(a, bits, cus, stream));
+}
+
+int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream) {
+  if (count < 0 || count > DDG_MAX_GROUPED) return DDG_ERR_SHAPE;
+  if (count == 0) return DDG_OK;
+  if (!descs) return DDG_ERR_ARG;
+  int busy = 0;
+  for (int i = 0; i < count; ++i) {
+    const ddg_gemm_desc& d = descs[i];
+    if (int st = check_gemm(d.x, d.m, d.k, d.packed, d.scales, d.bits, d.n, d.y, d.y_dtype))
+      return st;
+    busy += d.m > 0;
+  }
+  if (busy == 0) return DDG_OK;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  auto args_of = [](const ddg_gemm_desc& d) {
+    ddg::GemmArgs a{};
+    a.x = static_cast<const __bf16*>(d.x);
+    a.packed = d.packed;
+    a.scales = d.scales;
+    a.y = d.y;
+    a.t = nullptr;
+    a.lora_up = nullptr;
+    a.m = (int)d.m; a.n = (int)d.n; a.k = (int)d.k; a.r = 0;
+    a.out_bf16 = d.y_dtype == DDG_BF16;
+    return a;
+  };
+  // Products with M <= 16 share launches, longest workgroups first (their
+  // work is about K * bits per workgroup) so that the short ones fill in.
+  int small[DDG_MAX_GROUPED];
+  int n_small = 0;
+  for (int i = 0; i < count; ++i) {
+    if (descs[i].m == 0) continue;
+    if (descs[i].m <= 16) {
+      small[n_small++] = i;
+    } else {
+      ddg::GemmArgs a = args_of(descs[i]);
+      if (hipError_t e = launch_product(a, descs[i].bits, cus, stream)) return hip_status(e);
+    }
+  }
+  std::stable_sort(small, small + n_small, [&](int p, int q) {
+    return descs[p].k * descs[p].bits > descs[q].k * descs[q].bits;
+  });
+  for (int s0 = 0; s0 < n_small; s0 += ddg::kMaxGroup) {
+    ddg::GroupArgs ga{};
+    ga.count = std::min(ddg::kMaxGroup, n_small - s0);
+    ga.wg_start[0] = 0;
+    for (int j = 0; j < ga.count; ++j) {
+      const ddg_gemm_desc& d = descs[small[s0 + j]];
+      ga.g[j] = args_of(d);
+      ga.bits[j] = d.bits;
+      ga.kc[j] = skinny_chunk(d.k / DDG_GROUP);
+      const int64_t wgs = (d.n + 16 * ddg::kGroupedNcb - 1) / (16 * ddg::kGroupedNcb);
+      if (ga.wg_start[j] + wgs > kMaxDim) return DDG_ERR_SHAPE;
+      ga.wg_start[j + 1] = ga.wg_start[j] + (int)wgs;
+    }
+    if (hipError_t e = ddg::launch_gemm_grouped(ga, stream)) return hip_status(e);
+  }
+  return DDG_OK;
 }
 
 int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes) {

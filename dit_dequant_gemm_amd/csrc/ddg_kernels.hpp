@@ -644,25 +644,36 @@ __host__ __device__ constexpr size_t skinny_static_lds(int b, int kc, int ncb) {
 __host__ __device__ constexpr size_t skinny_scale_lds(int kc) { return (size_t)8 * kc * 64 * 4; }
 constexpr size_t kLdsLimit = 160 * 1024;
 
+// LDS layout of the skinny kernel body: two weight buffers (separate arrays,
+// so that the compiler can tell that a DMA into one does not feed reads of
+// the other, and does not wait for it; the first also holds the final
+// reduction) and the per-wave scale areas [wave][group j][row].
 template <int B, int KC, int NCB>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs args) {
-  constexpr int NW = 8;                  // waves = K splits
+struct SkinnyLds {
+  static constexpr int NW = 8;
+  static constexpr int NDMA = (KC * B + 3) / 4;       // 1 KB DMA instructions per wave per block
+  static constexpr int WBUF = NDMA * 1024;
+  static constexpr int RED = NW * NCB * 64 * 16;
+  static constexpr int W0 = NW * WBUF >= RED ? NW * WBUF : RED;
+  static constexpr int W1 = NW * WBUF;
+};
+
+// Workgroup wg of the product `args` (see the comment above).  wl0, wl1 and
+// scw are LDS arrays of at least SkinnyLds<B, KC, NCB>::W0, ::W1 bytes and
+// [8][KC][64] floats.
+template <int B, int KC, int NCB>
+__device__ __forceinline__ void skinny_body(const GemmArgs& args, int wg, uint8_t* wl0, uint8_t* wl1,
+                                            float (*scw)[KC][64]) {
+  constexpr int NW = SkinnyLds<B, KC, NCB>::NW;       // waves = K splits
   constexpr uint32_t kNoLoad = 0x80000000u;
-  constexpr int NDMA = (KC * B + 3) / 4; // 1 KB DMA instructions per wave per block
-  constexpr int WBUF = NDMA * 1024;
-  constexpr int RED = NW * NCB * 64 * 16;
-  // Two weight buffers as two arrays: the compiler can then tell that a DMA
-  // into one does not feed reads of the other, and does not wait for it.
-  __shared__ __attribute__((aligned(1024))) uint8_t wl0[NW * WBUF >= RED ? NW * WBUF : RED];
-  __shared__ __attribute__((aligned(1024))) uint8_t wl1[NW * WBUF];
-  // this wave's scales for the current chunk: [group j][row of the workgroup]
-  __shared__ __attribute__((aligned(256))) float scw[NW][KC][64];
+  constexpr int NDMA = SkinnyLds<B, KC, NCB>::NDMA;
+  constexpr int WBUF = SkinnyLds<B, KC, NCB>::WBUF;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int K = args.k, G = K / kGroup;
-  const int n0 = blockIdx.x * 16 * NCB;
+  const int n0 = wg * 16 * NCB;
   // (wave-uniform: kept in scalar registers)
   const int gs = __builtin_amdgcn_readfirstlane(wave * G / NW);
   const int cnt = __builtin_amdgcn_readfirstlane((wave + 1) * G / NW) - gs;
@@ -835,6 +846,36 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs args) {
   else
     store_tile<false>(args.y, args.n, 4 * lq, n0 + cb * 16 + lr, args.m, args.n, tot);
 }
+
+template <int B, int KC, int NCB>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs args) {
+  using L = SkinnyLds<B, KC, NCB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t wl0[L::W0];
+  __shared__ __attribute__((aligned(1024))) uint8_t wl1[L::W1];
+  __shared__ __attribute__((aligned(256))) float scw[L::NW][KC][64];
+  skinny_body<B, KC, NCB>(args, blockIdx.x, wl0, wl1, scw);
+}
+
+// ---------------------------------------------------------------------------
+// K3g: several independent products with M <= 16 (mixed bit widths) in one
+// launch -- e.g. the q, k and v projections of a block quantized to
+// different widths, which cannot share one packed tensor.  Workgroup i runs
+// workgroup i - wg_start[j] of product j (wg_start is a prefix sum over the
+// products' workgroup counts); the body is the K3s one, chosen per product
+// by bit width and chunk size.  The LDS arrays are sized for the widest case.
+// ---------------------------------------------------------------------------
+constexpr int kMaxGroup = 16;
+constexpr int kGroupedNcb = 4;
+
+struct GroupArgs {
+  GemmArgs g[kMaxGroup];
+  int wg_start[kMaxGroup + 1];
+  int bits[kMaxGroup];
+  int kc[kMaxGroup];
+  int count;
+};
+
+// gemm_grouped_skinny_kernel(GroupArgs) is defined in grouped.hip.
 
 // ---------------------------------------------------------------------------
 // K4: T = bf16(X * L1), with L1^T = lora_down (R x K) -- computed as

@@ -26,6 +26,10 @@ hipError_t launch_gemm_small(const GemmArgs& a, int rb, int nc, int nk, hipStrea
 template <int B>
 hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t stream);
 
+// up to kMaxGroup products with M <= 16 in one launch (ga.wg_start is the
+// prefix sum of ceil(n / (16 kGroupedNcb)) over the products)
+hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream);
+
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
 

@@ -1,0 +1,42 @@
+// Launcher of the grouped small-M product (all bit widths in one kernel).
+#include "ddg_launch.hpp"
+
+namespace ddg {
+
+__global__ __launch_bounds__(512) void gemm_grouped_skinny_kernel(GroupArgs ga) {
+  constexpr int NCB = kGroupedNcb;
+  using L = SkinnyLds<7, 5, NCB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t wl0[L::W0];
+  __shared__ __attribute__((aligned(1024))) uint8_t wl1[L::W1];
+  __shared__ __attribute__((aligned(256))) float scw_mem[L::NW * 5 * 64];
+  const int bid = blockIdx.x;
+  int j = 0;
+  while (j + 1 < ga.count && bid >= ga.wg_start[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const int wg = bid - ga.wg_start[j];
+  const int bits = ga.bits[j], kc = ga.kc[j];
+  auto run = [&]<int B, int KC>() __attribute__((always_inline)) {
+    skinny_body<B, KC, NCB>(ga.g[j], wg, wl0, wl1, reinterpret_cast<float (*)[KC][64]>(scw_mem));
+  };
+#define DDG_GROUPED_CASE(B)                      \
+  case B:                                        \
+    if (kc == 3) run.template operator()<B, 3>(); \
+    else if (kc == 4) run.template operator()<B, 4>(); \
+    else run.template operator()<B, 5>();        \
+    break;
+  switch (bits) {
+    DDG_GROUPED_CASE(3) DDG_GROUPED_CASE(4) DDG_GROUPED_CASE(5) DDG_GROUPED_CASE(6) DDG_GROUPED_CASE(7)
+  }
+#undef DDG_GROUPED_CASE
+}
+
+
+hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream) {
+  if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
+  const int wgs = ga.wg_start[ga.count];
+  if (wgs <= 0) return hipSuccess;
+  gemm_grouped_skinny_kernel<<<dim3((unsigned)wgs), dim3(512), 0, stream>>>(ga);
+  return hipGetLastError();
+}
+
+}  // namespace ddg

@@ -127,6 +127,38 @@ int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                      const float* scales, int bits, int64_t n, void* y, int y_dtype,
                      hipStream_t stream);
 
+/* One product of a grouped call: y = x * w_hat^T, arguments as in
+ * ddg_dequant_gemm. */
+typedef struct ddg_gemm_desc {
+  const void* x;            /* M x K bf16                                   */
+  const uint8_t* packed;    /* record of an N x K weight at `bits`          */
+  const float* scales;
+  void* y;                  /* M x N, y_dtype                               */
+  int64_t m, k, n;
+  int bits;
+  int y_dtype;
+} ddg_gemm_desc;
+
+#define DDG_MAX_GROUPED 256   /* products per ddg_dequant_gemm_grouped call */
+
+/*
+ * Several independent products in as few launches as possible ([WDQ] §1.3
+ * and §3.4: packed weights stay resident and are dequantized per block on
+ * the fly; §3.2: each tensor gets its own bit width, so e.g. the q, k and v
+ * projections of a block cannot share one packed tensor).  Equivalent to
+ * ddg_dequant_gemm on every descriptor, with every requirement of that call.
+ * Products with M <= 16 go into one launch per 16 products (mixed bit widths
+ * and shapes); the others are launched one by one on the same stream.
+ *   descs   host array of `count` descriptors, read during the call only.
+ *   count   0 .. DDG_MAX_GROUPED (0 is a no-op).
+ * No y may overlap another product's inputs or output.  Results equal those
+ * of separate calls up to floating-point summation order.
+ * Errors: as ddg_dequant_gemm, for the first failing descriptor (nothing is
+ * launched then), DDG_ERR_ARG for a null descs with count > 0, DDG_ERR_SHAPE
+ * for count outside 0..DDG_MAX_GROUPED.
+ */
+int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream);
+
 /*
  * Workspace bytes ddg_lowrank_fused_gemm needs for M rows and rank r
  * (the M x r bf16 intermediate T, rounded up to 256 bytes).  Host-only.

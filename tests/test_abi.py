@@ -126,6 +126,32 @@ def test_dequant_gemm_rejects_bad_arguments(lib):
     assert g(None, 0, 128, None, None, 4, 32, None, 0, None) == OK          # M == 0
 
 
+def test_grouped_gemm_rejects_bad_arguments(lib):
+    g = lib.ddg_dequant_gemm_grouped
+    D = api.GemmDesc
+
+    def descs(*items):
+        arr = (D * len(items))()
+        for i, kw in enumerate(items):
+            base = dict(x=FAKE, packed=FAKE, scales=FAKE, y=FAKE, m=4, k=128, n=32, bits=4, y_dtype=0)
+            base.update(kw)
+            arr[i] = D(**base)
+        return arr
+
+    assert g(None, 0, None) == OK                                   # empty group
+    assert g(None, 2, None) == E_ARG
+    assert g(descs({}), -1, None) == E_SHAPE
+    assert g(descs({}), api.MAX_GROUPED + 1, None) == E_SHAPE
+    # every descriptor is checked before anything runs; the first bad one decides
+    assert g(descs({}, {"bits": 8}), 2, None) == E_ARG
+    assert g(descs({}, {"k": 100}), 2, None) == E_SHAPE
+    assert g(descs({"n": 24}, {"bits": 8}), 2, None) == E_SHAPE
+    assert g(descs({}, {"y": None}), 2, None) == E_ARG
+    assert g(descs({}, {"x": MISALIGNED}), 2, None) == E_ALIGN
+    assert g(descs({}, {"y_dtype": 3}), 2, None) == E_ARG
+    assert g(descs({"m": 0, "x": None, "y": None, "packed": None, "scales": None}), 1, None) == OK
+
+
 def test_lowrank_fused_gemm_rejects_bad_arguments(lib):
     f = lib.ddg_lowrank_fused_gemm
     base = [FAKE, 64, 256, FAKE, FAKE, 4, 64, FAKE, FAKE, 32, FAKE, 0, FAKE, 64 * 64, None]

@@ -141,6 +141,57 @@ def test_gemm_wide_small_m(gpu_lib, bits, m, n, k):
     check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
 
 
+# Grouped products: mixed widths, shapes and output dtypes in one call.  Each
+# output is checked against the oracle on its own weight.
+_GROUP_CASES = [
+    # (m, n, k, bits, out dtype)
+    (16, 5120, 640, 5, torch.bfloat16),
+    (16, 272, 640, 6, torch.float32),       # a partial last workgroup
+    (7, 1024, 3328, 4, torch.bfloat16),     # 26 groups: short chunks
+    (1, 64, 128, 3, torch.float32),         # one group: 7 of 8 K-split waves idle
+    (16, 512, 13824, 7, torch.bfloat16),    # 108 groups: several chunks per wave
+    (48, 256, 384, 5, torch.float32),       # M > 16: its own launch
+]
+
+
+def _run_group(api, cases, seed):
+    items, refs = [], []
+    for i, (m, n, k, bits, dt) in enumerate(cases):
+        c = synth.random_case(seed * 97 + i, m, n, k)
+        qw = api.quantize_pack(dev_bf16(c["w"]), bits)
+        items.append((dev_bf16(c["x"]), qw, torch.empty((m, n), dtype=dt, device="cuda")))
+        refs.append((O.gemm_ref(c["x"], _oracle_w16(c["w"], bits)), dt))
+    outs = api.dequant_gemm_grouped(items)
+    for (m, n, k, bits, dt), y, (ref, _) in zip(cases, outs, refs):
+        check_product(host(y), ref, dt == torch.bfloat16, f"grouped m={m} n={n} k={k} bits={bits}")
+
+
+def test_gemm_grouped_mixed(gpu_lib):
+    _case("dequant_gemm_grouped mixed widths and shapes")
+    _run_group(gpu_lib, _GROUP_CASES, 1)
+
+
+def test_gemm_grouped_more_than_one_launch(gpu_lib):
+    _case("dequant_gemm_grouped 19 small products (two launches)")
+    cases = [(1 + (i % 16), 64 * (1 + i % 5), 128 * (1 + i % 7), 3 + i % 5,
+              torch.float32 if i % 2 else torch.bfloat16) for i in range(19)]
+    _run_group(gpu_lib, cases, 2)
+
+
+def test_gemm_grouped_matches_single_calls(gpu_lib):
+    _case("dequant_gemm_grouped against separate dequant_gemm calls")
+    c = synth.random_case(5, 16, 1024, 1280)
+    outs_single, items = [], []
+    for bits in (4, 5, 6):
+        qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+        x = dev_bf16(c["x"])
+        outs_single.append(host(gpu_lib.dequant_gemm(x, qw, torch.float32)))
+        items.append((x, qw))
+    outs = gpu_lib.dequant_gemm_grouped(items, out_dtype=torch.float32)
+    for a, b in zip(outs, outs_single):
+        check_product(host(a), b.astype(np.float64), False, "grouped vs single")
+
+
 def test_gemm_empty_batch_leaves_output(gpu_lib):
     _case("dequant_gemm m=0")
     c = synth.random_case(1, 4, 32, 128)
