@@ -57,10 +57,11 @@ def parse():
                                                       "dequant_gemm_attnproj3072_traffic.md"),
                     help="profile summary holding the measured HBM bytes per launch of the "
                          "dominant kernel (used only while the kernel sources are unchanged)")
-    ap.add_argument("--suite", choices=["block16"], default=None,
+    ap.add_argument("--suite", choices=["block16", "alloc"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
-                         "one by one and grouped, one JSON line each")
+                         "one by one and grouped, one JSON line each; alloc: error tables of a "
+                         "synthetic 4-block model on the GPU and the PD-guided bit allocation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -177,6 +178,106 @@ def block16_suite(steps, warmup):
     line("q,k,v (5,6,4 bits) grouped", qkv, timed(grouped(qkv)))
 
 
+def _greedy_allocation(mse, nparams, target, candidates):
+    """Reference only: marginal-gain greedy over convex error curves (start
+    at the lowest width, add one width at a time where it buys the largest
+    error drop per weight-bit) until the budget is spent."""
+    import heapq
+
+    import numpy as np
+    nc = len(candidates)
+    idx = np.zeros(len(nparams), dtype=np.int64)
+    budget = (target - candidates[0]) * float(np.sum(nparams))
+    heap = [(-(mse[i, 0] - mse[i, 1]) / (candidates[1] - candidates[0]), i) for i in range(len(nparams))]
+    heapq.heapify(heap)
+    spent = 0.0
+    while heap:
+        _, i = heapq.heappop(heap)
+        cost = float(nparams[i]) * (candidates[idx[i] + 1] - candidates[idx[i]])
+        if spent + cost > budget + 1e-6:
+            continue
+        spent += cost
+        idx[i] += 1
+        if idx[i] + 1 < nc:
+            heapq.heappush(heap, (-(mse[i, idx[i]] - mse[i, idx[i] + 1])
+                                  / (candidates[idx[i] + 1] - candidates[idx[i]]), i))
+    return np.asarray(candidates)[idx]
+
+
+def alloc_suite(args):
+    """Error tables of a synthetic 4-block DiT (40 tensors, Wan-14B block
+    shapes) on the GPU, then the PD-guided allocation at 5.0 bits/weight."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from dit_dequant_gemm_amd import api
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    shapes = ([(5120, 5120)] * 8 + [(13824, 5120), (5120, 13824)]) * 4
+    rng = np.random.default_rng(5)
+    sigma = np.exp(rng.uniform(np.log(0.01), np.log(0.04), size=len(shapes)))
+    spread = rng.uniform(0.0, 1.5, size=len(shapes))
+    outl = rng.uniform(0.0, 2e-3, size=len(shapes))
+    ws = []
+    for i, (n, k) in enumerate(shapes):
+        w = torch.randn((n, k), generator=gen, device=dev) * float(sigma[i])
+        w *= torch.exp(float(spread[i]) * 0.5 * torch.randn((n, 1), generator=gen, device=dev))
+        mask = torch.rand((n, k), generator=gen, device=dev) < float(outl[i])
+        w = torch.where(mask, w * 10.0, w).to(torch.bfloat16)
+        ws.append(w)
+    nweights = sum(w.numel() for w in ws)
+    api.mse_table(ws[:2])                                  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mse, nparams = api.mse_table(ws)
+    torch.cuda.synchronize()
+    t_tables = time.perf_counter() - t0
+    # the dominant kernel alone: events around one tensor's table on the stream
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        api.quant_sse(ws[0])
+    e1.record(stream)
+    e1.synchronize()
+    t_one = e0.elapsed_time(e1) / 5 * 1e-3
+    target = 5.0
+    t_init = 0.5 * np.random.default_rng(6).standard_normal((15, len(ws)))
+    t0 = time.perf_counter()
+    bits, info = api.pd_allocate(mse, nparams, target, t_init, iters=500)
+    t_search = time.perf_counter() - t0
+    # the oracle: its search on the same tables, its tables on one tensor (bounded sample)
+    t0 = time.perf_counter()
+    ro = O.pd_search(mse, nparams, target, t_init, iters=500)
+    t_search_cpu = time.perf_counter() - t0
+    w_cpu = ws[0][:1024].float().cpu().numpy()
+    t0 = time.perf_counter()
+    O.mse_table([w_cpu])
+    t_table_cpu = time.perf_counter() - t0
+    uniform = O.pd_objective(mse, nparams, [5] * len(ws))[0]
+    greedy = _greedy_allocation(mse, nparams, target, list(O.PD_CANDIDATES))
+    e_greedy, p_greedy = O.pd_objective(mse, nparams, greedy)
+    hist = {int(b): int(np.sum(bits == b)) for b in O.PD_CANDIDATES}
+    print(json.dumps({
+        "suite": "pd-bit-allocation", "tensors": len(ws), "weights": nweights,
+        "target_bpw": target,
+        "gpu_error_tables_s": round(t_tables, 4),
+        "gpu_error_table_weight_GBps": round(2 * nweights / t_tables / 1e9, 1),
+        "quant_sse_5120x5120_ms": round(t_one * 1e3, 3),
+        "quant_sse_5120x5120_weight_GBps": round(2 * 5120 * 5120 / t_one / 1e9, 1),
+        "search_s": round(t_search, 4), "oracle_search_s": round(t_search_cpu, 3),
+        "search_matches_oracle": bool(np.array_equal(bits, ro["bits"])),
+        "oracle_table_1024x5120_s": round(t_table_cpu, 3),
+        "allocation": {"mse": info["mse"], "bpw": info["bpw"], "widths": hist,
+                       "vs_uniform5": round(info["mse"] / uniform - 1.0, 4),
+                       "greedy_reference_vs_uniform5": round(e_greedy / uniform - 1.0, 4),
+                       "greedy_bpw": p_greedy},
+    }), flush=True)
+
+
 def system_info(torch):
     """GPU name, clock and ROCm build; host CPU model."""
     info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
@@ -272,6 +373,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.suite == "block16":
         block16_suite(args.steps, args.warmup)
+        return
+    if args.suite == "alloc":
+        alloc_suite(args)
         return
 
     c = synth.config2(m=M_BIG)

@@ -45,6 +45,11 @@ SIGNATURES = {
     "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
     "ddg_dequant_gemm_grouped": (_c_int, [ctypes.POINTER(GemmDesc), _c_int, _vp]),
     "ddg_lowrank_workspace_bytes": (_c_int, [_c_i64, _c_int, ctypes.POINTER(_sz)]),
+    "ddg_quant_sse": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ddg_pd_allocate": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64), _c_int,
+                                 ctypes.POINTER(_c_int), _c_int, ctypes.c_double,
+                                 ctypes.POINTER(ctypes.c_double), _c_int, _c_int,
+                                 ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_double)]),
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
 }
@@ -259,3 +264,64 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream_ptr(x.device)),
         "ddg_lowrank_fused_gemm")
     return y
+
+
+# ------------------------------------------------------------------ bit allocation
+PD_CANDIDATES = (3, 4, 5, 6, 7)
+
+
+def quant_sse(w: torch.Tensor):
+    """(row_sse n x 5 float64, total 5 float64) GPU tensors: sum of
+    (w - w_hat32)^2 per row and over the tensor at widths 3..7."""
+    _require_cuda(w, "w")
+    if w.dim() != 2 or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be a 2-D bf16 or float32 tensor")
+    n, k = w.shape
+    if k % GROUP:
+        w = torch.nn.functional.pad(w, (0, GROUP - k % GROUP)).contiguous()
+        k = w.shape[1]
+    rows = torch.empty((max(n, 1), 5), dtype=torch.float64, device=w.device)
+    total = torch.empty(5, dtype=torch.float64, device=w.device)
+    _check(load_library().ddg_quant_sse(w.data_ptr(), DDG_F32 if w.dtype == torch.float32 else DDG_BF16,
+                                        n, k, rows.data_ptr(), total.data_ptr(),
+                                        _stream_ptr(w.device)), "ddg_quant_sse")
+    return rows[:n], total
+
+
+def mse_table(weights):
+    """(mse N x 5, nparams N) numpy arrays: per-weight quantization error of
+    every tensor at widths 3..7 (the tables the allocation searches over).
+    Weights padded along the input dimension count their real elements."""
+    import numpy as np
+    mse = np.empty((len(weights), 5), dtype=np.float64)
+    nparams = np.empty(len(weights), dtype=np.int64)
+    totals = []
+    for w in weights:
+        totals.append(quant_sse(w)[1])
+    for i, (w, t) in enumerate(zip(weights, totals)):
+        nparams[i] = w.numel()
+        mse[i] = t.cpu().numpy() / nparams[i]
+    return mse, nparams
+
+
+def pd_allocate(mse, nparams, target_bpw: float, t_init, iters: int = 500,
+                candidates=PD_CANDIDATES):
+    """PD-guided widths for every tensor (host-side search in the library).
+    t_init: restarts x N starting parameters.  Returns (bits, info dict)."""
+    import numpy as np
+    mse = np.ascontiguousarray(mse, dtype=np.float64)
+    nparams = np.ascontiguousarray(nparams, dtype=np.int64)
+    t_init = np.ascontiguousarray(t_init, dtype=np.float64)
+    cand = np.ascontiguousarray(candidates, dtype=np.int32)
+    n = nparams.shape[0]
+    if mse.shape != (n, cand.shape[0]) or t_init.ndim != 2 or t_init.shape[1] != n:
+        raise ValueError("mse must be N x len(candidates) and t_init restarts x N")
+    bits = np.empty(n, dtype=np.int32)
+    info = np.empty(3, dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(load_library().ddg_pd_allocate(
+        mse.ctypes.data_as(dp), nparams.ctypes.data_as(ctypes.POINTER(_c_i64)), n,
+        cand.ctypes.data_as(ctypes.POINTER(_c_int)), cand.shape[0], float(target_bpw),
+        t_init.ctypes.data_as(dp), t_init.shape[0], iters, bits.ctypes.data_as(ctypes.POINTER(_c_int)),
+        info.ctypes.data_as(dp)), "ddg_pd_allocate")
+    return bits.astype(np.int64), {"mse": float(info[0]), "bpw": float(info[1]), "restart": int(info[2])}

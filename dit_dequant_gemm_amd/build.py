@@ -42,6 +42,7 @@ def _units():
     units = [(os.path.join(CSRC, "inst_bits.hip"), f"inst_b{b}", [f"-DDDG_BITS={b}"]) for b in BITS]
     units.append((os.path.join(CSRC, "lowrank.hip"), "lowrank", []))
     units.append((os.path.join(CSRC, "grouped.hip"), "grouped", []))
+    units.append((os.path.join(CSRC, "pd.hip"), "pd", []))
     units.append((os.path.join(CSRC, "api.hip"), "api", []))
     return units
 

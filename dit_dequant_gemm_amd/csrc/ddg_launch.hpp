@@ -30,6 +30,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t st
 // prefix sum of ceil(n / (16 kGroupedNcb)) over the products)
 hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream);
 
+// per-row and total quantization error at widths 3..7 (row_sse: n x 5)
+hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, double* row_sse,
+                            double* total, hipStream_t stream);
+
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
 

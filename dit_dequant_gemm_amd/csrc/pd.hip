@@ -1,0 +1,274 @@
+// Quantization-error tables and the PD-guided bit allocation ([WDQ] §3.2):
+//   quant_sse_kernel   per-row sum of (w - w_hat32)^2 at every width 3..7 in
+//                      one pass over W (the §3.1 quantizer, the same float32
+//                      arithmetic as quantize_pack_kernel), float64 sums
+//   sse_total_kernel   the rows' sums in a fixed order (deterministic)
+//   ddg_pd_allocate    the host-side primal-dual search over those tables
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "ddg.h"
+#include "ddg_launch.hpp"
+
+namespace ddg {
+
+constexpr int kSseWidths = 5;            // widths 3..7
+
+// One workgroup (256 lanes) per row; lane i takes chunks i, i+256, ... (32
+// weights each, the 4 chunks of a group in one quad).
+template <bool F32_IN>
+__global__ __launch_bounds__(256) void quant_sse_kernel(const void* __restrict__ w, int64_t k,
+                                                       double* __restrict__ row_sse) {
+  __shared__ double red[4][kSseWidths];
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int chunks = (int)(k / 32);
+  double acc[kSseWidths] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  // whole quads per pass, so that the butterfly never mixes groups
+  for (int c0 = 0; c0 < chunks; c0 += 256) {
+    const int c = c0 + lane;
+    const bool valid = c < chunks;
+    float v[32];
+    if (valid) {
+      if constexpr (F32_IN) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(w) + row * k + (int64_t)c * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 t = src[i];
+          v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+        }
+      } else {
+        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + row * k + (int64_t)c * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 t = src[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[8 * i + 2 * j] = bf16_bits_to_f32(t[j] & 0xFFFFu);
+            v[8 * i + 2 * j + 1] = bf16_bits_to_f32(t[j] >> 16);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 1));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 2));
+    const float a1 = a * 1.01f;
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      ([&] {
+        constexpr int B = J + 3;
+        constexpr float nh = (float)Bits<B>::n_half;
+        const float step = (2.0f * a1) / (float)((1 << B) - 1);
+        const bool zero_group = !(step != 0.0f);
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          float q = __builtin_rintf(v[i] / step);
+          q = __builtin_fminf(__builtin_fmaxf(q, -nh), nh);
+          const float wh = zero_group ? 0.0f : q * step;
+          const double d = (double)v[i] - (double)wh;
+          s = __builtin_fma(d, d, s);
+        }
+        acc[J] += s;
+      }(), ...);
+    }(std::make_integer_sequence<int, kSseWidths>{});
+  }
+  // workgroup sum: waves in order, lanes in a fixed butterfly
+#pragma unroll
+  for (int j = 0; j < kSseWidths; ++j) {
+    double x = acc[j];
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((lane & 63) == 0) red[lane >> 6][j] = x;
+  }
+  __syncthreads();
+  if (lane < kSseWidths)
+    row_sse[row * kSseWidths + lane] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+// totals[j] = sum over rows of row_sse[row][j], rows in order per lane
+// stride, then a fixed butterfly.
+__global__ __launch_bounds__(256) void sse_total_kernel(const double* __restrict__ row_sse, int64_t n,
+                                                        double* __restrict__ total) {
+  __shared__ double red[4][kSseWidths];
+  const int lane = threadIdx.x;
+  double acc[kSseWidths] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int64_t r = lane; r < n; r += 256)
+#pragma unroll
+    for (int j = 0; j < kSseWidths; ++j) acc[j] += row_sse[r * kSseWidths + j];
+#pragma unroll
+  for (int j = 0; j < kSseWidths; ++j) {
+    double x = acc[j];
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((lane & 63) == 0) red[lane >> 6][j] = x;
+  }
+  __syncthreads();
+  if (lane < kSseWidths) total[lane] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, double* row_sse,
+                            double* total, hipStream_t stream) {
+  if (n > 0) {
+    if (f32_in)
+      quant_sse_kernel<true><<<dim3((unsigned)n), dim3(256), 0, stream>>>(w, k, row_sse);
+    else
+      quant_sse_kernel<false><<<dim3((unsigned)n), dim3(256), 0, stream>>>(w, k, row_sse);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  sse_total_kernel<<<dim3(1), dim3(256), 0, stream>>>(row_sse, n, total);
+  return hipGetLastError();
+}
+
+}  // namespace ddg
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr double kPenalty = 1.0e4;       // the section's quadratic budget penalty
+constexpr double kLr = 0.05;             // Adam step on the tensor parameters
+constexpr double kLrDual = 0.05;         // ascent step on the multiplier
+constexpr double kBeta1 = 0.9, kBeta2 = 0.999, kEps = 1e-8;
+
+// index of the candidate nearest x (the lower one on ties)
+int nearest(const int* cand, int nc, double x) {
+  int best = 0;
+  double bd = std::fabs(x - cand[0]);
+  for (int c = 1; c < nc; ++c) {
+    const double d = std::fabs(x - cand[c]);
+    if (d < bd) { bd = d; best = c; }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_sse,
+                             double* total_sse, hipStream_t stream) {
+  if (w_dtype != DDG_BF16 && w_dtype != DDG_F32) return DDG_ERR_ARG;
+  if (n < 0 || n > 2147483647 || k <= 0 || k % DDG_GROUP || k > (INT64_C(1) << 31))
+    return DDG_ERR_SHAPE;
+  if (!total_sse) return DDG_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(total_sse) & 7) return DDG_ERR_ALIGN;
+  if (n > 0) {
+    if (!w || !row_sse) return DDG_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(row_sse) & 7))
+      return DDG_ERR_ALIGN;
+  }
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return DDG_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return DDG_ERR_UNSUPPORTED;
+  return ddg::launch_quant_sse(w, w_dtype == DDG_F32, n, k, row_sse, total_sse, stream) == hipSuccess
+             ? DDG_OK
+             : DDG_ERR_HIP;
+}
+
+extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int* candidates,
+                               int ncand, double target_bpw, const double* t_init, int restarts,
+                               int iters, int* bits_out, double* info) {
+  if (!mse || !nparams || !candidates || !t_init || !bits_out) return DDG_ERR_ARG;
+  if (n < 1 || ncand < 2 || ncand > 8 || restarts < 1 || iters < 1) return DDG_ERR_SHAPE;
+  for (int c = 1; c < ncand; ++c)
+    if (candidates[c] <= candidates[c - 1]) return DDG_ERR_ARG;
+  const double bmin = candidates[0], bmax = candidates[ncand - 1];
+  if (!(target_bpw >= bmin && target_bpw <= bmax)) return DDG_ERR_ARG;
+  for (int i = 0; i < n; ++i) {
+    if (nparams[i] <= 0) return DDG_ERR_ARG;
+    for (int c = 0; c < ncand; ++c)
+      if (!(mse[(int64_t)i * ncand + c] >= 0.0) || !std::isfinite(mse[(int64_t)i * ncand + c]))
+        return DDG_ERR_ARG;
+  }
+  // weights of the tensors, and the error table normalised by the uniform
+  // allocation at the candidate nearest the target
+  double tot = 0.0;
+  for (int i = 0; i < n; ++i) tot += (double)nparams[i];
+  std::vector<double> wgt(n), m((size_t)n * ncand);
+  for (int i = 0; i < n; ++i) wgt[i] = (double)nparams[i] / tot;
+  const int j0 = nearest(candidates, ncand, target_bpw);
+  double ref = 0.0;
+  for (int i = 0; i < n; ++i) ref += wgt[i] * mse[(int64_t)i * ncand + j0];
+  for (size_t x = 0; x < m.size(); ++x) m[x] = ref > 0.0 ? mse[x] / ref : mse[x];
+
+  std::vector<double> t(n), m1(n), m2(n), u(n), b(n), g(n), sw(ncand);
+  std::vector<int> bits(n), best_bits(n);
+  bool have = false;
+  int best_feasible = 0, best_restart = 0;
+  double best_e = 0.0, best_p = 0.0;
+  for (int r = 0; r < restarts; ++r) {
+    for (int i = 0; i < n; ++i) { t[i] = t_init[(int64_t)r * n + i]; m1[i] = 0.0; m2[i] = 0.0; }
+    double lam = 0.5;
+    for (int it = 0; it < iters; ++it) {
+      for (int i = 0; i < n; ++i) {
+        u[i] = 1.0 / (1.0 + std::exp(-t[i]));
+        b[i] = bmin + u[i] * (bmax - bmin);
+      }
+      const double temp = std::max(2.0 * (1.0 - (double)it / iters), 0.05);
+      double bpw = 0.0;
+      for (int i = 0; i < n; ++i) bpw += wgt[i] * b[i];
+      const double gap = bpw - target_bpw;
+      for (int i = 0; i < n; ++i) {
+        // soft assignment of b[i] to the candidates, and the blended error
+        double amax = -INFINITY;
+        for (int c = 0; c < ncand; ++c) amax = std::max(amax, -std::fabs(b[i] - candidates[c]) / temp);
+        double esum = 0.0;
+        for (int c = 0; c < ncand; ++c) {
+          sw[c] = std::exp(-std::fabs(b[i] - candidates[c]) / temp - amax);
+          esum += sw[c];
+        }
+        double s = 0.0;
+        for (int c = 0; c < ncand; ++c) { sw[c] /= esum; s += sw[c] * m[(size_t)i * ncand + c]; }
+        double ds_db = 0.0;
+        for (int c = 0; c < ncand; ++c) {
+          const double dd = b[i] - candidates[c];
+          const double sgn = dd > 0.0 ? 1.0 : (dd < 0.0 ? -1.0 : 0.0);
+          ds_db += sw[c] * (m[(size_t)i * ncand + c] - s) * (-sgn / temp);
+        }
+        const double dl_db = wgt[i] * (ds_db + lam + 2.0 * kPenalty * gap);
+        g[i] = dl_db * (bmax - bmin) * u[i] * (1.0 - u[i]);
+      }
+      const double c1 = 1.0 - std::pow(kBeta1, it + 1), c2 = 1.0 - std::pow(kBeta2, it + 1);
+      for (int i = 0; i < n; ++i) {
+        m1[i] = kBeta1 * m1[i] + (1.0 - kBeta1) * g[i];
+        m2[i] = kBeta2 * m2[i] + (1.0 - kBeta2) * g[i] * g[i];
+        t[i] = t[i] - kLr * (m1[i] / c1) / (std::sqrt(m2[i] / c2) + kEps);
+      }
+      lam = lam + kLrDual * gap;
+    }
+    // round to the nearest candidate and score the allocation exactly
+    double e = 0.0, p = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const double bc = bmin + (1.0 / (1.0 + std::exp(-t[i]))) * (bmax - bmin);
+      const int j = nearest(candidates, ncand, bc);
+      bits[i] = candidates[j];
+      e += (double)nparams[i] * mse[(int64_t)i * ncand + j];
+      p += (double)nparams[i] * (double)candidates[j];
+    }
+    e /= tot;
+    p /= tot;
+    const int feasible = p <= target_bpw + 1e-9 ? 1 : 0;
+    bool better;
+    if (!have) better = true;
+    else if (feasible != best_feasible) better = feasible > best_feasible;
+    else if (feasible) better = e < best_e || (e == best_e && p < best_p);
+    else better = p < best_p || (p == best_p && e < best_e);
+    if (better) {
+      have = true;
+      best_feasible = feasible;
+      best_e = e;
+      best_p = p;
+      best_restart = r;
+      best_bits = bits;
+    }
+  }
+  for (int i = 0; i < n; ++i) bits_out[i] = best_bits[i];
+  if (info) { info[0] = best_e; info[1] = best_p; info[2] = best_restart; }
+  return DDG_OK;
+}

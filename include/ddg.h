@@ -189,6 +189,51 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
                            void* y, int y_dtype, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Quantization error of an N x K weight at every width 3..7 ([WDQ] §3.2:
+ * the per-tensor error tables the bit allocation searches over; §3.1: the
+ * quantizer of ddg_quantize_pack, float32 arithmetic bit for bit):
+ *   row_sse[5 i + (b - 3)] = sum over row i of (w - w_hat32)^2,
+ *   w_hat32 = fl32((q_u - n_half) * scale), summed in float64;
+ *   total_sse[b - 3] = the rows' sum in a fixed order (deterministic).
+ *   w          N x K bf16 or float32 (w_dtype), finite.
+ *   row_sse    device, N x 5 doubles (also the scratch of the total).
+ *   total_sse  device, 5 doubles.
+ * n == 0 writes zero totals.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (n < 0, k
+ * not a positive multiple of 128 or above 2^31), DDG_ERR_ALIGN (w 16-byte,
+ * the outputs 8-byte), DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_sse,
+                  double* total_sse, hipStream_t stream);
+
+/*
+ * PD-guided mixed-precision bit allocation ([WDQ] §3.2).  Host only: every
+ * pointer is a host pointer and nothing runs on the GPU.  Minimises the
+ * parameter-weighted error sum_i n_i mse_i(b_i) / sum_i n_i subject to
+ * sum_i n_i b_i / sum_i n_i <= target_bpw by the section's relaxation: one
+ * parameter per tensor, b = bmin + sigmoid(t) (bmax - bmin); a softmax over
+ * the candidates of -|b - c| / temp, temp = max(2 (1 - it/iters), 0.05),
+ * blends the tensor's error row (normalised by the uniform allocation at the
+ * candidate nearest the target); loss = error + lambda (bpw - target)
+ * + 1e4 (bpw - target)^2; Adam steps (lr 0.05) on the parameters and ascent
+ * steps (0.05) on lambda, from lambda = 0.5.  Each restart's widths are the
+ * nearest candidates (the lower on ties); the kept restart has the lowest
+ * exact error within the budget, else the lowest bpw.
+ *   mse        n x ncand per-weight errors (row i: tensor i, column c: width
+ *              candidates[c]); finite, >= 0.
+ *   nparams    n weight counts, > 0.
+ *   candidates ncand (2..8) increasing widths; target_bpw within their range.
+ *   t_init     restarts x n starting parameters (the random draws).
+ *   bits_out   n chosen widths.
+ *   info       NULL or 3 doubles: error, bpw, kept restart.
+ * Errors: DDG_ERR_ARG (null pointer, bad table entry, candidates not
+ * increasing, target out of range), DDG_ERR_SHAPE (n < 1, ncand outside
+ * 2..8, restarts or iters < 1).
+ */
+int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int* candidates,
+                    int ncand, double target_bpw, const double* t_init, int restarts,
+                    int iters, int* bits_out, double* info);
+
 #ifdef __cplusplus
 }
 #endif

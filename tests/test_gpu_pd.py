@@ -1,0 +1,77 @@
+"""GPU parity of the quantization-error tables ([WDQ] §3.2 inputs): the
+library's per-row and total sums of (w - w_hat32)^2 at widths 3..7 against
+the oracle (float64 sums in another order: relative 1e-12), and the whole
+allocation (GPU tables + library search) against the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dit_dequant_gemm_amd import synth
+from parity_util import dev_bf16, dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _check_sse(api, w, f32):
+    rows, total = api.quant_sse(dev_f32(w) if f32 else dev_bf16(w))
+    torch.cuda.synchronize()
+    rows = rows.cpu().numpy()
+    total = total.cpu().numpy()
+    for j, b in enumerate(O.PD_CANDIDATES):
+        ref = O.quant_sse_rows(w, b)
+        assert np.allclose(rows[:, j], ref, rtol=1e-12, atol=0.0), (b, np.max(np.abs(rows[:, j] - ref)))
+        assert total[j] == pytest.approx(ref.sum(), rel=1e-12, abs=0.0)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 384), (64, 5120), (5, 13824), (3, 40960)])
+def test_quant_sse_random(gpu_lib, n, k):
+    _case(f"quant_sse n={n} k={k}")
+    w = synth.random_case(n * 7 + k, 1, n, k, wstd=0.03)["w"]
+    _check_sse(gpu_lib, w, False)
+
+
+def test_quant_sse_edge_groups(gpu_lib):
+    _case("quant_sse zero, constant, tiny and f32 groups")
+    rng = np.random.default_rng(3)
+    w = rng.standard_t(3, size=(8, 640)).astype(np.float32) * 0.02
+    w[0] = 0.0                                  # all-zero row
+    w[1, :128] = 0.0                            # one zero group
+    w[2, 128:256] = np.float32(0.25)            # constant group
+    w[3, 256:384] = -np.float32(0.25)
+    w[4] *= np.float32(1e-30)                   # tiny (subnormal steps at 7 bits)
+    _check_sse(gpu_lib, w, True)
+    _check_sse(gpu_lib, synth.to_bf16(w), False)
+
+
+def test_quant_sse_empty(gpu_lib):
+    _case("quant_sse n=0")
+    rows, total = gpu_lib.quant_sse(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert rows.shape == (0, 5) and np.all(total.cpu().numpy() == 0.0)
+
+
+def test_allocation_end_to_end(gpu_lib):
+    _case("mse_table on the GPU + library search against the oracle")
+    rng = np.random.default_rng(11)
+    ws = []
+    for i in range(10):
+        if i % 2:
+            w = rng.standard_t(3 + i, size=(64, 1024)) * 0.02
+        else:
+            w = rng.normal(0, 0.02 * (1 + i / 5), size=(64, 1024))
+        ws.append(synth.to_bf16(w))
+    mse_gpu, n_gpu = gpu_lib.mse_table([dev_bf16(w) for w in ws])
+    mse_ref, n_ref = O.mse_table(ws)
+    assert np.array_equal(n_gpu, n_ref)
+    assert np.allclose(mse_gpu, mse_ref, rtol=1e-12, atol=0.0)
+    t_init = 0.5 * np.random.default_rng(12).standard_normal((8, len(ws)))
+    for target in (4.0, 4.7, 5.0):
+        bits, info = gpu_lib.pd_allocate(mse_gpu, n_gpu, target, t_init, iters=300)
+        ro = O.pd_search(mse_ref, n_ref, target, t_init, iters=300)
+        assert np.array_equal(bits, ro["bits"]), (target, bits, ro["bits"])
+        assert info["bpw"] <= target + 1e-9

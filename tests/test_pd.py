@@ -1,0 +1,178 @@
+"""Bit allocation ([WDQ] §3.2): the oracle's error tables and search against
+what the mathematics fixes, the library's host-side search against the
+oracle, and the C-ABI argument checks.  All on the CPU."""
+import numpy as np
+import pytest
+
+import oracle as O
+from dit_dequant_gemm_amd import api
+
+CAND = np.array(O.PD_CANDIDATES, dtype=np.float64)
+
+
+def _tensors(seed, count=12, rows=16, cols=256):
+    """Weights of different shapes of distribution (the allocation has
+    something to choose between)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        kind = i % 3
+        if kind == 0:
+            w = rng.normal(0.0, 0.02 * rng.uniform(0.5, 2.0), size=(rows, cols))
+        elif kind == 1:
+            w = rng.standard_t(3, size=(rows, cols)) * 0.02
+        else:
+            w = rng.uniform(-0.03, 0.03, size=(rows, cols))
+        out.append(w.astype(np.float32))
+    return out
+
+
+# ------------------------------------------------------------------ error tables
+@pytest.mark.parametrize("bits", O.PD_CANDIDATES)
+def test_sse_of_constant_magnitude_group_is_closed_form(bits):
+    # every |w| = a: a/step = (2^b - 1)/2.02 rounds to n_half, so each weight
+    # is off by a - n_half * step exactly (up to float32 rounding of step)
+    a = np.float32(0.0371)
+    w = np.full((2, 256), a, dtype=np.float32)
+    w[1, ::2] = -a
+    step = np.float32(np.float32(2.0) * np.float32(a * np.float32(1.01))) / np.float32(2 ** bits - 1)
+    err = float(a) - float(np.float32(np.float32(O.n_half(bits)) * step))
+    got = O.quant_sse_rows(w, bits)
+    assert np.allclose(got, 256 * err * err, rtol=1e-6)
+
+
+@pytest.mark.parametrize("bits", O.PD_CANDIDATES)
+def test_sse_bounded_by_half_step(bits):
+    w = _tensors(1, count=1)[0]
+    q_u, s = O.quantize_groups(w, bits)
+    bound = np.sum((np.repeat(s, 128, axis=1).astype(np.float64) / 2) ** 2, axis=1)
+    assert np.all(O.quant_sse_rows(w, bits) <= bound * (1 + 1e-6))
+
+
+def test_sse_zero_and_monotone_in_width():
+    assert np.all(O.quant_sse_rows(np.zeros((3, 128), np.float32), 4) == 0.0)
+    w = np.random.default_rng(2).normal(0, 0.02, size=(32, 512)).astype(np.float32)
+    sse = [O.quant_sse_rows(w, b).sum() for b in O.PD_CANDIDATES]
+    ratios = np.array(sse[:-1]) / np.array(sse[1:])
+    assert np.all(ratios > 3.0) and np.all(ratios < 5.5)     # ~6 dB per bit
+
+
+def test_sse_matches_snr():
+    w = _tensors(3, count=1)[0]
+    for b in (3, 5, 7):
+        q_u, s = O.quantize_groups(w, b)
+        snr = O.snr_db(w, O.dequant_f32(q_u, s, b))
+        sse = O.quant_sse_rows(w, b).sum()
+        assert abs(10 * np.log10(np.sum(w.astype(np.float64) ** 2) / sse) - snr) < 1e-9
+
+
+# ------------------------------------------------------------------ the search
+def test_loss_gradient_matches_finite_differences():
+    mse, n = O.mse_table(_tensors(4, count=6))
+    wgt = n / n.sum()
+    m = mse / np.sum(wgt * mse[:, 1])
+    rng = np.random.default_rng(5)
+    for temp in (2.0, 0.7, 0.05):
+        t = rng.normal(0, 1.0, size=6)
+        loss, g, _ = O.pd_loss_grad(t, 0.3, m, wgt, CAND, 4.6, temp)
+        for i in range(6):
+            h = 1e-6
+            tp, tm = t.copy(), t.copy()
+            tp[i] += h
+            tm[i] -= h
+            fd = (O.pd_loss_grad(tp, 0.3, m, wgt, CAND, 4.6, temp)[0]
+                  - O.pd_loss_grad(tm, 0.3, m, wgt, CAND, 4.6, temp)[0]) / (2 * h)
+            assert abs(fd - g[i]) <= 1e-5 * max(1.0, abs(fd)), (temp, i, fd, g[i])
+
+
+def _search(mse, n, target, seed=0, restarts=6, iters=300):
+    t_init = 0.5 * np.random.default_rng(seed).standard_normal((restarts, len(n)))
+    return O.pd_search(mse, n, target, t_init, iters=iters), t_init
+
+
+def test_search_is_invariant_to_order_scale_and_counts():
+    mse, n = O.mse_table(_tensors(6))
+    r, t_init = _search(mse, n, 4.5)
+    perm = np.random.default_rng(1).permutation(len(n))
+    rp = O.pd_search(mse[perm], n[perm], 4.5, t_init[:, perm], iters=300)
+    assert np.array_equal(rp["bits"], r["bits"][perm])
+    rs = O.pd_search(mse * 1000.0, n, 4.5, t_init, iters=300)       # normalised table (R9)
+    assert np.array_equal(rs["bits"], r["bits"])
+    rn = O.pd_search(mse, n * 7, 4.5, t_init, iters=300)            # only shares of weights count
+    assert np.array_equal(rn["bits"], r["bits"])
+
+
+@pytest.mark.parametrize("target", [3.5, 4.0, 5.0, 5.5, 6.5])
+def test_search_result_is_a_valid_allocation(target):
+    mse, n = O.mse_table(_tensors(7))
+    r, _ = _search(mse, n, target)
+    assert set(np.unique(r["bits"])) <= set(O.PD_CANDIDATES)
+    e, p = O.pd_objective(mse, n, r["bits"])
+    assert e == r["mse"] and p == r["bpw"] and p <= target + 1e-9
+
+
+def test_search_bounded_by_exhaustive_optimum():
+    """The exact optimum (brute force over 5^6 allocations) bounds any
+    allocation within the budget from below, the search's included.  (How
+    close the search gets is a property of the heuristic, measured by the
+    bench's allocation suite, not a correctness condition.)"""
+    mse, n = O.mse_table(_tensors(8, count=6))
+    for target in (4.0, 5.0, 5.5):
+        r, _ = _search(mse, n, target, restarts=15, iters=500)
+        best_bits, best_e, best_p = O.pd_exhaustive(mse, n, target)
+        assert best_p <= target + 1e-9
+        assert best_e <= r["mse"] + 1e-18
+        assert O.pd_objective(mse, n, best_bits) == (best_e, best_p)
+
+
+# ------------------------------------------------------------------ library vs oracle
+@pytest.mark.parametrize("seed,target", [(10, 3.6), (11, 4.0), (12, 5.0), (13, 5.4), (14, 6.8)])
+def test_library_search_matches_oracle(seed, target):
+    mse, n = O.mse_table(_tensors(seed, count=30))
+    n = n * np.random.default_rng(seed).integers(1, 9, size=len(n))
+    t_init = 0.5 * np.random.default_rng(seed + 100).standard_normal((5, len(n)))
+    ro = O.pd_search(mse, n, target, t_init, iters=250)
+    bits, info = api.pd_allocate(mse, n, target, t_init, iters=250)
+    assert np.array_equal(bits, ro["bits"])
+    assert info["restart"] == ro["restart"]
+    assert abs(info["mse"] - ro["mse"]) <= 1e-12 * ro["mse"] and info["bpw"] == pytest.approx(ro["bpw"], abs=1e-12)
+
+
+def test_library_search_rejects_bad_arguments():
+    lib = api.load_library()
+    import ctypes
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int)
+    mse = np.ones((2, 5))
+    n = np.array([10, 20], dtype=np.int64)
+    cand = np.array([3, 4, 5, 6, 7], dtype=np.int32)
+    t0 = np.zeros((1, 2))
+    bits = np.zeros(2, dtype=np.int32)
+
+    def call(mse=mse, n=n, nt=2, cand=cand, nc=5, target=4.0, t0=t0, rs=1, it=5):
+        return lib.ddg_pd_allocate(mse.ctypes.data_as(dp), n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   nt, cand.ctypes.data_as(ip), nc, target, t0.ctypes.data_as(dp), rs, it,
+                                   bits.ctypes.data_as(ip), None)
+
+    assert call() == 0
+    assert call(target=2.5) == -1 and call(target=7.5) == -1
+    assert call(cand=np.array([3, 5, 4, 6, 7], dtype=np.int32)) == -1
+    assert call(mse=np.array([[1, 1, -1, 1, 1], [1, 1, 1, 1, 1]], dtype=np.float64)) == -1
+    assert call(mse=np.array([[1, 1, np.nan, 1, 1], [1, 1, 1, 1, 1]], dtype=np.float64)) == -1
+    assert call(n=np.array([10, 0], dtype=np.int64)) == -1
+    assert call(nt=0) == -2 and call(nc=1) == -2 and call(rs=0) == -2 and call(it=0) == -2
+    assert lib.ddg_pd_allocate(None, n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 2,
+                               cand.ctypes.data_as(ip), 5, 4.0, t0.ctypes.data_as(dp), 1, 5,
+                               bits.ctypes.data_as(ip), None) == -1
+
+
+def test_quant_sse_rejects_bad_arguments():
+    lib = api.load_library()
+    FAKE = 1 << 20
+    assert lib.ddg_quant_sse(FAKE, 5, 4, 128, FAKE, FAKE, None) == -1          # dtype
+    assert lib.ddg_quant_sse(FAKE, 0, 4, 100, FAKE, FAKE, None) == -2          # k % 128
+    assert lib.ddg_quant_sse(FAKE, 0, -1, 128, FAKE, FAKE, None) == -2
+    assert lib.ddg_quant_sse(FAKE, 0, 4, 128, FAKE, None, None) == -1          # total
+    assert lib.ddg_quant_sse(None, 0, 4, 128, FAKE, FAKE, None) == -1
+    assert lib.ddg_quant_sse(FAKE + 4, 0, 4, 128, FAKE, FAKE, None) == -3      # w alignment
+    assert lib.ddg_quant_sse(FAKE, 0, 4, 128, FAKE + 4, FAKE, None) == -3
