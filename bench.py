@@ -68,13 +68,16 @@ def parse():
     return ap.parse_args()
 
 
+PRODUCT_KERNEL_SOURCES = ("api.hip", "ddg_device.hpp", "ddg_kernels.hpp", "inst_bits.hip")
+
+
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) over the HIP sources, in name order."""
-    import glob
+    """sha256 (first 16 hex digits) over the sources that define and dispatch
+    the dequant-GEMM kernels, in this order."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "dit_dequant_gemm_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
+    for f in PRODUCT_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dit_dequant_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -244,38 +247,41 @@ def alloc_suite(args):
     e1.record(stream)
     e1.synchronize()
     t_one = e0.elapsed_time(e1) / 5 * 1e-3
-    target = 5.0
     t_init = 0.5 * np.random.default_rng(6).standard_normal((15, len(ws)))
-    t0 = time.perf_counter()
-    bits, info = api.pd_allocate(mse, nparams, target, t_init, iters=500)
-    t_search = time.perf_counter() - t0
-    # the oracle: its search on the same tables, its tables on one tensor (bounded sample)
-    t0 = time.perf_counter()
-    ro = O.pd_search(mse, nparams, target, t_init, iters=500)
-    t_search_cpu = time.perf_counter() - t0
     w_cpu = ws[0][:1024].float().cpu().numpy()
     t0 = time.perf_counter()
     O.mse_table([w_cpu])
     t_table_cpu = time.perf_counter() - t0
-    uniform = O.pd_objective(mse, nparams, [5] * len(ws))[0]
-    greedy = _greedy_allocation(mse, nparams, target, list(O.PD_CANDIDATES))
-    e_greedy, p_greedy = O.pd_objective(mse, nparams, greedy)
-    hist = {int(b): int(np.sum(bits == b)) for b in O.PD_CANDIDATES}
-    print(json.dumps({
+    out = {
         "suite": "pd-bit-allocation", "tensors": len(ws), "weights": nweights,
-        "target_bpw": target,
         "gpu_error_tables_s": round(t_tables, 4),
         "gpu_error_table_weight_GBps": round(2 * nweights / t_tables / 1e9, 1),
         "quant_sse_5120x5120_ms": round(t_one * 1e3, 3),
         "quant_sse_5120x5120_weight_GBps": round(2 * 5120 * 5120 / t_one / 1e9, 1),
-        "search_s": round(t_search, 4), "oracle_search_s": round(t_search_cpu, 3),
-        "search_matches_oracle": bool(np.array_equal(bits, ro["bits"])),
         "oracle_table_1024x5120_s": round(t_table_cpu, 3),
-        "allocation": {"mse": info["mse"], "bpw": info["bpw"], "widths": hist,
-                       "vs_uniform5": round(info["mse"] / uniform - 1.0, 4),
-                       "greedy_reference_vs_uniform5": round(e_greedy / uniform - 1.0, 4),
-                       "greedy_bpw": p_greedy},
-    }), flush=True)
+        "allocation": {},
+    }
+    for target in (4.0, 5.0, 6.0):
+        t0 = time.perf_counter()
+        bits, info = api.pd_allocate(mse, nparams, target, t_init, iters=500)
+        t_search = time.perf_counter() - t0
+        # the oracle's search on the same tables (numpy on the host)
+        t0 = time.perf_counter()
+        ro = O.pd_search(mse, nparams, target, t_init, iters=500)
+        t_search_cpu = time.perf_counter() - t0
+        uniform = O.pd_objective(mse, nparams, [int(target)] * len(ws))[0]
+        greedy = _greedy_allocation(mse, nparams, target, list(O.PD_CANDIDATES))
+        e_greedy, p_greedy = O.pd_objective(mse, nparams, greedy)
+        out["allocation"][str(target)] = {
+            "mse": info["mse"], "bpw": info["bpw"],
+            "widths": {int(b): int(np.sum(bits == b)) for b in O.PD_CANDIDATES},
+            "vs_uniform": round(info["mse"] / uniform - 1.0, 4),
+            "greedy_reference_vs_uniform": round(e_greedy / uniform - 1.0, 4),
+            "greedy_bpw": p_greedy,
+            "search_s": round(t_search, 4), "oracle_search_s": round(t_search_cpu, 3),
+            "search_matches_oracle": bool(np.array_equal(bits, ro["bits"])),
+        }
+    print(json.dumps(out), flush=True)
 
 
 def system_info(torch):

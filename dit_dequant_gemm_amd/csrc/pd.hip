@@ -4,6 +4,7 @@
 //                      arithmetic as quantize_pack_kernel), float64 sums
 //   sse_total_kernel   the rows' sums in a fixed order (deterministic)
 //   ddg_pd_allocate    the host-side primal-dual search over those tables
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -132,9 +133,7 @@ hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, do
 namespace {
 
 constexpr double kPenalty = 1.0e4;       // the section's quadratic budget penalty
-constexpr double kLr = 0.05;             // Adam step on the tensor parameters
-constexpr double kLrDual = 0.05;         // ascent step on the multiplier
-constexpr double kBeta1 = 0.9, kBeta2 = 0.999, kEps = 1e-8;
+constexpr double kErrorPercent = 100.0;  // error term in percent of the uniform allocation's
 
 // index of the candidate nearest x (the lower one on ties)
 int nearest(const int* cand, int nc, double x) {
@@ -145,6 +144,34 @@ int nearest(const int* cand, int nc, double x) {
     if (d < bd) { bd = d; best = c; }
   }
   return best;
+}
+
+// Largest-remainder rounding within the budget: every tensor starts at the
+// candidate at or below its continuous width; then, by decreasing fraction of
+// the way to the next candidate (lower index first on ties), a tensor moves up
+// one candidate when the added bits still fit in target * sum n.  idx gets the
+// candidate index of every tensor.
+void round_to_budget(const double* b, const int64_t* nparams, int n, const int* cand, int nc,
+                     double budget, std::vector<int>& idx, std::vector<double>& frac,
+                     std::vector<int>& order) {
+  double spent = 0.0;
+  for (int i = 0; i < n; ++i) {
+    int j = 0;
+    while (j + 1 < nc && (double)cand[j + 1] <= b[i]) ++j;
+    idx[i] = j;
+    frac[i] = j + 1 < nc ? (b[i] - cand[j]) / (double)(cand[j + 1] - cand[j]) : 0.0;
+    spent += (double)nparams[i] * (double)cand[j];
+  }
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return frac[x] > frac[y]; });
+  for (int i : order) {
+    if (!(frac[i] > 0.0)) continue;
+    const double add = (double)nparams[i] * (double)(cand[idx[i] + 1] - cand[idx[i]]);
+    if (spent + add <= budget) {
+      ++idx[i];
+      spent += add;
+    }
+  }
 }
 
 }  // namespace
@@ -186,24 +213,34 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
       if (!(mse[(int64_t)i * ncand + c] >= 0.0) || !std::isfinite(mse[(int64_t)i * ncand + c]))
         return DDG_ERR_ARG;
   }
-  // weights of the tensors, and the error table normalised by the uniform
+  // weights of the tensors, and the error table in percent of the uniform
   // allocation at the candidate nearest the target
   double tot = 0.0;
   for (int i = 0; i < n; ++i) tot += (double)nparams[i];
   std::vector<double> wgt(n), m((size_t)n * ncand);
-  for (int i = 0; i < n; ++i) wgt[i] = (double)nparams[i] / tot;
+  double wsq = 0.0;
+  for (int i = 0; i < n; ++i) {
+    wgt[i] = (double)nparams[i] / tot;
+    wsq += wgt[i] * wgt[i];
+  }
   const int j0 = nearest(candidates, ncand, target_bpw);
   double ref = 0.0;
   for (int i = 0; i < n; ++i) ref += wgt[i] * mse[(int64_t)i * ncand + j0];
-  for (size_t x = 0; x < m.size(); ++x) m[x] = ref > 0.0 ? mse[x] / ref : mse[x];
+  for (size_t x = 0; x < m.size(); ++x)
+    m[x] = ref > 0.0 ? kErrorPercent * mse[x] / ref : kErrorPercent * mse[x];
+  // one step size for both updates: 1 / L, L the Lipschitz bound of the
+  // budget penalty's gradient in the tensor parameters
+  const double span = (bmax - bmin) / 4.0;
+  const double step = 1.0 / (2.0 * kPenalty * span * span * wsq);
+  const double budget = target_bpw * tot;
 
-  std::vector<double> t(n), m1(n), m2(n), u(n), b(n), g(n), sw(ncand);
-  std::vector<int> bits(n), best_bits(n);
+  std::vector<double> t(n), u(n), b(n), g(n), sw(ncand), frac(n);
+  std::vector<int> idx(n), order(n), best_bits(n);
   bool have = false;
   int best_feasible = 0, best_restart = 0;
   double best_e = 0.0, best_p = 0.0;
   for (int r = 0; r < restarts; ++r) {
-    for (int i = 0; i < n; ++i) { t[i] = t_init[(int64_t)r * n + i]; m1[i] = 0.0; m2[i] = 0.0; }
+    for (int i = 0; i < n; ++i) t[i] = t_init[(int64_t)r * n + i];
     double lam = 0.5;
     for (int it = 0; it < iters; ++it) {
       for (int i = 0; i < n; ++i) {
@@ -234,22 +271,16 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
         const double dl_db = wgt[i] * (ds_db + lam + 2.0 * kPenalty * gap);
         g[i] = dl_db * (bmax - bmin) * u[i] * (1.0 - u[i]);
       }
-      const double c1 = 1.0 - std::pow(kBeta1, it + 1), c2 = 1.0 - std::pow(kBeta2, it + 1);
-      for (int i = 0; i < n; ++i) {
-        m1[i] = kBeta1 * m1[i] + (1.0 - kBeta1) * g[i];
-        m2[i] = kBeta2 * m2[i] + (1.0 - kBeta2) * g[i] * g[i];
-        t[i] = t[i] - kLr * (m1[i] / c1) / (std::sqrt(m2[i] / c2) + kEps);
-      }
-      lam = lam + kLrDual * gap;
+      for (int i = 0; i < n; ++i) t[i] = t[i] - step * g[i];
+      lam = lam + step * gap;
     }
-    // round to the nearest candidate and score the allocation exactly
+    // round within the budget and score the allocation exactly
+    for (int i = 0; i < n; ++i) b[i] = bmin + (1.0 / (1.0 + std::exp(-t[i]))) * (bmax - bmin);
+    round_to_budget(b.data(), nparams, n, candidates, ncand, budget, idx, frac, order);
     double e = 0.0, p = 0.0;
     for (int i = 0; i < n; ++i) {
-      const double bc = bmin + (1.0 / (1.0 + std::exp(-t[i]))) * (bmax - bmin);
-      const int j = nearest(candidates, ncand, bc);
-      bits[i] = candidates[j];
-      e += (double)nparams[i] * mse[(int64_t)i * ncand + j];
-      p += (double)nparams[i] * (double)candidates[j];
+      e += (double)nparams[i] * mse[(int64_t)i * ncand + idx[i]];
+      p += (double)nparams[i] * (double)candidates[idx[i]];
     }
     e /= tot;
     p /= tot;
@@ -265,7 +296,7 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
       best_e = e;
       best_p = p;
       best_restart = r;
-      best_bits = bits;
+      for (int i = 0; i < n; ++i) best_bits[i] = candidates[idx[i]];
     }
   }
   for (int i = 0; i < n; ++i) bits_out[i] = best_bits[i];

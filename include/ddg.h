@@ -213,12 +213,17 @@ int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_
  * sum_i n_i b_i / sum_i n_i <= target_bpw by the section's relaxation: one
  * parameter per tensor, b = bmin + sigmoid(t) (bmax - bmin); a softmax over
  * the candidates of -|b - c| / temp, temp = max(2 (1 - it/iters), 0.05),
- * blends the tensor's error row (normalised by the uniform allocation at the
- * candidate nearest the target); loss = error + lambda (bpw - target)
- * + 1e4 (bpw - target)^2; Adam steps (lr 0.05) on the parameters and ascent
- * steps (0.05) on lambda, from lambda = 0.5.  Each restart's widths are the
- * nearest candidates (the lower on ties); the kept restart has the lowest
- * exact error within the budget, else the lowest bpw.
+ * blends the tensor's error row (in percent of the error of the uniform
+ * allocation at the candidate nearest the target); loss = error
+ * + lambda (bpw - target) + 1e4 (bpw - target)^2.  Plain gradient descent on
+ * the parameters and ascent on lambda (from 0.5), both with the step 1/L,
+ * L = 2e4 ((bmax - bmin)/4)^2 sum_i (n_i / sum n)^2 the Lipschitz bound of the
+ * penalty's gradient.  Each restart's widths come from largest-remainder
+ * rounding within the budget: every tensor starts at the candidate at or below
+ * its width, then moves up one candidate, by decreasing fraction of the way
+ * there (lower index first on ties), while the added bits fit in
+ * target * sum n.  The kept restart has the lowest exact error within the
+ * budget, else the lowest bpw; ties go to the earlier restart.
  *   mse        n x ncand per-weight errors (row i: tensor i, column c: width
  *              candidates[c]); finite, >= 0.
  *   nparams    n weight counts, > 0.

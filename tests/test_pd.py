@@ -85,6 +85,59 @@ def test_loss_gradient_matches_finite_differences():
             assert abs(fd - g[i]) <= 1e-5 * max(1.0, abs(fd)), (temp, i, fd, g[i])
 
 
+def test_round_to_budget_worked_examples():
+    # floors 4,4,5 spend 13 of 15; fractions .6 .4 .9: raise the third, then
+    # the first; the second no longer fits
+    assert list(O.round_to_budget([4.6, 4.4, 5.9], [1, 1, 1], 5.0)) == [5, 4, 6]
+    # equal fractions: the earlier tensor goes first, but its 3 bits do not fit
+    # in the 1.2 left; the later one's single bit does
+    assert list(O.round_to_budget([4.5, 4.5], [3, 1], 4.3)) == [4, 5]
+    # widths on candidates stay; the top candidate never moves up
+    assert list(O.round_to_budget([3.0, 7.0, 5.0], [2, 2, 2], 7.0)) == [3, 7, 5]
+    # uneven candidates: 4.5 is a quarter of the way from 4 to 6
+    assert list(O.round_to_budget([4.5, 4.9], [1, 1], 5.0, candidates=(3, 4, 6, 8))) == [4, 6]
+
+
+def test_round_to_budget_is_within_budget_and_maximal():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        k = int(rng.integers(1, 12))
+        n = rng.integers(1, 100, size=k).astype(np.int64)
+        b = rng.uniform(3.0, 7.0, size=k)
+        target = float(np.sum(n * b) / np.sum(n)) + float(rng.uniform(-0.3, 0.3))
+        target = min(max(target, 3.0), 7.0)
+        r = O.round_to_budget(b, n, target)
+        lo = np.floor(b)
+        assert np.all((r == lo) | (r == lo + 1))
+        if np.sum(n * lo) <= target * np.sum(n):
+            left = target * np.sum(n) - np.sum(n * r)
+            assert left >= 0
+            # every tensor left below its width could not have moved up
+            for i in np.nonzero((r == lo) & (b > lo))[0]:
+                assert n[i] > left
+
+
+def test_step_is_the_penalty_curvature_bound():
+    """At t = 0 (sigmoid slope 1/4 everywhere) on the budget (gap 0) the
+    penalty's Hessian is the rank-one 2e4 v v^T with |v|^2 = sum_i (w_i span/4)^2,
+    so its largest eigenvalue, taken here by finite differences of the loss
+    gradient with the error term off, is exactly 1/step."""
+    n = np.array([3, 1, 4, 1, 5, 9], dtype=np.int64) * 1000
+    wgt = n / n.sum()
+    zero = np.zeros((6, 5))
+    h = 1e-6
+    hess = np.empty((6, 6))
+    for i in range(6):
+        tp, tm = np.zeros(6), np.zeros(6)
+        tp[i] += h
+        tm[i] -= h
+        gp = O.pd_loss_grad(tp, 0.0, zero, wgt, CAND, 5.0, 1.0)[1]
+        gm = O.pd_loss_grad(tm, 0.0, zero, wgt, CAND, 5.0, 1.0)[1]
+        hess[:, i] = (gp - gm) / (2 * h)
+    top = np.linalg.eigvalsh(0.5 * (hess + hess.T)).max()
+    assert top == pytest.approx(1.0 / O.pd_step(n), rel=1e-5)
+
+
 def _search(mse, n, target, seed=0, restarts=6, iters=300):
     t_init = 0.5 * np.random.default_rng(seed).standard_normal((restarts, len(n)))
     return O.pd_search(mse, n, target, t_init, iters=iters), t_init
@@ -96,7 +149,7 @@ def test_search_is_invariant_to_order_scale_and_counts():
     perm = np.random.default_rng(1).permutation(len(n))
     rp = O.pd_search(mse[perm], n[perm], 4.5, t_init[:, perm], iters=300)
     assert np.array_equal(rp["bits"], r["bits"][perm])
-    rs = O.pd_search(mse * 1000.0, n, 4.5, t_init, iters=300)       # normalised table (R9)
+    rs = O.pd_search(mse * 1024.0, n, 4.5, t_init, iters=300)       # normalised table (R9)
     assert np.array_equal(rs["bits"], r["bits"])
     rn = O.pd_search(mse, n * 7, 4.5, t_init, iters=300)            # only shares of weights count
     assert np.array_equal(rn["bits"], r["bits"])
