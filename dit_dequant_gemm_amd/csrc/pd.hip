@@ -6,6 +6,7 @@
 //   ddg_pd_allocate    the host-side primal-dual search over those tables
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <vector>
 
@@ -16,18 +17,20 @@ namespace ddg {
 
 constexpr int kSseWidths = 5;            // widths 3..7
 
-// One workgroup (256 lanes) per row; lane i takes chunks i, i+256, ... (32
-// weights each, the 4 chunks of a group in one quad).
+// One workgroup of 1..4 waves per row; lane i takes chunks i, i+lanes, ...
+// (32 weights each, the 4 chunks of a group in one quad).  The wave count is
+// chosen on the host so that the last pass leaves few lanes idle.
 template <bool F32_IN>
 __global__ __launch_bounds__(256) void quant_sse_kernel(const void* __restrict__ w, int64_t k,
                                                        double* __restrict__ row_sse) {
   __shared__ double red[4][kSseWidths];
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
+  const int lanes = blockDim.x;
   const int chunks = (int)(k / 32);
   double acc[kSseWidths] = {0.0, 0.0, 0.0, 0.0, 0.0};
   // whole quads per pass, so that the butterfly never mixes groups
-  for (int c0 = 0; c0 < chunks; c0 += 256) {
+  for (int c0 = 0; c0 < chunks; c0 += lanes) {
     const int c = c0 + lane;
     const bool valid = c < chunks;
     float v[32];
@@ -88,8 +91,11 @@ __global__ __launch_bounds__(256) void quant_sse_kernel(const void* __restrict__
     if ((lane & 63) == 0) red[lane >> 6][j] = x;
   }
   __syncthreads();
-  if (lane < kSseWidths)
-    row_sse[row * kSseWidths + lane] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  if (lane < kSseWidths) {
+    double x = red[0][lane];
+    for (int wv = 1; wv < lanes / 64; ++wv) x += red[wv][lane];
+    row_sse[row * kSseWidths + lane] = x;
+  }
 }
 
 // totals[j] = sum over rows of row_sse[row][j], rows in order per lane
@@ -115,10 +121,18 @@ __global__ __launch_bounds__(256) void sse_total_kernel(const double* __restrict
 hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, double* row_sse,
                             double* total, hipStream_t stream) {
   if (n > 0) {
+    // waves per row: the fewest lane slots over all passes, then the most waves
+    const int64_t chunks = k / 32;
+    int waves = 1;
+    int64_t best = INT64_MAX;
+    for (int wv = 1; wv <= 4; ++wv) {
+      const int64_t slots = (chunks + 64 * wv - 1) / (64 * wv) * (64 * wv);
+      if (slots <= best) { best = slots; waves = wv; }
+    }
     if (f32_in)
-      quant_sse_kernel<true><<<dim3((unsigned)n), dim3(256), 0, stream>>>(w, k, row_sse);
+      quant_sse_kernel<true><<<dim3((unsigned)n), dim3(64 * waves), 0, stream>>>(w, k, row_sse);
     else
-      quant_sse_kernel<false><<<dim3((unsigned)n), dim3(256), 0, stream>>>(w, k, row_sse);
+      quant_sse_kernel<false><<<dim3((unsigned)n), dim3(64 * waves), 0, stream>>>(w, k, row_sse);
     if (hipError_t e = hipGetLastError()) return e;
   }
   sse_total_kernel<<<dim3(1), dim3(256), 0, stream>>>(row_sse, n, total);

@@ -28,7 +28,7 @@ def _check_sse(api, w, f32):
         assert total[j] == pytest.approx(ref.sum(), rel=1e-12, abs=0.0)
 
 
-@pytest.mark.parametrize("n,k", [(1, 128), (33, 384), (64, 5120), (5, 13824), (3, 40960)])
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 384), (7, 4096), (64, 5120), (5, 13824), (3, 40960)])
 def test_quant_sse_random(gpu_lib, n, k):
     _case(f"quant_sse n={n} k={k}")
     w = synth.random_case(n * 7 + k, 1, n, k, wstd=0.03)["w"]
@@ -75,3 +75,33 @@ def test_allocation_end_to_end(gpu_lib):
         ro = O.pd_search(mse_ref, n_ref, target, t_init, iters=300)
         assert np.array_equal(bits, ro["bits"]), (target, bits, ro["bits"])
         assert info["bpw"] <= target + 1e-9
+
+
+def test_allocation_drives_a_grouped_block(gpu_lib):
+    """The search's widths drive the block's products: every tensor packed at
+    its allocated width (bytes and scales as the oracle's), then one grouped
+    launch of the block's products at 16 tokens against the oracle product."""
+    _case("allocation -> quantize_pack at the chosen widths -> grouped products")
+    from parity_util import check_product, host
+    rng = np.random.default_rng(31)
+    shapes = [(256, 512), (256, 512), (256, 512), (256, 512), (704, 512), (512, 768)]
+    ws = [synth.to_bf16(rng.normal(0, 0.01 * (1 + i), size=s)) for i, s in enumerate(shapes)]
+    ws[3] = synth.to_bf16(rng.standard_t(3, size=shapes[3]) * 0.02)
+    mse, nparams = gpu_lib.mse_table([dev_bf16(w) for w in ws])
+    t_init = 0.5 * np.random.default_rng(32).standard_normal((6, len(ws)))
+    bits, info = gpu_lib.pd_allocate(mse, nparams, 5.0, t_init, iters=300)
+    assert info["bpw"] <= 5.0 + 1e-9 and len(set(bits.tolist())) > 1
+    items, refs = [], []
+    for i, (w, b) in enumerate(zip(ws, bits)):
+        qw = gpu_lib.quantize_pack(dev_bf16(w), int(b))
+        packed_ref, scales_ref, _ = O.quantize_pack(w, int(b))
+        assert np.array_equal(host(qw.packed).reshape(-1), np.asarray(packed_ref).reshape(-1))
+        assert np.array_equal(host(qw.scales).view(np.uint32).reshape(-1),
+                              np.asarray(scales_ref, dtype=np.float32).view(np.uint32).reshape(-1))
+        x = synth.to_bf16(rng.normal(0, 1, size=(16, w.shape[1])))
+        items.append((dev_bf16(x), qw, torch.empty((16, w.shape[0]), dtype=torch.float32, device="cuda")))
+        q_u, s = O.quantize_groups(w, int(b))
+        refs.append(O.gemm_ref(x, O.dequant_bf16(q_u, s, int(b))))
+    outs = gpu_lib.dequant_gemm_grouped(items)
+    for b, y, ref in zip(bits, outs, refs):
+        check_product(host(y), ref, False, f"allocated width {b}")
