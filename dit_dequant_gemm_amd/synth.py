@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = ["to_bf16", "config1", "config2", "config3", "config4", "config5_weights",
            "config5_bits", "config5_x", "C5_SHAPES", "C5_BIT_CHOICES", "C5_BIT_PROBS",
-           "random_case"]
+           "random_case", "rpbh_draw"]
 
 
 def to_bf16(a) -> np.ndarray:
@@ -155,3 +155,12 @@ def random_case(seed: int, m: int, n: int, k: int, wstd: float = 0.02):
     rng = np.random.default_rng([99, seed])
     return {"w": to_bf16(rng.normal(0.0, wstd, size=(n, k))),
             "x": to_bf16(rng.normal(0.0, 1.0, size=(m, k)))}
+
+
+def rpbh_draw(d: int, seed: int):
+    """The random draws of a rotation over d coordinates: a permutation of
+    0..d-1 (int32) and Rademacher signs +-1 (int8)."""
+    rng = np.random.default_rng([77, seed, d])
+    perm = rng.permutation(d).astype(np.int32)
+    signs = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    return perm, signs
