@@ -52,7 +52,10 @@ SIGNATURES = {
                                  ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_double)]),
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
+    "ddg_rpbh_rotate": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp]),
 }
+
+ROTATE_MAX_D, ROTATE_MAX_H = 16384, 1024
 
 
 class DDGError(RuntimeError):
@@ -161,6 +164,38 @@ def quantize_pack(w: torch.Tensor, bits: int) -> QWeight:
                                  n, k, bits, packed.data_ptr(), scales.data_ptr(),
                                  _stream_ptr(w.device)), "ddg_quantize_pack")
     return QWeight(packed, scales, bits, n, k, orig_in)
+
+
+def rpbh_rotate(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor, h: int,
+                out_dtype: Optional[torch.dtype] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of x (n x d, bf16 or float32) rotated by the random-permuted block
+    Hadamard map: permute by perm (int32), flip by signs (int8, negative = -1),
+    then a normalised Walsh-Hadamard transform on each block of h.  Rotate the
+    weight rows once (then quantize them) and every activation row with the
+    same perm, signs and h: the product is unchanged."""
+    for t, name in ((x, "x"), (perm, "perm"), (signs, "signs")):
+        _require_cuda(t, name)
+    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a 2-D bf16 or float32 tensor")
+    n, d = x.shape
+    if perm.dtype != torch.int32 or signs.dtype != torch.int8 or perm.shape != (d,) or signs.shape != (d,):
+        raise ValueError("perm must be int32 and signs int8, each of length d")
+    x = x.contiguous()
+    perm = perm.contiguous()
+    signs = signs.contiguous()
+    odt = out_dtype or (out.dtype if out is not None else x.dtype)
+    if out is None:
+        out = torch.empty((n, d), dtype=odt, device=x.device)
+    elif out.shape != (n, d) or out.dtype != odt or not out.is_contiguous():
+        raise ValueError("out must be a contiguous n x d tensor of the output dtype")
+    code = {torch.bfloat16: DDG_BF16, torch.float32: DDG_F32}
+    if odt not in code:
+        raise ValueError("out dtype must be bf16 or float32")
+    _check(load_library().ddg_rpbh_rotate(x.data_ptr(), code[x.dtype], n, d, perm.data_ptr(),
+                                          signs.data_ptr(), h, out.data_ptr(), code[odt],
+                                          _stream_ptr(x.device)), "ddg_rpbh_rotate")
+    return out
 
 
 def dequantize(qw: QWeight) -> torch.Tensor:

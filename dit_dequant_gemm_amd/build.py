@@ -43,6 +43,7 @@ def _units():
     units.append((os.path.join(CSRC, "lowrank.hip"), "lowrank", []))
     units.append((os.path.join(CSRC, "grouped.hip"), "grouped", []))
     units.append((os.path.join(CSRC, "pd.hip"), "pd", []))
+    units.append((os.path.join(CSRC, "rotate.hip"), "rotate", []))
     units.append((os.path.join(CSRC, "api.hip"), "api", []))
     return units
 

@@ -327,4 +327,26 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
   return hip_status(launch_product(a, bits, cus, stream));
 }
 
+int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,
+                    const int8_t* signs, int h, void* out, int out_dtype, hipStream_t stream) {
+  if ((x_dtype != DDG_BF16 && x_dtype != DDG_F32) || (out_dtype != DDG_BF16 && out_dtype != DDG_F32))
+    return DDG_ERR_ARG;
+  if (n < 0 || n > kMaxDim || d <= 0 || d % 64 || d > DDG_ROTATE_MAX_D || h < 2 ||
+      h > DDG_ROTATE_MAX_H || (h & (h - 1)) || d % h || !mul_ok(n, d) || !mul_ok(n * d, 4))
+    return DDG_ERR_SHAPE;
+  if (n == 0) return DDG_OK;
+  if (!x || !perm || !signs || !out) return DDG_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(perm, 4)) return DDG_ERR_ALIGN;
+  // in place only as the very same buffer and type; otherwise no overlap
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t xb = xa + (uintptr_t)(n * d * (x_dtype == DDG_F32 ? 4 : 2));
+  const uintptr_t ob = oa + (uintptr_t)(n * d * (out_dtype == DDG_F32 ? 4 : 2));
+  const bool same = xa == oa && x_dtype == out_dtype;
+  if (!same && xa < ob && oa < xb) return DDG_ERR_ARG;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(ddg::launch_rpbh_rotate(x, x_dtype == DDG_F32, n, (int)d, perm, signs, h, out,
+                                            out_dtype == DDG_F32, cus, stream));
+}
+
 }  // extern "C"

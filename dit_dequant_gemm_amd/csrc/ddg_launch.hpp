@@ -34,6 +34,13 @@ hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream);
 hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, double* row_sse,
                             double* total, hipStream_t stream);
 
+// RPBH rotation of n rows of d (d % 64 == 0, d % h == 0, d <= kRotateMaxD,
+// h a power of two in 2..1024)
+constexpr int kRotateMaxD = 16384;
+hipError_t launch_rpbh_rotate(const void* x, bool f32_in, int64_t n, int d, const int32_t* perm,
+                              const int8_t* signs, int h, void* out, bool f32_out, int cus,
+                              hipStream_t stream);
+
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
 

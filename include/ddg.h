@@ -239,6 +239,32 @@ int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int*
                     int ncand, double target_bpw, const double* t_init, int restarts,
                     int iters, int* bits_out, double* info);
 
+/*
+ * Random-permuted block-Hadamard (RPBH) rotation of rows (the OrbitQuant
+ * article, §2.1 "rotation quantization", §2.2 "offline-online"): for each of the
+ * n rows of x (n x d, row-major),
+ *   out[r, b h + j] = sum_t H[j, t] / sqrt(h) * s[b h + t] * x[r, perm[b h + t]],
+ * H the Sylvester Walsh-Hadamard matrix of order h (H_2k = [[H_k, H_k],
+ * [H_k, -H_k]]), s = -1 where signs[i] < 0, else +1.  With perm a permutation
+ * of 0..d-1 the map is orthogonal: rotating the weight rows offline (then
+ * quantizing them) and the activation rows online leaves X W^T unchanged.
+ * Arithmetic in float32 (butterfly order fixed); bf16 outputs are rounded to
+ * nearest even.
+ *   x, out     device, n x d, x_dtype / out_dtype (DDG_BF16 or DDG_F32),
+ *              16-byte aligned.  out may be x itself when the dtypes match;
+ *              otherwise the buffers must not overlap.
+ *   perm       device, d int32 (4-byte aligned); entries outside [0, d) read as 0.
+ *   signs      device, d int8.
+ *   h          block size: a power of two, 2..DDG_ROTATE_MAX_H, dividing d.
+ *   d          a multiple of 64, at most DDG_ROTATE_MAX_D.
+ * n == 0 is a no-op.  Errors: DDG_ERR_ARG (dtype, null pointer, overlapping
+ * buffers), DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+#define DDG_ROTATE_MAX_D 16384
+#define DDG_ROTATE_MAX_H 1024
+int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,
+                    const int8_t* signs, int h, void* out, int out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

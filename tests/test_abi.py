@@ -181,3 +181,27 @@ def test_lowrank_fused_gemm_rejects_bad_arguments(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         api.load_library(str(tmp_path / "missing.so"))
+
+
+def test_rpbh_rotate_rejects_bad_arguments(lib):
+    f = lib.ddg_rpbh_rotate
+    base = dict(x=FAKE, xdt=0, n=4, d=256, perm=FAKE, signs=FAKE, h=64, out=FAKE + (1 << 20), odt=0)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return f(a["x"], a["xdt"], a["n"], a["d"], a["perm"], a["signs"], a["h"], a["out"], a["odt"], None)
+
+    assert call(xdt=2) == E_ARG and call(odt=-1) == E_ARG
+    assert call(d=100) == E_SHAPE                  # d % 64
+    assert call(d=api.ROTATE_MAX_D + 64) == E_SHAPE
+    assert call(h=48) == E_SHAPE and call(h=1) == E_SHAPE and call(h=2048) == E_SHAPE
+    assert call(d=192, h=128) == E_SHAPE           # h does not divide d
+    assert call(n=-1) == E_SHAPE
+    assert call(x=None) == E_ARG and call(perm=None) == E_ARG and call(signs=None) == E_ARG
+    assert call(out=None) == E_ARG
+    assert call(x=MISALIGNED) == E_ALIGN and call(out=FAKE + (1 << 20) + 8) == E_ALIGN
+    assert call(perm=FAKE + 2) == E_ALIGN
+    assert call(out=FAKE + 512, xdt=0, odt=0) == E_ARG            # partial overlap
+    assert call(out=FAKE, xdt=0, odt=1) == E_ARG                  # same start, other dtype
+    assert call(n=0, x=None, perm=None, signs=None, out=None) == OK
