@@ -57,11 +57,13 @@ def parse():
                                                       "dequant_gemm_attnproj3072_traffic.md"),
                     help="profile summary holding the measured HBM bytes per launch of the "
                          "dominant kernel (used only while the kernel sources are unchanged)")
-    ap.add_argument("--suite", choices=["block16", "alloc"], default=None,
+    ap.add_argument("--suite", choices=["block16", "alloc", "rotate"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
                          "one by one and grouped, one JSON line each; alloc: error tables of a "
-                         "synthetic 4-block model on the GPU and the PD-guided bit allocation")
+                         "synthetic 4-block model on the GPU and the PD-guided bit allocation; "
+                         "rotate: the block-Hadamard activation pre-pass against HBM, its cost next "
+                         "to the product, and its accuracy on the outlier workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -314,6 +316,114 @@ def alloc_suite(args):
     print(json.dumps(out), flush=True)
 
 
+def rotate_suite(args):
+    """The rotation row: the activation pre-pass (4096 x 3072 bf16, h = 128)
+    against HBM (round-robin over copies totalling >= 1 GiB), its cost next to
+    the 4-bit product it feeds, the offline weight rotation + quantization, and
+    what it buys on the outlier workload: relative Frobenius error of the 4-bit
+    product against the float32 product of the unquantized weight."""
+    import numpy as np
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    h = 128
+
+    def burst(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        reps = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            reps.append(e0.elapsed_time(e1) / steps)
+        return sorted(reps)[2]
+
+    c2 = synth.config2()
+    m, k = c2["x"].shape
+    n = c2["w"].shape[0]
+    perm, signs = synth.rpbh_draw(k, 1)
+    pd, sd = torch.from_numpy(perm).to(dev), torch.from_numpy(signs).to(dev)
+    x0 = torch.from_numpy(c2["x"]).to(dev, torch.bfloat16)
+    copies = max(2, -(-ROTATE_BYTES // (x0.numel() * 2)))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    outs = [torch.empty_like(x0) for _ in range(copies)]
+    api.rpbh_rotate(xs[0], pd, sd, h, out=outs[0])            # checks once through the binding
+    # then the entry point itself with prepared arguments, so that the burst
+    # measures the GPU rather than Python's argument handling
+    lib = api.load_library()
+    sp = torch.cuda.current_stream().cuda_stream
+    calls = [(xs[i].data_ptr(), outs[i].data_ptr()) for i in range(copies)]
+    it = [0]
+
+    def rot():
+        xp, op = calls[it[0] % copies]
+        it[0] += 1
+        st = lib.ddg_rpbh_rotate(xp, api.DDG_BF16, m, k, pd.data_ptr(), sd.data_ptr(), h, op,
+                                 api.DDG_BF16, sp)
+        if st:
+            raise api.DDGError(st, "ddg_rpbh_rotate")
+
+    ms_rot = burst(rot, args.steps)
+    rot_bytes = m * k * 4
+    # offline: rotate the weight (float32 out) and quantize it
+    w = torch.from_numpy(c2["w"]).to(dev, torch.bfloat16)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    wr = api.rpbh_rotate(w, pd, sd, h, out_dtype=torch.float32)
+    qw = api.quantize_pack(wr, 4)
+    e1.record(stream)
+    e1.synchronize()
+    ms_offline = e0.elapsed_time(e1)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ms_gemm = burst(lambda: api.dequant_gemm(outs[0], qw, out=y), args.steps)
+    del xs, outs
+
+    # accuracy on the outlier workload (first 1024 tokens)
+    c4 = synth.config4()
+    w4 = torch.from_numpy(c4["w"]).to(dev, torch.bfloat16)
+    x4 = torch.from_numpy(c4["x"][:1024]).to(dev, torch.bfloat16)
+    y_ref = x4.float() @ w4.float().t().contiguous()
+    perm4, signs4 = synth.rpbh_draw(c4["w"].shape[1], 2)
+    p4, s4 = torch.from_numpy(perm4).to(dev), torch.from_numpy(signs4).to(dev)
+
+    def rel(a):
+        return float(torch.linalg.norm(a.float() - y_ref) / torch.linalg.norm(y_ref))
+
+    def wsnr(w_ref, qw_):
+        d = api.dequantize(qw_).float()
+        return float(10 * torch.log10((w_ref.float() ** 2).sum() / ((w_ref.float() - d) ** 2).sum()))
+
+    acc = {}
+    for bits in (3, 4):
+        qp = api.quantize_pack(w4, bits)
+        yp = api.dequant_gemm(x4, qp, torch.float32)
+        wr4 = api.rpbh_rotate(w4, p4, s4, h, out_dtype=torch.float32)
+        qr = api.quantize_pack(wr4, bits)
+        yr = api.dequant_gemm(api.rpbh_rotate(x4, p4, s4, h), qr, torch.float32)
+        acc[str(bits)] = {"plain_rel_err": round(rel(yp), 5), "rotated_rel_err": round(rel(yr), 5),
+                          "plain_weight_snr_db": round(wsnr(w4, qp), 2),
+                          "rotated_weight_snr_db": round(wsnr(wr4, qr), 2)}
+    print(json.dumps({
+        "suite": "rpbh-rotation", "h": h,
+        "activation_prepass": {"shape": [m, k], "dtype": "bf16->bf16", "us": round(ms_rot * 1e3, 2),
+                               "GBps": round(rot_bytes / ms_rot / 1e6, 1),
+                               "frac_of_hbm_peak": round(rot_bytes / ms_rot / 1e6 / 8000.0, 4),
+                               "copies_rotated": copies},
+        "gemm_4bit_on_rotated_x_us": round(ms_gemm * 1e3, 2),
+        "prepass_overhead_vs_gemm": round(ms_rot / ms_gemm, 4),
+        "offline_weight_rotate_and_quantize_us": round(ms_offline * 1e3, 1),
+        "outlier_workload_accuracy": acc,
+    }), flush=True)
+
+
 def system_info(torch):
     """GPU name, clock and ROCm build; host CPU model."""
     info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
@@ -412,6 +522,9 @@ def main():
         return
     if args.suite == "alloc":
         alloc_suite(args)
+        return
+    if args.suite == "rotate":
+        rotate_suite(args)
         return
 
     c = synth.config2(m=M_BIG)

@@ -139,3 +139,24 @@ def test_rotated_product_end_to_end(gpu_lib, bits):
     q_u, s = O.quantize_groups(wr_ref, bits)
     y_ref = O.gemm_ref(xr_ref, O.dequant_bf16(q_u, s, bits))
     check_product(y, y_ref, False, f"rotated product bits={bits}")
+
+
+@pytest.mark.parametrize("n,d,h,f32", [(600, 16384, 64, False), (520, 16384, 64, True),
+                                       (9000, 256, 16, False), (700, 13824, 128, True)])
+def test_rotate_several_rows_per_wave(gpu_lib, n, d, h, f32):
+    """Row counts above the resident waves: each wave rotates several rows,
+    loading the next while it computes (two row buffers), or one after the
+    other where two float32 rows do not fit next to the table."""
+    _case(f"rpbh_rotate n={n} d={d} h={h} f32={f32} (several rows per wave)")
+    rng = np.random.default_rng(n + d)
+    x = rng.normal(0, 1, size=(n, d)).astype(np.float32)
+    if not f32:
+        x = synth.to_bf16(x)
+    perm, signs, pd, sd = _draw(d, n)
+    xd = dev_f32(x) if f32 else dev_bf16(x)
+    got = host(gpu_lib.rpbh_rotate(xd, pd, sd, h, out_dtype=torch.float32))
+    rows = np.r_[0:8, n // 2:n // 2 + 8, n - 8:n]
+    _check_f32(got[rows], x[rows], perm, signs, h)
+    # every row, through a cheaper exact property: the rotation keeps each row's norm
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)
+    assert np.allclose(np.linalg.norm(got.astype(np.float64), axis=1), nx, rtol=2e-6)
