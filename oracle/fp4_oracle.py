@@ -1,0 +1,156 @@
+"""CPU oracle for the FP4-weight / FP8-activation (W4A8) product.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module; the
+product (libddg.so) shares no code with it.
+
+Source: [FP4] the FP4DiT article (aijishu.com).
+  - §3.1.2: floating-point quantization -- the exponent picks a range, the
+    mantissa gives uniform levels inside it.
+  - §3.2.1 / §4.1: 4-bit weight formats E2M1, E3M0 (denser near zero, for the
+    first linear of the pointwise feed-forward network) and E1M2; weight groups
+    of 128.
+  - §3.2.3 / §4.1: per-token online min-max activation quantization to 8 bits
+    (W4A8).
+
+Readings where the article is silent (each is repeated in the design doc):
+
+R18  The 4-bit formats are sign + magnitude minifloats, subnormal when the
+     exponent field is 0: E2M1 bias 1 (0, .5, 1, 1.5, 2, 3, 4, 6), E1M2 bias 1
+     (0, .25, .5, .75, 1, 1.25, 1.5, 1.75), E3M0 bias 3 (0, 2^-2 .. 2^4).  Code =
+     sign << 3 | magnitude index; a zero magnitude is always code 0.
+R19  Weight groups are 128 consecutive weights along the input dimension (as the
+     integer path; the article's "along the output channel" is garbled next to
+     its group size and the storage of [WDQ]).  Scale s = fl32(amax / vmax),
+     r = fl32(w / s) (correctly rounded division), code = the nearest format value
+     to |r|, ties to the even code; an all-zero group gets scale 0 and code 0.
+R20  The 8-bit activations are FP8 E4M3 (bias 7, largest 448, no infinities),
+     the 8-bit format of the MFMA that takes FP4 operands; per token (row)
+     s_x = fl32(amax / 448), r = fl32(x / s_x), q = E4M3 round-to-nearest-even
+     of r (|r| clamped to 448 first); an all-zero row gets scale 0 and zeros.
+R21  Packing: two codes per byte, the even index in the low nibble (the operand
+     order of the gfx950 FP4 matrix instructions), rows of k/2 bytes.
+R22  The product: Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k],
+     q_x and v_w the exact E4M3 and FP4 values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["FP4_FORMATS", "fp4_values", "minifloat_value", "quantize_fp4_groups", "pack_fp4",
+           "unpack_fp4", "fp4_decode", "e4m3_values", "e4m3_round", "e4m3_decode",
+           "quantize_rows_e4m3", "w4a8_ref"]
+
+FP4_FORMATS = {"e2m1": (2, 1, 1), "e3m0": (3, 0, 3), "e1m2": (1, 2, 1)}   # ebits, mbits, bias
+GROUP = 128
+E4M3_MAX = 448.0
+
+
+def minifloat_value(code: int, ebits: int, mbits: int, bias: int) -> float:
+    """Value of a sign + magnitude minifloat code (subnormal when the exponent field is 0)."""
+    sign = -1.0 if (code >> (ebits + mbits)) & 1 else 1.0
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    if e == 0:
+        return sign * (m / float(1 << mbits)) * 2.0 ** (1 - bias)
+    return sign * (1.0 + m / float(1 << mbits)) * 2.0 ** (e - bias)
+
+
+def fp4_values(fmt: str) -> np.ndarray:
+    """The 8 magnitudes of a 4-bit format, by magnitude index (R18)."""
+    eb, mb, bias = FP4_FORMATS[fmt]
+    return np.array([minifloat_value(i, eb, mb, bias) for i in range(8)], dtype=np.float64)
+
+
+def fp4_decode(codes, fmt: str) -> np.ndarray:
+    mag = fp4_values(fmt)[np.asarray(codes) & 7]
+    return np.where(np.asarray(codes) & 8, -mag, mag)
+
+
+def _nearest_index(mag_r, levels):
+    """Index of the level nearest each |r| (levels ascending), ties to the even index."""
+    mag_r = np.asarray(mag_r, dtype=np.float64)
+    idx = np.searchsorted(levels, mag_r, side="left")          # levels[idx-1] < r <= levels[idx]
+    idx = np.clip(idx, 1, len(levels) - 1)
+    lo, hi = levels[idx - 1], levels[idx]
+    dlo, dhi = mag_r - lo, hi - mag_r
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (idx % 2 == 0))
+    out = np.where(pick_hi, idx, idx - 1)
+    out = np.where(mag_r >= levels[-1], len(levels) - 1, out)
+    return out
+
+
+def quantize_fp4_groups(w, fmt: str):
+    """(codes n x k uint8 in 0..15, scales n x k/128 float32) per R19."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    levels = fp4_values(fmt)
+    vmax = np.float32(levels[-1])
+    g = w.reshape(n, k // GROUP, GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = (amax / vmax).astype(np.float32)
+        r = (g / s[:, :, None]).astype(np.float32)
+    zero = s[:, :, None] == 0
+    r = np.where(zero, np.float32(0), r)
+    idx = _nearest_index(np.abs(r), levels)
+    codes = np.where((idx > 0) & (r < 0), idx | 8, idx).astype(np.uint8)
+    return codes.reshape(n, k), s
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """Rows of k codes -> rows of k/2 bytes, even index in the low nibble (R21)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 15
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def e4m3_values() -> np.ndarray:
+    """All finite E4M3 magnitudes (codes 0..126), ascending (bias 7; 127 is NaN)."""
+    return np.array([minifloat_value(c, 4, 3, 7) for c in range(127)], dtype=np.float64)
+
+
+def e4m3_round(r) -> np.ndarray:
+    """E4M3 codes (uint8) of float32 values: clamp to +-448, round to nearest even (R20)."""
+    r = np.asarray(r, dtype=np.float64)
+    mag = np.minimum(np.abs(r), E4M3_MAX)
+    idx = _nearest_index(mag, e4m3_values())
+    return np.where((idx > 0) & (r < 0), idx | 0x80, idx).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = e4m3_values()[c & 0x7F]
+    return np.where(c & 0x80, -mag, mag)
+
+
+def quantize_rows_e4m3(x):
+    """(codes m x k uint8, scales m float32) per token (R20)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = (x / s[:, None]).astype(np.float32)
+    r = np.where(s[:, None] == 0, np.float32(0), r)
+    return e4m3_round(r), s
+
+
+def w4a8_ref(xcodes, xscales, wcodes, wscales, fmt: str) -> np.ndarray:
+    """R22 in float64: s_x[m] * sum_g s_w[n, g] (Q_x,g @ V_w,g^T)."""
+    qx = e4m3_decode(xcodes)
+    vw = fp4_decode(wcodes, fmt)
+    m, k = qx.shape
+    n = vw.shape[0]
+    y = np.zeros((m, n), dtype=np.float64)
+    sw = np.asarray(wscales, dtype=np.float64)
+    for g in range(k // GROUP):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        y += (qx[:, sl] @ vw[:, sl].T) * sw[None, :, g]
+    return y * np.asarray(xscales, dtype=np.float64)[:, None]
