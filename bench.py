@@ -57,13 +57,14 @@ def parse():
                                                       "dequant_gemm_attnproj3072_traffic.md"),
                     help="profile summary holding the measured HBM bytes per launch of the "
                          "dominant kernel (used only while the kernel sources are unchanged)")
-    ap.add_argument("--suite", choices=["block16", "alloc", "rotate"], default=None,
+    ap.add_argument("--suite", choices=["block16", "alloc", "rotate", "w4a8"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
                          "one by one and grouped, one JSON line each; alloc: error tables of a "
                          "synthetic 4-block model on the GPU and the PD-guided bit allocation; "
                          "rotate: the block-Hadamard activation pre-pass against HBM, its cost next "
-                         "to the product, and its accuracy on the outlier workload")
+                         "to the product, and its accuracy on the outlier workload; w4a8: FP4 "
+                         "weights x FP8 per-token activations on the scaled matrix cores")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -424,6 +425,82 @@ def rotate_suite(args):
     }), flush=True)
 
 
+def w4a8_suite(args):
+    """FP4 (E2M1) weights x per-token FP8 (E4M3) activations at the attention
+    projection (4096 x 3072 x 3072): the activation quantizer against HBM, the
+    product against the dense FP8 matrix peak, the 4-bit bf16 product beside
+    it, and each path's error against the float32 product of the unquantized
+    weight."""
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def burst(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        reps = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            reps.append(e0.elapsed_time(e1) / steps)
+        return sorted(reps)[2]
+
+    c = synth.config2()
+    m, k = c["x"].shape
+    n = c["w"].shape[0]
+    x = torch.from_numpy(c["x"]).to(dev, torch.bfloat16)
+    w = torch.from_numpy(c["w"]).to(dev, torch.bfloat16)
+    qf = api.fp4_quantize_pack(w, "e2m1")
+    xq, xs = api.fp8_quantize_rows(x)
+    copies = max(2, -(-ROTATE_BYTES // (m * k * 2)))
+    xcs = [x] + [x.clone() for _ in range(copies - 1)]
+    xqs = [torch.empty_like(xq) for _ in range(copies)]
+    xss = [torch.empty_like(xs) for _ in range(copies)]
+    lib = api.load_library()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def quant_rows():
+        i = it[0] % copies
+        it[0] += 1
+        st = lib.ddg_fp8_quantize_rows(xcs[i].data_ptr(), m, k, xqs[i].data_ptr(), xss[i].data_ptr(), sp)
+        if st:
+            raise api.DDGError(st, "ddg_fp8_quantize_rows")
+
+    ms_q = burst(quant_rows, args.steps)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ms_g = burst(lambda: api.w4a8_gemm(xq, xs, qf, out=y), args.steps)
+    qi = api.quantize_pack(w, 4)
+    ms_i = burst(lambda: api.dequant_gemm(x, qi, out=y), args.steps)
+    del xcs, xqs, xss
+    # accuracy on the first 1024 tokens against the float32 product of the bf16 weight
+    xr = x[:1024]
+    yref = xr.float() @ w.float().t().contiguous()
+
+    def rel(a):
+        return float(torch.linalg.norm(a.float() - yref) / torch.linalg.norm(yref))
+
+    e_w4a8 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qf, torch.float32))
+    e_int4 = rel(api.dequant_gemm(xr, qi, torch.float32))
+    flops = 2.0 * m * n * k
+    print(json.dumps({
+        "suite": "w4a8-fp4", "shape": [m, n, k], "weight_format": "e2m1", "activation_format": "e4m3",
+        "fp8_quantize_rows_us": round(ms_q * 1e3, 2),
+        "fp8_quantize_rows_GBps": round(m * k * 3 / ms_q / 1e6, 1),
+        "w4a8_gemm_us": round(ms_g * 1e3, 2), "w4a8_TFLOPs": round(flops / ms_g / 1e9, 1),
+        "w4a8_frac_of_fp8_peak": round(flops / ms_g / 1e9 / 5000.0, 4),
+        "int4_bf16_gemm_us": round(ms_i * 1e3, 2), "int4_bf16_TFLOPs": round(flops / ms_i / 1e9, 1),
+        "w4a8_rel_err_vs_f32": round(e_w4a8, 5), "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
+    }), flush=True)
+
+
 def system_info(torch):
     """GPU name, clock and ROCm build; host CPU model."""
     info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
@@ -525,6 +602,9 @@ def main():
         return
     if args.suite == "rotate":
         rotate_suite(args)
+        return
+    if args.suite == "w4a8":
+        w4a8_suite(args)
         return
 
     c = synth.config2(m=M_BIG)

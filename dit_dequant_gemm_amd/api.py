@@ -53,7 +53,12 @@ SIGNATURES = {
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
     "ddg_rpbh_rotate": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+    "ddg_fp4_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
+    "ddg_fp8_quantize_rows": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ddg_w4a8_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
 }
+
+FP4_FORMATS = {"e2m1": 0, "e3m0": 1, "e1m2": 2}
 
 ROTATE_MAX_D, ROTATE_MAX_H = 16384, 1024
 
@@ -196,6 +201,63 @@ def rpbh_rotate(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor, h: int
                                           signs.data_ptr(), h, out.data_ptr(), code[odt],
                                           _stream_ptr(x.device)), "ddg_rpbh_rotate")
     return out
+
+
+class QWeightFP4:
+    """A weight in a 4-bit floating-point format: packed (n x k/2 bytes, code
+    2i in the low nibble of byte i), scales (n x k/128 float32), fmt."""
+
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, fmt: str, n: int, k: int):
+        self.packed, self.scales, self.fmt, self.n, self.k = packed, scales, fmt, n, k
+
+
+def fp4_quantize_pack(w: torch.Tensor, fmt: str = "e2m1") -> QWeightFP4:
+    """Per-group(128) 4-bit float quantization of an (out x in) GPU weight."""
+    _require_cuda(w, "w")
+    if fmt not in FP4_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP4_FORMATS)}")
+    if w.dim() != 2 or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be a 2-D bf16 or float32 tensor")
+    w = w.contiguous()
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, max(k // GROUP, 0)), dtype=torch.float32, device=w.device)
+    _check(load_library().ddg_fp4_quantize_pack(w.data_ptr(), DDG_F32 if w.dtype == torch.float32 else DDG_BF16,
+                                                n, k, FP4_FORMATS[fmt], packed.data_ptr(), scales.data_ptr(),
+                                                _stream_ptr(w.device)), "ddg_fp4_quantize_pack")
+    return QWeightFP4(packed, scales, fmt, n, k)
+
+
+def fp8_quantize_rows(x: torch.Tensor):
+    """Per-token E4M3 codes (m x k uint8) and scales (m float32) of a bf16 X."""
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    x = x.contiguous()
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(load_library().ddg_fp8_quantize_rows(x.data_ptr(), m, k, xq.data_ptr(), xs.data_ptr(),
+                                                _stream_ptr(x.device)), "ddg_fp8_quantize_rows")
+    return xq, xs
+
+
+def w4a8_gemm(xq: torch.Tensor, xs: torch.Tensor, qw: QWeightFP4, out_dtype=torch.bfloat16,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = s_x[m] * sum_g s_w[n, g] (X_q W_q^T)_g on the FP8 x FP4 matrix cores."""
+    for t, name in ((xq, "xq"), (xs, "xs")):
+        _require_cuda(t, name)
+    if xq.dtype != torch.uint8 or xq.dim() != 2 or xq.shape[1] != qw.k or xs.shape != (xq.shape[0],):
+        raise ValueError("xq must be m x k uint8 codes with m float32 scales")
+    m = xq.shape[0]
+    y = out if out is not None else torch.empty((m, qw.n), dtype=out_dtype, device=xq.device)
+    if y.shape != (m, qw.n) or y.dtype not in (torch.bfloat16, torch.float32) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous m x n bf16 or float32 tensor")
+    _check(load_library().ddg_w4a8_gemm(xq.contiguous().data_ptr(), xs.contiguous().data_ptr(), m, qw.k,
+                                        qw.packed.data_ptr(), qw.scales.data_ptr(), FP4_FORMATS[qw.fmt],
+                                        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
+                                        _stream_ptr(xq.device)), "ddg_w4a8_gemm")
+    return y
 
 
 def dequantize(qw: QWeight) -> torch.Tensor:

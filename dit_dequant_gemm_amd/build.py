@@ -44,6 +44,7 @@ def _units():
     units.append((os.path.join(CSRC, "grouped.hip"), "grouped", []))
     units.append((os.path.join(CSRC, "pd.hip"), "pd", []))
     units.append((os.path.join(CSRC, "rotate.hip"), "rotate", []))
+    units.append((os.path.join(CSRC, "w4a8.hip"), "w4a8", []))
     units.append((os.path.join(CSRC, "api.hip"), "api", []))
     return units
 

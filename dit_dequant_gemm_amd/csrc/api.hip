@@ -349,4 +349,57 @@ int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int3
                                             out_dtype == DDG_F32, cus, stream));
 }
 
+int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt, uint8_t* packed,
+                          float* scales, hipStream_t stream) {
+  if (fmt < DDG_FP4_E2M1 || fmt > DDG_FP4_E1M2 || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
+    return DDG_ERR_ARG;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4)) return DDG_ERR_SHAPE;
+  if (n == 0) return DDG_OK;
+  if (!w || !packed || !scales) return DDG_ERR_ARG;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(ddg::launch_fp4_quantize_pack(w, w_dtype == DDG_F32, n * k / 32, fmt,
+                                                  reinterpret_cast<uint32_t*>(packed), scales, stream));
+}
+
+int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, float* xscales,
+                          hipStream_t stream) {
+  if (m < 0 || m > kMaxDim || !k_ok(k) || !mul_ok(m, k) || !mul_ok(m * k, 2)) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!x || !xq || !xscales) return DDG_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 8) || !aligned(xscales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(ddg::launch_fp8_quantize_rows(static_cast<const uint16_t*>(x), m, (int)k, xq,
+                                                  xscales, stream));
+}
+
+int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, const uint8_t* packed,
+                  const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
+  if (fmt < DDG_FP4_E2M1 || fmt > DDG_FP4_E1M2 || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))
+    return DDG_ERR_ARG;
+  if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || !mul_ok(m, n) ||
+      !mul_ok(m * n, 4) || !mul_ok(n, k))
+    return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!xq || !xscales || !packed || !wscales || !y) return DDG_ERR_ARG;
+  if (!aligned(xq, 16) || !aligned(packed, 16) || !aligned(xscales, 4) || !aligned(wscales, 4) ||
+      !aligned(y, y_dtype == DDG_F32 ? 4 : 2))
+    return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  ddg::W4A8Args a{};
+  a.xq = xq;
+  a.xscales = xscales;
+  a.packed = packed;
+  a.wscales = wscales;
+  a.y = y;
+  a.m = (int)m; a.n = (int)n; a.k = (int)k;
+  a.tiles_m = (int)((m + 255) / 256);
+  a.tiles_n = (int)((n + 255) / 256);
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return hip_status(ddg::launch_w4a8_gemm(a, fmt, stream));
+}
+
 }  // extern "C"

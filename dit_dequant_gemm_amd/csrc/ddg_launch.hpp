@@ -41,6 +41,24 @@ hipError_t launch_rpbh_rotate(const void* x, bool f32_in, int64_t n, int d, cons
                               const int8_t* signs, int h, void* out, bool f32_out, int cus,
                               hipStream_t stream);
 
+// FP4 weights x FP8 activations (formats: kFp4E2M1, kFp4E3M0, kFp4E1M2)
+constexpr int kFp4E2M1 = 0, kFp4E3M0 = 1, kFp4E1M2 = 2;
+struct W4A8Args {
+  const uint8_t* xq;        // M x K E4M3 codes
+  const float* xscales;     // M per-token scales
+  const uint8_t* packed;    // N x K/2 bytes of 4-bit codes
+  const float* wscales;     // N x K/128 group scales
+  void* y;                  // M x N
+  int m, n, k;
+  int tiles_m, tiles_n;     // 256 x 256 tiles
+  int out_bf16;
+};
+hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n_chunks, int fmt,
+                                    uint32_t* packed, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t* q, float* sx,
+                                    hipStream_t stream);
+hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, hipStream_t stream);
+
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
 

@@ -265,6 +265,62 @@ int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int*
 int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,
                     const int8_t* signs, int h, void* out, int out_dtype, hipStream_t stream);
 
+/*
+ * FP4 weights and FP8 activations (W4A8), the FP4DiT article: 4-bit
+ * floating-point weight formats in groups of 128 (§3.2.1, §4.1) and 8-bit
+ * per-token activations (§3.2.3), multiplied on the gfx950 scaled matrix
+ * instructions.
+ *
+ * Formats (sign + magnitude, subnormal when the exponent field is 0):
+ *   DDG_FP4_E2M1  bias 1: 0 .5 1 1.5 2 3 4 6
+ *   DDG_FP4_E3M0  bias 3: 0 .25 .5 1 2 4 8 16
+ *   DDG_FP4_E1M2  bias 1: 0 .25 .5 .75 1 1.25 1.5 1.75
+ * code = sign << 3 | magnitude index (a zero magnitude is always code 0).
+ */
+#define DDG_FP4_E2M1 0
+#define DDG_FP4_E3M0 1
+#define DDG_FP4_E1M2 2
+
+/*
+ * Per group of 128 weights along K: s = fl32(amax / vmax), r = fl32(w / s)
+ * (correctly rounded), code = the level nearest |r| (ties to the even code);
+ * an all-zero group gets s = 0 and codes 0.  packed: n x k/2 bytes, code 2i
+ * in the low nibble of byte i of its row; scales: n x k/128 floats.
+ *   w       device, n x k bf16 or float32 (w_dtype), finite, 16-byte aligned.
+ *   packed  device, 16-byte aligned.   scales  device, 4-byte aligned.
+ * n == 0 is a no-op.  Errors: DDG_ERR_ARG (fmt, dtype, null), DDG_ERR_SHAPE
+ * (k not a positive multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt,
+                          uint8_t* packed, float* scales, hipStream_t stream);
+
+/*
+ * Per token (row) of x (m x k bf16): s_x = fl32(amax / 448), r = fl32(x / s_x),
+ * xq = the E4M3 code of r (|r| clamped to 448, round to nearest even; E4M3:
+ * bias 7, subnormals, largest 448); an all-zero row gets s_x = 0 and zeros.
+ *   x   device, 16-byte aligned.  xq  device m x k bytes, 8-byte aligned.
+ *   xscales  device, m floats.
+ * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (k not a positive multiple of 128),
+ * DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, float* xscales,
+                          hipStream_t stream);
+
+/*
+ * Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k]
+ * (q_x, v_w the E4M3 and FP4 values), accumulated in float32 on the matrix
+ * cores; y (m x n) in bf16 (rounded once) or float32.  Inputs as written by
+ * the two calls above.  DDG_FP4_E2M1 weights enter the matrix instructions as
+ * FP4 operands; E3M0 and E1M2 (not matrix formats, every value exact in E4M3)
+ * as FP8 operands converted in registers.
+ * m == 0 is a no-op.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (k a positive
+ * multiple of 128 up to 2^20, n >= 1), DDG_ERR_ALIGN (xq, packed 16 bytes),
+ * DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
+                  const uint8_t* packed, const float* wscales, int fmt, int64_t n, void* y,
+                  int y_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

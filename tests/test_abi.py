@@ -205,3 +205,39 @@ def test_rpbh_rotate_rejects_bad_arguments(lib):
     assert call(out=FAKE + 512, xdt=0, odt=0) == E_ARG            # partial overlap
     assert call(out=FAKE, xdt=0, odt=1) == E_ARG                  # same start, other dtype
     assert call(n=0, x=None, perm=None, signs=None, out=None) == OK
+
+
+def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
+    q = lib.ddg_fp4_quantize_pack
+    assert q(FAKE, 0, 4, 128, 3, FAKE, FAKE, None) == E_ARG           # fmt
+    assert q(FAKE, 2, 4, 128, 0, FAKE, FAKE, None) == E_ARG           # dtype
+    assert q(FAKE, 0, 4, 100, 0, FAKE, FAKE, None) == E_SHAPE
+    assert q(FAKE, 0, -1, 128, 0, FAKE, FAKE, None) == E_SHAPE
+    assert q(None, 0, 4, 128, 0, FAKE, FAKE, None) == E_ARG
+    assert q(MISALIGNED, 0, 4, 128, 0, FAKE, FAKE, None) == E_ALIGN
+    assert q(FAKE, 0, 4, 128, 0, FAKE + 8, FAKE, None) == E_ALIGN
+    assert q(None, 0, 0, 128, 0, None, None, None) == OK
+    r = lib.ddg_fp8_quantize_rows
+    assert r(FAKE, 4, 100, FAKE, FAKE, None) == E_SHAPE
+    assert r(FAKE, -1, 128, FAKE, FAKE, None) == E_SHAPE
+    assert r(None, 4, 128, FAKE, FAKE, None) == E_ARG
+    assert r(MISALIGNED, 4, 128, FAKE, FAKE, None) == E_ALIGN
+    assert r(FAKE, 4, 128, FAKE + 4, FAKE, None) == E_ALIGN
+    assert r(None, 0, 128, None, None, None) == OK
+    g = lib.ddg_w4a8_gemm
+    base = [FAKE, FAKE, 4, 128, FAKE, FAKE, 0, 32, FAKE, 0, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = {"xq": 0, "xs": 1, "m": 2, "k": 3, "packed": 4, "ws": 5, "fmt": 6, "n": 7, "y": 8, "ydt": 9}
+        for key, v in kw.items():
+            a[idx[key]] = v
+        return g(*a)
+
+    assert call(fmt=5) == E_ARG and call(ydt=3) == E_ARG
+    assert call(k=130) == E_SHAPE and call(k=2 ** 20 + 128) == E_SHAPE
+    assert call(n=0) == E_SHAPE and call(m=-1) == E_SHAPE
+    assert call(xq=None) == E_ARG and call(packed=None) == E_ARG and call(y=None) == E_ARG
+    assert call(xq=MISALIGNED) == E_ALIGN and call(packed=FAKE + 8) == E_ALIGN
+    assert call(ws=FAKE + 2) == E_ALIGN and call(y=FAKE + 1) == E_ALIGN
+    assert call(m=0, xq=None, xs=None, packed=None, ws=None, y=None) == OK

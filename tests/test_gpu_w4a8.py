@@ -1,0 +1,148 @@
+"""GPU parity of the FP4-weight / FP8-activation path ([FP4] §3.2, §4.1):
+both quantizers bit for bit against the oracle, and the W4A8 product against
+the oracle's float64 sum on the oracle's own codes and scales, to the usual
+product bounds (relative Frobenius 1e-3, per-row 2e-2 of the row's largest).
+Tighter, for float32 outputs: every element within 2^-14 times the same sum
+over absolute values.  A chain of float32 additions would stay within
+(130 + G) 2^-24 of it; the matrix instruction's own accumulation measured up
+to 1.15x that, so the envelope sits well above it and far below what any
+mis-paired operand produces (about 1/sqrt(k) of the absolute sum)."""
+import numpy as np
+import pytest
+import torch
+
+from dit_dequant_gemm_amd import synth
+from oracle import fp4 as F
+from parity_util import check_product, dev_bf16, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _cuda_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _cuda_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("n,k,f32", [(16, 128, False), (33, 384, True), (64, 5120, False), (7, 1024, True)])
+def test_fp4_quantize_bit_exact(gpu_lib, fmt, n, k, f32):
+    _case(f"fp4_quantize_pack {fmt} n={n} k={k} f32={f32}")
+    rng = np.random.default_rng(n * k)
+    w = (rng.standard_t(4, size=(n, k)) * 0.02).astype(np.float32)
+    if not f32:
+        w = synth.to_bf16(w)
+    qw = gpu_lib.fp4_quantize_pack(dev_f32(w) if f32 else dev_bf16(w), fmt)
+    codes, s = F.quantize_fp4_groups(w, fmt)
+    assert np.array_equal(host(qw.packed), F.pack_fp4(codes))
+    assert np.array_equal(host(qw.scales).view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+def test_fp4_quantize_ties_zero_and_tiny_groups(gpu_lib, fmt):
+    _case(f"fp4_quantize_pack {fmt}: ties, zero, constant and tiny groups")
+    lv = F.fp4_values(fmt)
+    w = np.zeros((4, 256), dtype=np.float32)
+    # group 0 of row 0: scale 1 (amax = vmax), values on every midpoint, both signs
+    mids = (lv[1:] + lv[:-1]) / 2
+    w[0, :128] = np.resize(np.concatenate([mids, -mids, [lv[-1]]]), 128)
+    w[0, 0] = lv[-1]
+    w[1, 128:] = np.float32(0.37)                      # constant group
+    w[2, :128] = np.random.default_rng(1).normal(0, 1, 128).astype(np.float32) * np.float32(1e-41)
+    # row 3 stays zero
+    qw = gpu_lib.fp4_quantize_pack(dev_f32(w), fmt)
+    codes, s = F.quantize_fp4_groups(w, fmt)
+    assert np.array_equal(host(qw.packed), F.pack_fp4(codes))
+    assert np.array_equal(host(qw.scales).view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (64, 3072), (3, 13824)])
+def test_fp8_rows_bit_exact(gpu_lib, m, k):
+    _case(f"fp8_quantize_rows m={m} k={k}")
+    x = synth.to_bf16(np.random.default_rng(m + k).normal(0, 1, size=(m, k)))
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(x))
+    cq, cs = F.quantize_rows_e4m3(x)
+    assert np.array_equal(host(xq), cq)
+    assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
+
+
+def test_fp8_rows_ties_subnormals_and_zero_rows(gpu_lib):
+    _case("fp8_quantize_rows: ties, subnormal range, zero row")
+    lv = F.e4m3_values()
+    x = np.zeros((3, 384), dtype=np.float64)
+    mids = (lv[1:] + lv[:-1]) / 2                      # scale 1: amax = 448
+    x[0, :len(mids)] = mids
+    x[0, 200:200 + 100] = -mids[:100]
+    x[0, 383] = 448.0
+    x[1, :] = np.random.default_rng(2).normal(0, 1, 384)
+    x[1, 0] = 4096.0                                   # most of the row lands in the subnormal range
+    x = synth.to_bf16(x)
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(x))
+    cq, cs = F.quantize_rows_e4m3(x)
+    assert np.array_equal(host(xq), cq)
+    assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
+
+
+def _check_f32_product(y, xc, xs, wc, ws, ref, fmt="e2m1"):
+    absref = F.w4a8_ref(xc & 0x7F, xs, wc & 7, ws, fmt)           # the same sum over magnitudes
+    assert np.all(np.abs(y - ref) <= 2.0 ** -14 * absref + 1e-37), \
+        float(np.max(np.abs(y - ref) / (absref + 1e-37)))
+    check_product(y, ref, False, f"w4a8 f32 k={xc.shape[1]}")
+
+
+def _product_case(gpu_lib, m, n, k, seed, out_dtype, fmt="e2m1"):
+    rng = np.random.default_rng(seed)
+    w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
+    x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
+    wc, ws = F.quantize_fp4_groups(w, fmt)
+    xc, xs = F.quantize_rows_e4m3(x)
+    qw = gpu_lib.QWeightFP4(_cuda_u8(F.pack_fp4(wc)), _cuda_f32(ws), fmt, n, k)
+    y = host(gpu_lib.w4a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, out_dtype))
+    return y, F.w4a8_ref(xc, xs, wc, ws, fmt), (xc, xs, wc, ws)
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (17, 48, 384), (256, 256, 1024), (300, 272, 640),
+                                   (513, 300, 2048), (64, 1000, 128)])
+def test_w4a8_gemm(gpu_lib, m, n, k, fmt):
+    _case(f"w4a8_gemm {fmt} m={m} n={n} k={k}")
+    y, ref, codes = _product_case(gpu_lib, m, n, k, m * n + k, torch.float32, fmt)
+    _check_f32_product(y, *codes, ref, fmt)
+    yb, _, _ = _product_case(gpu_lib, m, n, k, m * n + k, torch.bfloat16, fmt)
+    check_product(yb, ref, True, f"w4a8 bf16 {fmt} m={m} n={n} k={k}")
+
+
+def test_w4a8_attention_projection_sampled(gpu_lib):
+    """The bench shape (4096 x 3072 x 3072) on sampled rows."""
+    _case("w4a8_gemm 4096 x 3072 x 3072 (sampled rows)")
+    c = synth.config2()
+    wc, ws = F.quantize_fp4_groups(c["w"], "e2m1")
+    xc, xs = F.quantize_rows_e4m3(c["x"])
+    qw = gpu_lib.QWeightFP4(_cuda_u8(F.pack_fp4(wc)), _cuda_f32(ws), "e2m1", 3072, 3072)
+    y = host(gpu_lib.w4a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, torch.float32))
+    rows = np.r_[0:32, 2040:2072, 4064:4096]
+    ref = F.w4a8_ref(xc[rows], xs[rows], wc, ws, "e2m1")
+    _check_f32_product(y[rows], xc[rows], xs[rows], wc, ws, ref)
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+def test_w4a8_chain(gpu_lib, fmt):
+    """The GPU quantizers feed the product; m = 0 is a no-op."""
+    _case(f"w4a8 chain {fmt}: GPU quantizers -> product")
+    rng = np.random.default_rng(9)
+    w = synth.to_bf16(rng.normal(0, 0.02, size=(64, 256)))
+    x = synth.to_bf16(rng.normal(0, 1, size=(40, 256)))
+    qw = gpu_lib.fp4_quantize_pack(dev_bf16(w), fmt)
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(x))
+    y = host(gpu_lib.w4a8_gemm(xq, xs, qw, torch.float32))
+    wc, wsc = F.quantize_fp4_groups(w, fmt)
+    xc, xsc = F.quantize_rows_e4m3(x)
+    ref = F.w4a8_ref(xc, xsc, wc, wsc, fmt)
+    _check_f32_product(y, xc, xsc, wc, wsc, ref, fmt)
+    assert gpu_lib.w4a8_gemm(xq[:0], xs[:0], qw, torch.float32).shape == (0, 64)
