@@ -477,6 +477,15 @@ def w4a8_suite(args):
     ms_q = burst(quant_rows, args.steps)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     ms_g = burst(lambda: api.w4a8_gemm(xq, xs, qf, out=y), args.steps)
+    qp = api.fp4_quantize_pack(w, "e2m1", pow2=True)
+    ms_p = burst(lambda: api.w4a8_gemm(xq, xs, qp, out=y), args.steps)
+    qt = api.fp4_quantize_pack(w, "e2m1", tiled=True)
+    ms_t = burst(lambda: api.w4a8_gemm(xq, xs, qt, out=y), args.steps)
+    qtp = api.fp4_quantize_pack(w, "e2m1", pow2=True, tiled=True)
+    ms_tp = burst(lambda: api.w4a8_gemm(xq, xs, qtp, out=y), args.steps)
+    ms_fmt = {f: burst(lambda: api.w4a8_gemm(xq, xs, q, out=y), args.steps)
+              for f, q in (("e3m0", api.fp4_quantize_pack(w, "e3m0", tiled=True)),
+                           ("e1m2", api.fp4_quantize_pack(w, "e1m2", tiled=True)))}
     qi = api.quantize_pack(w, 4)
     ms_i = burst(lambda: api.dequant_gemm(x, qi, out=y), args.steps)
     del xcs, xqs, xss
@@ -487,17 +496,22 @@ def w4a8_suite(args):
     def rel(a):
         return float(torch.linalg.norm(a.float() - yref) / torch.linalg.norm(yref))
 
-    e_w4a8 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qf, torch.float32))
+    e_w4a8 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qt, torch.float32))
+    e_pow2 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qtp, torch.float32))
     e_int4 = rel(api.dequant_gemm(xr, qi, torch.float32))
     flops = 2.0 * m * n * k
     print(json.dumps({
         "suite": "w4a8-fp4", "shape": [m, n, k], "weight_format": "e2m1", "activation_format": "e4m3",
         "fp8_quantize_rows_us": round(ms_q * 1e3, 2),
         "fp8_quantize_rows_GBps": round(m * k * 3 / ms_q / 1e6, 1),
-        "w4a8_gemm_us": round(ms_g * 1e3, 2), "w4a8_TFLOPs": round(flops / ms_g / 1e9, 1),
-        "w4a8_frac_of_fp8_peak": round(flops / ms_g / 1e9 / 5000.0, 4),
+        "w4a8_tiled_us": round(ms_t * 1e3, 2), "w4a8_tiled_TFLOPs": round(flops / ms_t / 1e9, 1),
+        "w4a8_tiled_frac_of_fp8_peak": round(flops / ms_t / 1e9 / 5000.0, 4),
+        "w4a8_tiled_pow2_us": round(ms_tp * 1e3, 2), "w4a8_tiled_pow2_TFLOPs": round(flops / ms_tp / 1e9, 1),
+        "w4a8_rows_us": round(ms_g * 1e3, 2), "w4a8_rows_pow2_us": round(ms_p * 1e3, 2),
+        "w4a8_e3m0_tiled_us": round(ms_fmt["e3m0"] * 1e3, 2), "w4a8_e1m2_tiled_us": round(ms_fmt["e1m2"] * 1e3, 2),
         "int4_bf16_gemm_us": round(ms_i * 1e3, 2), "int4_bf16_TFLOPs": round(flops / ms_i / 1e9, 1),
-        "w4a8_rel_err_vs_f32": round(e_w4a8, 5), "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
+        "w4a8_rel_err_vs_f32": round(e_w4a8, 5), "w4a8_pow2_rel_err_vs_f32": round(e_pow2, 5),
+        "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
     }), flush=True)
 
 

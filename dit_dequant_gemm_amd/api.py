@@ -59,6 +59,8 @@ SIGNATURES = {
 }
 
 FP4_FORMATS = {"e2m1": 0, "e3m0": 1, "e1m2": 2}
+FP4_POW2 = 0x100
+FP4_TILED = 0x200
 
 ROTATE_MAX_D, ROTATE_MAX_H = 16384, 1024
 
@@ -205,14 +207,25 @@ def rpbh_rotate(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor, h: int
 
 class QWeightFP4:
     """A weight in a 4-bit floating-point format: packed (n x k/2 bytes, code
-    2i in the low nibble of byte i), scales (n x k/128 float32), fmt."""
+    2i in the low nibble of byte i), scales (n x k/128 float32), fmt; pow2:
+    the scales are powers of two, applied by the matrix instructions; tiled:
+    codes and scales in 32-column blocks ordered for the matrix operands
+    (flat, ceil(n/32) * k/128 * 2048 bytes and * 32 floats)."""
 
-    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, fmt: str, n: int, k: int):
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, fmt: str, n: int, k: int,
+                 pow2: bool = False, tiled: bool = False):
         self.packed, self.scales, self.fmt, self.n, self.k = packed, scales, fmt, n, k
+        self.pow2, self.tiled = pow2, tiled
+
+    @property
+    def fmt_code(self) -> int:
+        return FP4_FORMATS[self.fmt] | (FP4_POW2 if self.pow2 else 0) | (FP4_TILED if self.tiled else 0)
 
 
-def fp4_quantize_pack(w: torch.Tensor, fmt: str = "e2m1") -> QWeightFP4:
-    """Per-group(128) 4-bit float quantization of an (out x in) GPU weight."""
+def fp4_quantize_pack(w: torch.Tensor, fmt: str = "e2m1", pow2: bool = False, tiled: bool = False) -> QWeightFP4:
+    """Per-group(128) 4-bit float quantization of an (out x in) GPU weight;
+    pow2 rounds each group scale up to a power of two; tiled writes the
+    storage ordered for the matrix operands."""
     _require_cuda(w, "w")
     if fmt not in FP4_FORMATS:
         raise ValueError(f"fmt must be one of {sorted(FP4_FORMATS)}")
@@ -220,12 +233,19 @@ def fp4_quantize_pack(w: torch.Tensor, fmt: str = "e2m1") -> QWeightFP4:
         raise ValueError("w must be a 2-D bf16 or float32 tensor")
     w = w.contiguous()
     n, k = w.shape
-    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((n, max(k // GROUP, 0)), dtype=torch.float32, device=w.device)
+    g = max(k // GROUP, 0)
+    if tiled:
+        nb = -(-n // 32)
+        packed = torch.empty((nb * g * 2048,), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((nb * g * 32,), dtype=torch.float32, device=w.device)
+    else:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((n, g), dtype=torch.float32, device=w.device)
+    q = QWeightFP4(packed, scales, fmt, n, k, pow2, tiled)
     _check(load_library().ddg_fp4_quantize_pack(w.data_ptr(), DDG_F32 if w.dtype == torch.float32 else DDG_BF16,
-                                                n, k, FP4_FORMATS[fmt], packed.data_ptr(), scales.data_ptr(),
+                                                n, k, q.fmt_code, packed.data_ptr(), scales.data_ptr(),
                                                 _stream_ptr(w.device)), "ddg_fp4_quantize_pack")
-    return QWeightFP4(packed, scales, fmt, n, k)
+    return q
 
 
 def fp8_quantize_rows(x: torch.Tensor):
@@ -254,7 +274,7 @@ def w4a8_gemm(xq: torch.Tensor, xs: torch.Tensor, qw: QWeightFP4, out_dtype=torc
     if y.shape != (m, qw.n) or y.dtype not in (torch.bfloat16, torch.float32) or not y.is_contiguous():
         raise ValueError("out must be a contiguous m x n bf16 or float32 tensor")
     _check(load_library().ddg_w4a8_gemm(xq.contiguous().data_ptr(), xs.contiguous().data_ptr(), m, qw.k,
-                                        qw.packed.data_ptr(), qw.scales.data_ptr(), FP4_FORMATS[qw.fmt],
+                                        qw.packed.data_ptr(), qw.scales.data_ptr(), qw.fmt_code,
                                         qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
                                         _stream_ptr(xq.device)), "ddg_w4a8_gemm")
     return y

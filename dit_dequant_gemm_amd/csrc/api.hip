@@ -349,9 +349,18 @@ int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int3
                                             out_dtype == DDG_F32, cus, stream));
 }
 
+namespace {
+// the 4-bit format in the low bits, DDG_FP4_POW2 and DDG_FP4_TILED the flags
+constexpr int kFp4Flags = DDG_FP4_POW2 | DDG_FP4_TILED;
+bool fp4_fmt_ok(int fmt) {
+  const int f = fmt & ~kFp4Flags;
+  return f >= DDG_FP4_E2M1 && f <= DDG_FP4_E1M2;
+}
+}  // namespace
+
 int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt, uint8_t* packed,
                           float* scales, hipStream_t stream) {
-  if (fmt < DDG_FP4_E2M1 || fmt > DDG_FP4_E1M2 || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
+  if (!fp4_fmt_ok(fmt) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
     return DDG_ERR_ARG;
   if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4)) return DDG_ERR_SHAPE;
   if (n == 0) return DDG_OK;
@@ -359,7 +368,8 @@ int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
   int cus = 0;
   if (int st = device_info(&cus)) return st;
-  return hip_status(ddg::launch_fp4_quantize_pack(w, w_dtype == DDG_F32, n * k / 32, fmt,
+  return hip_status(ddg::launch_fp4_quantize_pack(w, w_dtype == DDG_F32, n, (int)k, fmt & ~kFp4Flags,
+                                                  (fmt & DDG_FP4_POW2) != 0, (fmt & DDG_FP4_TILED) != 0,
                                                   reinterpret_cast<uint32_t*>(packed), scales, stream));
 }
 
@@ -377,7 +387,7 @@ int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, floa
 
 int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, const uint8_t* packed,
                   const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
-  if (fmt < DDG_FP4_E2M1 || fmt > DDG_FP4_E1M2 || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))
+  if (!fp4_fmt_ok(fmt) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))
     return DDG_ERR_ARG;
   if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || !mul_ok(m, n) ||
       !mul_ok(m * n, 4) || !mul_ok(n, k))
@@ -396,10 +406,9 @@ int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
   a.wscales = wscales;
   a.y = y;
   a.m = (int)m; a.n = (int)n; a.k = (int)k;
-  a.tiles_m = (int)((m + 255) / 256);
-  a.tiles_n = (int)((n + 255) / 256);
   a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(ddg::launch_w4a8_gemm(a, fmt, stream));
+  return hip_status(ddg::launch_w4a8_gemm(a, fmt & ~kFp4Flags, (fmt & DDG_FP4_POW2) != 0,
+                                          (fmt & DDG_FP4_TILED) != 0, stream));
 }
 
 }  // extern "C"

@@ -216,6 +216,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            kBufferFlags);
 }
 
+// Workgroup barrier that orders LDS only (waits on lgkmcnt, not vmcnt):
+// global loads and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The B dwords of one chunk through a buffer resource (dword-aligned offsets).
 template <int B>
 __device__ __forceinline__ void load_chunk_buf(rsrc_t r, uint32_t voff, uint32_t soff,

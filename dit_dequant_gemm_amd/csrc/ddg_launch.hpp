@@ -50,14 +50,17 @@ struct W4A8Args {
   const float* wscales;     // N x K/128 group scales
   void* y;                  // M x N
   int m, n, k;
-  int tiles_m, tiles_n;     // 256 x 256 tiles
+  int tiles_m, tiles_n;     // set by the launcher (its tile shape)
   int out_bf16;
 };
-hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n_chunks, int fmt,
+// pow2: group scales rounded up to powers of two, applied by the matrix
+// instructions as their block scales; tiled: codes and scales in 32-column
+// blocks, in the order the matrix operands load them
+hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n, int k, int fmt, bool pow2, bool tiled,
                                     uint32_t* packed, float* scales, hipStream_t stream);
 hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t* q, float* sx,
                                     hipStream_t stream);
-hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, hipStream_t stream);
+hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, bool pow2, bool tiled, hipStream_t stream);
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);

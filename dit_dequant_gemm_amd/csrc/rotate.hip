@@ -35,13 +35,6 @@ __device__ __forceinline__ void wait_vmcnt(int v) {
   }(std::make_integer_sequence<int, 64>{});
 }
 
-// Workgroup barrier that orders LDS only: global stores stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Value of the lane whose index differs from this lane's in bit M (M = 1, 2,
 // ..., 32).  Strides within a row of 16 lanes use DPP moves (quad_perm for 1
 // and 2; a half-row or row mirror followed by a quad_perm for 4 and 8), 16 a

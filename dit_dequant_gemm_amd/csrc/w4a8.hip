@@ -77,19 +77,40 @@ __device__ __forceinline__ uint32_t fp4_index(float a) {
   return idx;
 }
 
-// One lane per 32 consecutive weights; the four lanes of a 128-group share
-// the abs-max through a quad butterfly.  Output: 4 dwords of codes per lane
-// (code 8 j + i in bits 4 i of dword j) and one scale per group.
-template <int FMT, bool F32_IN>
+// The smallest power of two >= s (s >= 0 finite; 0 stays 0), at least 2^-126:
+// the block-scale form (E8M0) the matrix instructions apply themselves.
+__device__ __forceinline__ float pow2_at_least(float s) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, s);
+  const uint32_t e = b & 0x7F800000u;
+  uint32_t r;
+  if (b == 0u) r = 0u;
+  else if (e == 0u) r = 0x00800000u;                  // below 2^-126
+  else if ((b & 0x007FFFFFu) == 0u) r = b;            // already a power of two
+  else r = e + 0x00800000u;
+  return __builtin_bit_cast(float, r);
+}
+
+// One lane per 32 consecutive weights (chunk c: row c / cpr, chunk c % cpr
+// of the row, cpr = k / 32); the four lanes of a 128-group share the abs-max
+// through a quad butterfly.  Output: 4 dwords of codes per lane (code 8 j + i
+// in bits 4 i of dword j) and one scale per group, in row order or tiled:
+// 32-column blocks, each (block, group) 2048 bytes in the order the matrix
+// operands load them (see w4a8_gemm_kernel), the last block padded with zero
+// codes and scales (chunks n_in .. n_out - 1 read no input).
+template <int FMT, bool F32_IN, bool POW2, bool TILED>
 __global__ __launch_bounds__(256) void fp4_quantize_pack_kernel(const void* __restrict__ w,
-                                                               int64_t n_chunks,
+                                                               int64_t n_in, int64_t n_out, int cpr,
                                                                uint32_t* __restrict__ packed,
                                                                float* __restrict__ scales) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = c < n_chunks;
-  const int64_t cc = valid ? c : n_chunks - 1;               // whole quads past the end
+  const bool valid = c < n_out;
+  const bool has_src = c < n_in;
+  const int64_t cc = has_src ? c : 0;
   float v[32];
-  if constexpr (F32_IN) {
+  if (!has_src) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  } else if constexpr (F32_IN) {
     const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(w) + cc * 32);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -113,7 +134,8 @@ __global__ __launch_bounds__(256) void fp4_quantize_pack_kernel(const void* __re
   for (int i = 0; i < 32; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
   a = __builtin_fmaxf(a, __shfl_xor(a, 1));
   a = __builtin_fmaxf(a, __shfl_xor(a, 2));
-  const float s = a / Fp4Fmt<FMT>::vmax;
+  float s = a / Fp4Fmt<FMT>::vmax;
+  if constexpr (POW2) s = pow2_at_least(s);
   const bool zero = !(s != 0.0f);
   u32x4 out = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -124,8 +146,17 @@ __global__ __launch_bounds__(256) void fp4_quantize_pack_kernel(const void* __re
     out[i >> 3] |= code << (4 * (i & 7));
   }
   if (valid) {
-    reinterpret_cast<u32x4*>(packed)[c] = out;
-    if ((threadIdx.x & 3) == 0) scales[c >> 2] = zero ? 0.0f : s;
+    if constexpr (TILED) {
+      const int64_t row = c / cpr;
+      const int j = (int)(c - row * cpr);
+      const int64_t G = cpr / 4, g = j >> 2, q = j & 3;
+      const int64_t blk = (row >> 5) * G + g, lr = row & 31;
+      reinterpret_cast<u32x4*>(packed)[blk * 128 + (q >> 1) * 64 + (q & 1) * 32 + lr] = out;
+      if (q == 0) scales[blk * 32 + lr] = zero ? 0.0f : s;
+    } else {
+      reinterpret_cast<u32x4*>(packed)[c] = out;
+      if ((threadIdx.x & 3) == 0) scales[c >> 2] = zero ? 0.0f : s;
+    }
   }
 }
 
@@ -187,204 +218,350 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16e __attribute__((ext_vector_type(16)));
 
 // X tile per 128-group: 256 rows x 128 bytes of E4M3 (32 KB); row r holds
-// its 16-byte chunk c at slot c ^ (r & 7), so that the eight lanes of a
-// ds_read_b128 phase (eight consecutive rows, one chunk) hit distinct banks.
+// its 16-byte chunk c at slot c ^ xswz(r).  A ds_read_b128 serves 16 lanes
+// (256 bytes, all 64 banks) per cycle: 16 consecutive rows, one chunk, must
+// land on 16 distinct 16-byte bank groups, i.e. distinct slots among the
+// even rows and among the odd rows (a row is half a bank line); eight
+// consecutive rows get eight distinct slots as well.  The slot depends on
+// r % 32 only, so every 32-row block shares the same read addresses.
+__device__ __forceinline__ int xswz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+// Three stages: the DMA of group g + 2 runs while group g is multiplied.
 constexpr int kW8Stage = 256 * 128;
+constexpr int kW8Stages = 3;
 
-// Workgroup = 8 waves, tile 256 rows x 256 columns; wave w owns columns
-// 32w .. 32w + 31 for all 256 rows (8 row blocks of 32).  Per 128-group and
-// row block: two v_mfma_scale_f32_32x32x64_f8f6f4 (A = X as E4M3 from LDS,
-// B = the packed codes from the weight rows, unit block scales)
-// accumulate the group's partial sum, which is then scaled by the column's
-// group scale into the running fp32 accumulator.  A: lane half h holds the
-// bytes of k 32 h .. 32 h + 31 of a 64-wide step; B: see load_w below.
-template <int FMT>
+// Workgroup = 8 waves on a 256-row tile: WM waves along M, each owning RB =
+// 8 / WM row blocks of 32, times 8 / WM waves along N, each owning CB column
+// blocks of 32 (tile width TN = 32 CB 8 / WM).  Per 128-group, row block and
+// column block: two v_mfma_scale_f32_32x32x64_f8f6f4 (A = X as E4M3 from
+// LDS, B = the packed codes straight from the weight rows).  With float32
+// group scales the pair runs from zero and its partial sum is scaled by the
+// column's group scale into the running accumulator (overlapping the next
+// pair); with power-of-two scales (POW2) the instruction applies the scale
+// itself (its B block scale, E8M0 = the scale's exponent field) and
+// accumulates straight into acc.
+template <int FMT, bool POW2, bool TILED, int WM, int CB>
 __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW8Stage];
+  constexpr int RB = 8 / WM;
+  constexpr int TN = 32 * CB * (8 / WM);
+  // one array per stage, every stage index a compile-time constant: the
+  // compiler can then tell the stage being read from the one being filled
+  // and keeps the fill in flight across the barrier
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kW8Stage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kW8Stage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kW8Stage];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
+  const int wm = wave % WM, wn = wave / WM;
   int tm, tn;
   tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
   const int m0 = tm * 256;
-  const int nw0 = tn * 256;
+  const int n0 = tn * TN;
   const int K = args.k;
   const int G = K / 128;
   const uint32_t wrow = (uint32_t)K / 2;
   const int m_valid = min(256, args.m - m0);
-  const int n_valid = min(256, args.n - nw0);
+  const int n_valid = min(TN, args.n - n0);
   const rsrc_t rx = make_rsrc(args.xq + (int64_t)m0 * K, (uint32_t)m_valid * (uint32_t)K);
-  const rsrc_t rw = make_rsrc(args.packed + (int64_t)nw0 * wrow, (uint32_t)n_valid * wrow);
-  const rsrc_t rs = make_rsrc(args.wscales + (int64_t)nw0 * G, (uint32_t)n_valid * G * 4);
+  // weights and scales of this tile's columns (tiled: its whole 32-column
+  // blocks, 2048 bytes and 32 scales per block and group)
+  const int nblk = (n_valid + 31) / 32;
+  const rsrc_t rw = TILED ? make_rsrc(args.packed + (int64_t)(n0 / 32) * G * 2048, (uint32_t)(nblk * G) * 2048u)
+                          : make_rsrc(args.packed + (int64_t)n0 * wrow, (uint32_t)n_valid * wrow);
+  const rsrc_t rs = TILED ? make_rsrc(args.wscales + (int64_t)(n0 / 32) * G * 32, (uint32_t)(nblk * G) * 128u)
+                          : make_rsrc(args.wscales + (int64_t)n0 * G, (uint32_t)n_valid * G * 4);
 
   // X -> LDS: DMA i (0..3) of wave w fills 1 KB block 4w + i: rows
-  // 8 (4w + i) + lane/8, slot lane%8 holding chunk slot ^ (row & 7).
+  // 8 (4w + i) + lane/8, slot lane%8 holding chunk slot ^ xswz(row).
   uint32_t xoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * (4 * wave + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = (lane & 7) ^ xswz(r);
     xoff[i] = (uint32_t)r * (uint32_t)K + (uint32_t)c * 16;
   }
-  auto issue_x = [&](int g, int stage) __attribute__((always_inline)) {
+  auto issue_x = [&](int g, uint8_t* stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_ptr_t)(lds + stage * kW8Stage + (4 * wave + i) * 1024), 16, xoff[i],
-          (uint32_t)g * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stage + (4 * wave + i) * 1024), 16, xoff[i],
+                                               (uint32_t)g * 128, 0, 0);
   };
-  // The lane's column and its 32 codes per 64-wide step.
-  //  * E2M1 runs as an FP4 B operand: lane half h carries k 16h .. 16h + 15 of
-  //    the step in its first 16 nibbles and k 32 + 16h .. 32 + 16h + 15 in the
-  //    other 16 (the pairing with A's k 32h' + e was read off the instruction
-  //    with one-hot operands): two 8-byte pieces of the packed row, at byte
-  //    offsets 8h and 16 + 8h.
+  // B: the lane's column of each column block; per 64-wide step ks, lane
+  // half h loads the 16 bytes (codes 32 h .. 32 h + 31 of the step) at byte
+  // 32 ks + 16 h of the group's slice of the column's row, or (tiled) at
+  // 1024 ks + 512 h + 16 (lane % 32) of the (block, group) record: one load
+  // instruction reads 1 KB in one piece instead of 32 pieces of 32 bytes.
+  //  * E2M1 runs as an FP4 B operand.  The instruction pairs B's lane half
+  //    h nibbles 0-15 with A's k 16h .. 16h + 15 and nibbles 16-31 with A's
+  //    k 32 + 16h .. 32 + 16h + 15 (read off it with one-hot operands), A's
+  //    lane half h holding k 32h .. 32h + 31.  With B's half h carrying the
+  //    step's codes 32h .. 32h + 31, A's half 0 must carry the step's X at
+  //    k 0-15 and 32-47, half 1 at k 16-31 and 48-63: 16-byte chunks h, h + 2.
   //  * E3M0 and E1M2 are not matrix formats; their values are exact in E4M3,
-  //    so B is FP8, which pairs like A: lane half h takes the 16 bytes (codes
-  //    32h .. 32h + 31) at offset 16h, converted through a byte lookup.
+  //    so B is FP8 (converted in registers through a byte lookup), which
+  //    pairs like A: lane half h holds k 32 h .. 32 h + 31; A takes chunks
+  //    2h and 2h + 1.
   constexpr bool kNative = FMT == kFp4E2M1;
-  const uint32_t ncol = (uint32_t)(32 * wave + lr);
-  const uint32_t woff = ncol * wrow + (kNative ? 8u : 16u) * (uint32_t)lh;
-  const uint32_t soff = ncol * (uint32_t)G * 4;
-  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-  auto load_w = [&](int g, u32x4 (&b)[2], float& sc) __attribute__((always_inline)) {
+  uint32_t woff[CB], soff[CB];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if constexpr (kNative) {
-        const v2u lo = __builtin_amdgcn_raw_buffer_load_b64(rw, woff + 32u * ks, (uint32_t)g * 64, 0);
-        const v2u hi = __builtin_amdgcn_raw_buffer_load_b64(rw, woff + 32u * ks + 16u, (uint32_t)g * 64, 0);
-        b[ks][0] = lo.x; b[ks][1] = lo.y; b[ks][2] = hi.x; b[ks][3] = hi.y;
-      } else {
-        b[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 32u * ks,
-                                                                                (uint32_t)g * 64, 0));
-      }
+  for (int cb = 0; cb < CB; ++cb) {
+    if constexpr (TILED) {
+      const uint32_t blk = (uint32_t)(wn * CB + cb);
+      woff[cb] = blk * (uint32_t)G * 2048u + 512u * (uint32_t)lh + 16u * (uint32_t)lr;
+      soff[cb] = blk * (uint32_t)G * 128u + 4u * (uint32_t)lr;
+    } else {
+      const uint32_t ncol = (uint32_t)(wn * 32 * CB + cb * 32 + lr);
+      woff[cb] = ncol * wrow + 16u * (uint32_t)lh;
+      soff[cb] = ncol * (uint32_t)G * 4;
     }
-    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff, (uint32_t)g * 4, 0));
+  }
+  constexpr uint32_t kStepOff = TILED ? 1024u : 32u;           // ks = 1
+  constexpr uint32_t kGroupW = TILED ? 2048u : 64u, kGroupS = TILED ? 128u : 4u;
+  auto load_w = [&](int g, u32x4 (&b)[CB][2], float (&sc)[CB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        b[cb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rw, woff[cb] + kStepOff * ks, (uint32_t)g * kGroupW, 0));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff[cb], (uint32_t)g * kGroupS, 0));
   };
-  auto read_a = [&](int stage, int rb, int ks) __attribute__((always_inline)) -> i32x8 {
-    const int r = rb * 32 + lr;
-    const int c0 = 4 * ks + 2 * lh;
-    const uint8_t* base = lds + stage * kW8Stage + r * 128;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + ((c0 ^ (r & 7)) * 16));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (((c0 + 1) ^ (r & 7)) * 16));
+  auto read_a = [&](const uint8_t* stage, int rb, int ks) __attribute__((always_inline)) -> i32x8 {
+    const int r = wm * 32 * RB + rb * 32 + lr;
+    const int c0 = kNative ? 4 * ks + lh : 4 * ks + 2 * lh;
+    const int c1 = kNative ? c0 + 2 : c0 + 1;
+    const uint8_t* base = stage + r * 128;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + ((c0 ^ xswz(r)) * 16));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + ((c1 ^ xswz(r)) * 16));
     i32x8 a;
     a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
     a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
     return a;
   };
 
-  f32x16e acc[8];
+  f32x16e acc[RB][CB];
 #pragma unroll
-  for (int rb = 0; rb < 8; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.0f;
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][cb][i] = 0.0f;
   f32x16e zero16;
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
 
-  u32x4 bc[2], bn[2];
-  float sc = 0.0f, sn = 0.0f;
-  issue_x(0, 0);
-  load_w(0, bc, sc);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int stage = 0;
-  // the last group fetches itself again into the idle stage (never read), so
-  // that the loop body stays one straight block
-  for (int g = 0; g < G; ++g) {
-    const int gn = min(g + 1, G - 1);
-    issue_x(gn, stage ^ 1);
-    load_w(gn, bn, sn);
-    i32x8 b0, b1;
-    if constexpr (kNative) {
+  u32x4 bc[CB][2], bn[CB][2];
+  float sc[CB], sn[CB];
+  // Group g: fetch group g + 1's weights into (bn, sn) and group g + 2's X
+  // into the stage read in g - 1 (fill), multiply stage st with (bc, sc).
+  // The last groups fetch themselves again into idle stages (never read), so
+  // that the body stays one straight block.
+  auto step = [&](int g, const uint8_t* st, uint8_t* fill) __attribute__((always_inline)) {
+    load_w(min(g + 1, G - 1), bn, sn);
+    __builtin_amdgcn_sched_barrier(0);           // weights before X: the wait below counts on it
+    issue_x(min(g + 2, G - 1), fill);
+    i32x8 bop[CB][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b0[j] = (int)bc[0][j]; b0[j + 4] = 0;
-        b1[j] = (int)bc[1][j]; b1[j + 4] = 0;
-      }
-    } else {
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 c0 = fp4_codes_to_e4m3<FMT>(bc[0][j]);
-        const u32x2 c1 = fp4_codes_to_e4m3<FMT>(bc[1][j]);
-        b0[2 * j] = (int)c0[0]; b0[2 * j + 1] = (int)c0[1];
-        b1[2 * j] = (int)c1[0]; b1[2 * j + 1] = (int)c1[1];
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (kNative) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bop[cb][ks][j] = (int)bc[cb][ks][j];
+            bop[cb][ks][j + 4] = 0;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 c = fp4_codes_to_e4m3<FMT>(bc[cb][ks][j]);
+            bop[cb][ks][2 * j] = (int)c[0];
+            bop[cb][ks][2 * j + 1] = (int)c[1];
+          }
+        }
       }
-    }
+    int sb[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) sb[cb] = (int)((__builtin_bit_cast(uint32_t, sc[cb]) >> 23) & 0xFFu);
     constexpr int kBFmt = kNative ? 4 : 0;                // B as FP4 (E2M1) or FP8 (E4M3)
-    // row block rb: its A reads were issued one block earlier; its partial sum
-    // is scaled into acc while the next block's MFMAs run
-    i32x8 a0 = read_a(stage, 0, 0), a1 = read_a(stage, 0, 1);
+    // with power-of-two scales row block rb's A reads are issued one row
+    // block earlier; with float32 scales (16 more registers live for the
+    // rescale) at the top of the row block, behind the previous MFMAs
+    constexpr bool kPrefetchA = POW2;
+    // float32 scales: a block's partial sum is scaled into acc while the next
+    // block's MFMAs run (kPipeScale), or right after its own MFMAs where the
+    // tile leaves too few registers for the second partial sum (the other
+    // wave on the SIMD covers the wait)
+    constexpr bool kPipeScale = RB * CB <= 4;
+    i32x8 a0 = read_a(st, 0, 0), a1 = read_a(st, 0, 1);
     f32x16e tp;
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-      i32x8 n0, n1;
-      if (rb < 7) {
-        n0 = read_a(stage, rb + 1, 0);
-        n1 = read_a(stage, rb + 1, 1);
+    for (int rb = 0; rb < RB; ++rb) {
+      i32x8 n0a, n1a;
+      if (kPrefetchA && rb + 1 < RB) {
+        n0a = read_a(st, rb + 1, 0);
+        n1a = read_a(st, rb + 1, 1);
+      } else if (!kPrefetchA && rb > 0) {
+        a0 = read_a(st, rb, 0);
+        a1 = read_a(st, rb, 1);
       }
-      f32x16e t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, zero16, 0, kBFmt, 0, 127, 0, 127);
-      t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, t, 0, kBFmt, 0, 127, 0, 127);
-      if (rb > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rb - 1][i] = __builtin_fmaf(tp[i], sc, acc[rb - 1][i]);
+      for (int cb = 0; cb < CB; ++cb) {
+        if constexpr (POW2) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], acc[rb][cb], 0, kBFmt,
+                                                                        0, 127, 0, sb[cb]);
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], acc[rb][cb], 0, kBFmt,
+                                                                        0, 127, 0, sb[cb]);
+        } else {
+          f32x16e t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], zero16, 0, kBFmt,
+                                                                      0, 127, 0, 127);
+          t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], t, 0, kBFmt, 0, 127, 0, 127);
+          if constexpr (kPipeScale) {
+            if (rb * CB + cb > 0) {
+              const int p = rb * CB + cb - 1;                // the previous block, scaled now
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                acc[p / CB][p % CB][i] = __builtin_fmaf(tp[i], sc[p % CB], acc[p / CB][p % CB][i]);
+            }
+            tp = t;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[rb][cb][i] = __builtin_fmaf(t[i], sc[cb], acc[rb][cb][i]);
+          }
+        }
       }
-      tp = t;
-      if (rb < 7) {
-        a0 = n0;
-        a1 = n1;
+      if (kPrefetchA && rb + 1 < RB) {
+        a0 = n0a;
+        a1 = n1a;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!POW2 && kPipeScale) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[7][i] = __builtin_fmaf(tp[i], sc, acc[7][i]);
-    __builtin_amdgcn_s_waitcnt(0);             // the next group's X and weights have landed
-    __syncthreads();                           // ... and every wave is done with this stage
-    bc[0] = bn[0];
-    bc[1] = bn[1];
-    sc = sn;
-    stage ^= 1;
+      for (int i = 0; i < 16; ++i)
+        acc[RB - 1][CB - 1][i] = __builtin_fmaf(tp[i], sc[CB - 1], acc[RB - 1][CB - 1][i]);
+    }
+    // everything but this wave's four X DMAs of group g + 2 has landed: the
+    // next group's weights and (for every wave, after the barrier) its X
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+    // ... and every wave is done with stage st.  A plain barrier: a release
+    // fence would also wait for the X DMAs just issued.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      bc[cb][0] = bn[cb][0];
+      bc[cb][1] = bn[cb][1];
+      sc[cb] = sn[cb];
+    }
+  };
+
+  issue_x(0, lds0);
+  issue_x(min(1, G - 1), lds1);
+  load_w(0, bc, sc);
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  // three groups per trip: group g reads stage g % 3
+  int g = 0;
+  for (; g + 2 < G; g += 3) {
+    step(g, lds0, lds2);
+    step(g + 1, lds1, lds0);
+    step(g + 2, lds2, lds1);
   }
+  if (g < G) step(g, lds0, lds2);
+  if (g + 1 < G) step(g + 1, lds1, lds0);
+  __builtin_amdgcn_s_waitcnt(0);                 // the idle stages' DMAs, before the workgroup ends
 
   // Epilogue: lane holds rows 8(r/4) + 4h + r%4 of column lane%32, r = 0..15.
-  const int col = nw0 + 32 * wave + lr;
-  if (col < args.n) {
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
+    float xs[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < args.m) {
-          const float v = acc[rb][r] * args.xscales[row];
-          if (args.out_bf16)
-            static_cast<__bf16*>(args.y)[(int64_t)row * args.n + col] = (__bf16)v;
-          else
-            static_cast<float*>(args.y)[(int64_t)row * args.n + col] = v;
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 32 * RB + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      xs[r] = row < args.m ? args.xscales[row] : 0.0f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = n0 + wn * 32 * CB + cb * 32 + lr;
+      if (col < args.n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 32 * RB + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (row < args.m) {
+            const float v = acc[rb][cb][r] * xs[r];
+            if (args.out_bf16)
+              static_cast<__bf16*>(args.y)[(int64_t)row * args.n + col] = (__bf16)v;
+            else
+              static_cast<float*>(args.y)[(int64_t)row * args.n + col] = v;
+          }
         }
       }
     }
   }
 }
 
-template <int FMT>
-hipError_t launch_fp4_quant(const void* w, bool f32_in, int64_t n_chunks, uint32_t* packed,
-                            float* scales, hipStream_t stream) {
-  const dim3 grid((unsigned)((n_chunks + 255) / 256)), block(256);
-  if (f32_in)
-    fp4_quantize_pack_kernel<FMT, true><<<grid, block, 0, stream>>>(w, n_chunks, packed, scales);
+template <int FMT, bool F32_IN, bool POW2>
+hipError_t launch_fp4_quant3(int64_t n, int k, bool tiled, const void* w, uint32_t* packed, float* scales,
+                             hipStream_t stream) {
+  const int cpr = k / 32;
+  const int64_t n_in = n * cpr;
+  const int64_t n_out = tiled ? (n + 31) / 32 * 32 * cpr : n_in;
+  const dim3 grid((unsigned)((n_out + 255) / 256)), block(256);
+  if (tiled)
+    fp4_quantize_pack_kernel<FMT, F32_IN, POW2, true><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
   else
-    fp4_quantize_pack_kernel<FMT, false><<<grid, block, 0, stream>>>(w, n_chunks, packed, scales);
+    fp4_quantize_pack_kernel<FMT, F32_IN, POW2, false><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fp4_quant(const void* w, bool f32_in, bool pow2, bool tiled, int64_t n, int k, uint32_t* packed,
+                            float* scales, hipStream_t stream) {
+  if (f32_in)
+    return pow2 ? launch_fp4_quant3<FMT, true, true>(n, k, tiled, w, packed, scales, stream)
+                : launch_fp4_quant3<FMT, true, false>(n, k, tiled, w, packed, scales, stream);
+  return pow2 ? launch_fp4_quant3<FMT, false, true>(n, k, tiled, w, packed, scales, stream)
+              : launch_fp4_quant3<FMT, false, false>(n, k, tiled, w, packed, scales, stream);
+}
+
+template <int FMT, bool POW2, bool TILED, int WM, int CB>
+hipError_t launch_w4a8_cfg(W4A8Args a, hipStream_t stream) {
+  constexpr int TN = 32 * CB * (8 / WM);
+  a.tiles_m = (a.m + 255) / 256;
+  a.tiles_n = (a.n + TN - 1) / TN;
+  w4a8_gemm_kernel<FMT, POW2, TILED, WM, CB><<<dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Tile shapes (measured at 4096 x 3072 x 3072): E2M1 on tiled storage runs
+// 4 waves along M x 2 along N, 64 rows x 96 columns each (256 x 192 tiles:
+// a quarter of the LDS reads, and 256 tiles at N = 3072 fill 256 CUs); row
+// storage (32 scattered pieces per operand load) and the byte-lookup formats
+// (whose conversion would be repeated by every wave along M) keep one wave
+// per 32 columns of all 256 rows.
+template <int FMT, bool POW2>
+hipError_t launch_w4a8(const W4A8Args& a, bool tiled, hipStream_t stream) {
+  if constexpr (FMT == kFp4E2M1) {
+    if (tiled) return launch_w4a8_cfg<FMT, POW2, true, 4, 3>(a, stream);
+  }
+  return tiled ? launch_w4a8_cfg<FMT, POW2, true, 1, 1>(a, stream) : launch_w4a8_cfg<FMT, POW2, false, 1, 1>(a, stream);
+}
+
+template <int FMT>
+hipError_t launch_w4a8(const W4A8Args& a, bool pow2, bool tiled, hipStream_t stream) {
+  return pow2 ? launch_w4a8<FMT, true>(a, tiled, stream) : launch_w4a8<FMT, false>(a, tiled, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n_chunks, int fmt,
+hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n, int k, int fmt, bool pow2, bool tiled,
                                     uint32_t* packed, float* scales, hipStream_t stream) {
   switch (fmt) {
-    case kFp4E2M1: return launch_fp4_quant<kFp4E2M1>(w, f32_in, n_chunks, packed, scales, stream);
-    case kFp4E3M0: return launch_fp4_quant<kFp4E3M0>(w, f32_in, n_chunks, packed, scales, stream);
-    case kFp4E1M2: return launch_fp4_quant<kFp4E1M2>(w, f32_in, n_chunks, packed, scales, stream);
+    case kFp4E2M1: return launch_fp4_quant<kFp4E2M1>(w, f32_in, pow2, tiled, n, k, packed, scales, stream);
+    case kFp4E3M0: return launch_fp4_quant<kFp4E3M0>(w, f32_in, pow2, tiled, n, k, packed, scales, stream);
+    case kFp4E1M2: return launch_fp4_quant<kFp4E1M2>(w, f32_in, pow2, tiled, n, k, packed, scales, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -396,12 +573,11 @@ hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t
   return hipGetLastError();
 }
 
-hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
+hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, bool pow2, bool tiled, hipStream_t stream) {
   switch (fmt) {
-    case kFp4E2M1: w4a8_gemm_kernel<kFp4E2M1><<<grid, block, 0, stream>>>(a); return hipGetLastError();
-    case kFp4E3M0: w4a8_gemm_kernel<kFp4E3M0><<<grid, block, 0, stream>>>(a); return hipGetLastError();
-    case kFp4E1M2: w4a8_gemm_kernel<kFp4E1M2><<<grid, block, 0, stream>>>(a); return hipGetLastError();
+    case kFp4E2M1: return launch_w4a8<kFp4E2M1>(a, pow2, tiled, stream);
+    case kFp4E3M0: return launch_w4a8<kFp4E3M0>(a, pow2, tiled, stream);
+    case kFp4E1M2: return launch_w4a8<kFp4E1M2>(a, pow2, tiled, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -280,12 +280,36 @@ int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int3
 #define DDG_FP4_E2M1 0
 #define DDG_FP4_E3M0 1
 #define DDG_FP4_E1M2 2
+/*
+ * OR-ed into fmt: power-of-two group scales, the block-scale form (E8M0) the
+ * gfx950 matrix instructions apply themselves.  The quantizer rounds each
+ * group's s up to the next power of two (at least 2^-126; s = 0 stays 0) and
+ * quantizes with it; the product then passes each scale's exponent field to
+ * the instruction instead of rescaling partial sums.  Scales stay float32 in
+ * memory.  The product reads only the exponent field of each scale in this
+ * mode, so its wscales must come from the quantizer in the same mode.
+ * Weights beyond 2^127 times the format's largest value are not supported.
+ */
+#define DDG_FP4_POW2 0x100
+/*
+ * OR-ed into fmt: tiled storage, the same codes and scales reordered for the
+ * matrix instructions so that each operand load reads one contiguous 1 KB
+ * piece.  Columns go in blocks of 32, the last padded with zero codes and
+ * zero scales; blocks are stored in (block, group) order, 2048 bytes each:
+ * byte 1024 s + 512 h + 16 j + t of record (b, g) is byte 32 s + 16 h + t
+ * of column 32 b + j's 64-byte slice of group g in the row storage.  Scales:
+ * 32 floats per record, column 32 b + j at position j.  Sizes:
+ * ceil(n/32) * (k/128) * 2048 bytes and ceil(n/32) * (k/128) * 32 floats.
+ * The product must be told the storage its weights were written in.
+ */
+#define DDG_FP4_TILED 0x200
 
 /*
  * Per group of 128 weights along K: s = fl32(amax / vmax), r = fl32(w / s)
  * (correctly rounded), code = the level nearest |r| (ties to the even code);
  * an all-zero group gets s = 0 and codes 0.  packed: n x k/2 bytes, code 2i
- * in the low nibble of byte i of its row; scales: n x k/128 floats.
+ * in the low nibble of byte i of its row; scales: n x k/128 floats (or the
+ * tiled storage with DDG_FP4_TILED).
  *   w       device, n x k bf16 or float32 (w_dtype), finite, 16-byte aligned.
  *   packed  device, 16-byte aligned.   scales  device, 4-byte aligned.
  * n == 0 is a no-op.  Errors: DDG_ERR_ARG (fmt, dtype, null), DDG_ERR_SHAPE

@@ -32,6 +32,17 @@ R21  Packing: two codes per byte, the even index in the low nibble (the operand
      order of the gfx950 FP4 matrix instructions), rows of k/2 bytes.
 R22  The product: Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k],
      q_x and v_w the exact E4M3 and FP4 values.
+R24  Tiled storage (an option of this implementation, not of the article): the
+     same codes and scales, reordered for the matrix instructions.  Columns
+     are taken in blocks of 32 (the last padded with zero codes and zero
+     scales); block b, group g is 2048 contiguous bytes: byte 1024 s + 512 h +
+     16 j + t holds byte 32 s + 16 h + t of column 32 b + j's 64-byte slice of
+     group g (rows of R21).  Blocks are ordered (b, g).  Scales: 32 floats per
+     (b, g), column 32 b + j at position j.
+R23  Power-of-two scale mode (the scale format the matrix instructions apply
+     themselves, E8M0): s = the smallest power of two >= fl32(amax / vmax), and at
+     least 2^-126; then as R19 with that s.  Every code stays within the format's
+     range, at the cost of up to one bit of it.
 """
 from __future__ import annotations
 
@@ -39,7 +50,7 @@ import numpy as np
 
 __all__ = ["FP4_FORMATS", "fp4_values", "minifloat_value", "quantize_fp4_groups", "pack_fp4",
            "unpack_fp4", "fp4_decode", "e4m3_values", "e4m3_round", "e4m3_decode",
-           "quantize_rows_e4m3", "w4a8_ref"]
+           "quantize_rows_e4m3", "w4a8_ref", "tile_fp4", "untile_fp4"]
 
 FP4_FORMATS = {"e2m1": (2, 1, 1), "e3m0": (3, 0, 3), "e1m2": (1, 2, 1)}   # ebits, mbits, bias
 GROUP = 128
@@ -80,8 +91,16 @@ def _nearest_index(mag_r, levels):
     return out
 
 
-def quantize_fp4_groups(w, fmt: str):
-    """(codes n x k uint8 in 0..15, scales n x k/128 float32) per R19."""
+def _pow2_at_least(s):
+    """Smallest power of two >= s (float32 s > 0), at least 2^-126 (R23)."""
+    s = np.asarray(s, dtype=np.float32)
+    m, e = np.frexp(s.astype(np.float64))            # s = m 2^e, m in [0.5, 1)
+    p = np.where(m == 0.5, np.ldexp(1.0, e - 1), np.ldexp(1.0, e))
+    return np.maximum(p, 2.0 ** -126).astype(np.float32)
+
+
+def quantize_fp4_groups(w, fmt: str, pow2: bool = False):
+    """(codes n x k uint8 in 0..15, scales n x k/128 float32) per R19 (R23 with pow2)."""
     w = np.asarray(w, dtype=np.float32)
     n, k = w.shape
     levels = fp4_values(fmt)
@@ -90,6 +109,8 @@ def quantize_fp4_groups(w, fmt: str):
     amax = np.max(np.abs(g), axis=2)
     with np.errstate(divide="ignore", invalid="ignore"):
         s = (amax / vmax).astype(np.float32)
+        if pow2:
+            s = np.where(s > 0, _pow2_at_least(np.where(s > 0, s, 1.0)), np.float32(0)).astype(np.float32)
         r = (g / s[:, :, None]).astype(np.float32)
     zero = s[:, :, None] == 0
     r = np.where(zero, np.float32(0), r)
@@ -110,6 +131,32 @@ def unpack_fp4(packed) -> np.ndarray:
     out[:, 0::2] = p & 15
     out[:, 1::2] = p >> 4
     return out
+
+
+def tile_fp4(packed, scales):
+    """Row storage (n x k/2 bytes, n x k/128 scales) -> tiled storage (R24):
+    (flat bytes of ceil(n/32) * G * 2048, flat floats of ceil(n/32) * G * 32)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.float32)
+    n, kb = p.shape
+    g = kb // 64
+    nb = -(-n // 32)
+    pp = np.zeros((nb * 32, kb), dtype=np.uint8)
+    pp[:n] = p
+    ss = np.zeros((nb * 32, g), dtype=np.float32)
+    ss[:n] = sc
+    # axes of a row slice: block b, column j, group g, step s, half h, byte t
+    t = pp.reshape(nb, 32, g, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5)
+    return t.reshape(-1).copy(), ss.reshape(nb, 32, g).transpose(0, 2, 1).reshape(-1).copy()
+
+
+def untile_fp4(tiled, tscales, n: int, k: int):
+    """Inverse of tile_fp4 (padding dropped)."""
+    g = k // GROUP
+    nb = -(-n // 32)
+    t = np.asarray(tiled, dtype=np.uint8).reshape(nb, g, 2, 2, 32, 16).transpose(0, 4, 1, 2, 3, 5)
+    s = np.asarray(tscales, dtype=np.float32).reshape(nb, g, 32).transpose(0, 2, 1)
+    return t.reshape(nb * 32, k // 2)[:n].copy(), s.reshape(nb * 32, g)[:n].copy()
 
 
 def e4m3_values() -> np.ndarray:

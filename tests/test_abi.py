@@ -210,6 +210,10 @@ def test_rpbh_rotate_rejects_bad_arguments(lib):
 def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     q = lib.ddg_fp4_quantize_pack
     assert q(FAKE, 0, 4, 128, 3, FAKE, FAKE, None) == E_ARG           # fmt
+    assert q(FAKE, 0, 4, 128, 0x103, FAKE, FAKE, None) == E_ARG       # power-of-two flag, bad format
+    assert q(FAKE, 0, 4, 128, 0x400, FAKE, FAKE, None) == E_ARG       # unknown flag
+    assert q(FAKE, 0, 4, 128, 0x303, FAKE, FAKE, None) == E_ARG       # both flags, bad format
+    assert q(None, 0, 0, 128, 0x302, None, None, None) == OK          # both flags accepted
     assert q(FAKE, 2, 4, 128, 0, FAKE, FAKE, None) == E_ARG           # dtype
     assert q(FAKE, 0, 4, 100, 0, FAKE, FAKE, None) == E_SHAPE
     assert q(FAKE, 0, -1, 128, 0, FAKE, FAKE, None) == E_SHAPE
@@ -235,6 +239,8 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
         return g(*a)
 
     assert call(fmt=5) == E_ARG and call(ydt=3) == E_ARG
+    assert call(fmt=0x103) == E_ARG and call(fmt=0x400) == E_ARG and call(fmt=0x203) == E_ARG
+    assert call(fmt=0x101, m=0, xq=None) == OK and call(fmt=0x302, m=0, xq=None) == OK
     assert call(k=130) == E_SHAPE and call(k=2 ** 20 + 128) == E_SHAPE
     assert call(n=0) == E_SHAPE and call(m=-1) == E_SHAPE
     assert call(xq=None) == E_ARG and call(packed=None) == E_ARG and call(y=None) == E_ARG

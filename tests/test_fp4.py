@@ -118,3 +118,61 @@ def test_w4a8_reference_against_loops():
             for kk in range(k):
                 acc += float(sw[j, kk // 128]) * qx[i, kk] * vw[j, kk]
             assert abs(y[i, j] - float(sx[i]) * acc) <= 1e-9 * max(1.0, abs(y[i, j]))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+def test_power_of_two_scales(fmt):
+    rng = np.random.default_rng(7)
+    w = (rng.normal(0, 0.02, size=(6, 384))).astype(np.float32)
+    w[1, :128] = 0.0
+    w[2, 128:256] *= np.float32(1e-40)                        # group scale below 2^-126
+    codes, s = F.quantize_fp4_groups(w, fmt, pow2=True)
+    _, s_plain = F.quantize_fp4_groups(w, fmt)
+    nz = s > 0
+    m, _ = np.frexp(s[nz].astype(np.float64))
+    assert np.all(m == 0.5)                                    # powers of two
+    assert np.all(s[nz] >= s_plain[nz]) and np.all(s[nz] < 2 * s_plain[nz] + 2.0 ** -126)
+    assert s[1, 0] == 0 and np.all(codes[1, :128] == 0)
+    assert s[2, 1] == np.float32(2.0 ** -126)
+    lv = F.fp4_values(fmt)
+    q = (w.reshape(6, 3, 128) / np.where(s > 0, s, 1)[:, :, None]).astype(np.float32)
+    assert np.all(np.abs(q) <= lv[-1])                         # nothing saturates
+    want = np.minimum(_brute_nearest(np.minimum(np.abs(q.reshape(-1)), lv[-1]), lv), 7).reshape(6, 384)
+    assert np.array_equal(np.where(np.repeat(s, 128, axis=1) > 0, codes & 7, 0), np.where(np.repeat(s, 128, axis=1) > 0, want, 0))
+    # exactly a power of two already: kept
+    assert np.all(F._pow2_at_least(np.float32([0.25, 1.0, 3.0, 2.0 ** -130])) == np.float32([0.25, 1.0, 4.0, 2.0 ** -126]))
+
+
+def test_tiled_layout_positions_by_hand():
+    """R24 positions worked out by hand for n = 40 (two blocks, the second
+    padded), k = 256 (G = 2)."""
+    n, k = 40, 256
+    rng = np.random.default_rng(3)
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = rng.random((n, 2), dtype=np.float32) + 1
+    t, ts = F.tile_fp4(packed, scales)
+    assert t.shape == (2 * 2 * 2048,) and ts.shape == (2 * 2 * 32,)
+    # column 33 (block 1, j = 1), group 1, row byte 64 + 32*1 + 16*0 + 5:
+    # (1*2 + 1)*2048 + 1*1024 + 0*512 + 1*16 + 5 = 7189
+    assert t[7189] == packed[33, 64 + 32 + 5]
+    # column 0, group 0, row byte 16 + 15 (s = 0, h = 1, t = 15): 512 + 15
+    assert t[527] == packed[0, 31]
+    # column 31, group 1, row byte 64 + 32 + 16 + 0 (s = 1, h = 1): 2048 + 1024 + 512 + 31*16
+    assert t[2048 + 1024 + 512 + 496] == packed[31, 112]
+    # padded column 45 of block 1 reads zero everywhere
+    assert t[2 * 2048 + 13 * 16: 2 * 2048 + 14 * 16].sum() == 0
+    assert ts[(1 * 2 + 1) * 32 + 1] == scales[33, 1] and ts[(1 * 2 + 0) * 32 + 13] == 0
+    assert ts[0 * 32 + 31] == scales[31, 0]
+
+
+def test_tiled_layout_is_a_permutation_and_inverts():
+    n, k = 70, 384
+    # every byte value distinct per position: tag each byte by its position
+    packed = (np.arange(n * k // 2, dtype=np.int64).reshape(n, k // 2) % 251 + 1).astype(np.uint8)
+    scales = np.arange(n * 3, dtype=np.float32).reshape(n, 3) + 1
+    t, ts = F.tile_fp4(packed, scales)
+    back, bs = F.untile_fp4(t, ts, n, k)
+    assert np.array_equal(back, packed) and np.array_equal(bs, scales)
+    # multiset of bytes kept, the rest zeros (padding)
+    assert np.array_equal(np.sort(t[t > 0]), np.sort(packed.reshape(-1)))
+    assert np.count_nonzero(t) == packed.size and np.count_nonzero(ts) == scales.size

@@ -146,3 +146,107 @@ def test_w4a8_chain(gpu_lib, fmt):
     ref = F.w4a8_ref(xc, xsc, wc, wsc, fmt)
     _check_f32_product(y, xc, xsc, wc, wsc, ref, fmt)
     assert gpu_lib.w4a8_gemm(xq[:0], xs[:0], qw, torch.float32).shape == (0, 64)
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("n,k,f32", [(16, 128, False), (33, 384, True), (64, 5120, False)])
+def test_fp4_quantize_pow2_bit_exact(gpu_lib, fmt, n, k, f32):
+    _case(f"fp4_quantize_pack {fmt} power-of-two scales n={n} k={k} f32={f32}")
+    rng = np.random.default_rng(n * k + 1)
+    w = (rng.standard_t(4, size=(n, k)) * 0.02).astype(np.float32)
+    w[0, :128] = 0.0
+    w[-1, -128:] *= np.float32(1e-39)                    # scale below 2^-126
+    if not f32:
+        w = synth.to_bf16(w)
+    qw = gpu_lib.fp4_quantize_pack(dev_f32(w) if f32 else dev_bf16(w), fmt, pow2=True)
+    codes, s = F.quantize_fp4_groups(w, fmt, pow2=True)
+    assert qw.pow2
+    assert np.array_equal(host(qw.packed), F.pack_fp4(codes))
+    assert np.array_equal(host(qw.scales).view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (300, 272, 640), (513, 300, 2048)])
+def test_w4a8_gemm_pow2(gpu_lib, m, n, k, fmt):
+    """Power-of-two group scales, applied by the matrix instruction."""
+    _case(f"w4a8_gemm power-of-two scales {fmt} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m + n + k)
+    w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
+    w[1, :128] = 0.0                                     # a zero group: scale 0
+    x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
+    wc, ws = F.quantize_fp4_groups(w, fmt, pow2=True)
+    xc, xs = F.quantize_rows_e4m3(x)
+    ref = F.w4a8_ref(xc, xs, wc, ws, fmt)
+    for dt in (torch.float32, torch.bfloat16):
+        qw = gpu_lib.QWeightFP4(_cuda_u8(F.pack_fp4(wc)), _cuda_f32(ws), fmt, n, k, pow2=True)
+        y = host(gpu_lib.w4a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, dt))
+        if dt == torch.float32:
+            _check_f32_product(y, xc, xs, wc, ws, ref, fmt)
+        else:
+            check_product(y, ref, True, f"w4a8 pow2 bf16 {fmt} m={m} n={n} k={k}")
+
+
+def test_w4a8_pow2_chain_attention_projection_sampled(gpu_lib):
+    """GPU quantizers (power-of-two scales) feeding the product at 4096 x 3072 x 3072."""
+    _case("w4a8 pow2 chain 4096 x 3072 x 3072 (sampled rows)")
+    c = synth.config2()
+    qw = gpu_lib.fp4_quantize_pack(dev_bf16(c["w"]), "e2m1", pow2=True)
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(c["x"]))
+    y = host(gpu_lib.w4a8_gemm(xq, xs, qw, torch.float32))
+    wc, ws = F.quantize_fp4_groups(c["w"], "e2m1", pow2=True)
+    rows = np.r_[0:32, 4064:4096]
+    xc, xsc = F.quantize_rows_e4m3(c["x"][rows])
+    assert np.array_equal(host(qw.scales).view(np.uint32), ws.view(np.uint32))
+    _check_f32_product(y[rows], xc, xsc, wc, ws, F.w4a8_ref(xc, xsc, wc, ws, "e2m1"))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("n,k,f32,pow2", [(16, 128, False, False), (33, 384, True, True), (100, 5120, False, False),
+                                          (64, 256, True, False), (7, 1024, False, True)])
+def test_fp4_quantize_tiled_bit_exact(gpu_lib, fmt, n, k, f32, pow2):
+    _case(f"fp4_quantize_pack tiled {fmt} n={n} k={k} f32={f32} pow2={pow2}")
+    rng = np.random.default_rng(n * k + 2)
+    w = (rng.standard_t(4, size=(n, k)) * 0.02).astype(np.float32)
+    w[n // 2, :128] = 0.0
+    if not f32:
+        w = synth.to_bf16(w)
+    qw = gpu_lib.fp4_quantize_pack(dev_f32(w) if f32 else dev_bf16(w), fmt, pow2=pow2, tiled=True)
+    codes, s = F.quantize_fp4_groups(w, fmt, pow2=pow2)
+    t, ts = F.tile_fp4(F.pack_fp4(codes), s)
+    assert qw.tiled and qw.packed.shape == t.shape and qw.scales.shape == ts.shape
+    assert np.array_equal(host(qw.packed), t)                  # padding columns included: zero codes
+    assert np.array_equal(host(qw.scales).view(np.uint32), ts.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (300, 272, 640), (513, 300, 2048), (64, 1000, 128),
+                                   (257, 33, 384)])
+def test_w4a8_gemm_tiled(gpu_lib, m, n, k, fmt, pow2):
+    """The product on tiled weights (oracle codes, tiled by the oracle)."""
+    _case(f"w4a8_gemm tiled {fmt} pow2={pow2} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 7 + n + k)
+    w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
+    x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
+    wc, ws = F.quantize_fp4_groups(w, fmt, pow2=pow2)
+    xc, xs = F.quantize_rows_e4m3(x)
+    t, ts = F.tile_fp4(F.pack_fp4(wc), ws)
+    qw = gpu_lib.QWeightFP4(_cuda_u8(t), _cuda_f32(ts), fmt, n, k, pow2=pow2, tiled=True)
+    ref = F.w4a8_ref(xc, xs, wc, ws, fmt)
+    y = host(gpu_lib.w4a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, torch.float32))
+    _check_f32_product(y, xc, xs, wc, ws, ref, fmt)
+    yb = host(gpu_lib.w4a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, torch.bfloat16))
+    check_product(yb, ref, True, f"w4a8 tiled bf16 {fmt} m={m} n={n} k={k}")
+
+
+def test_w4a8_tiled_chain_attention_projection_sampled(gpu_lib):
+    """GPU quantizers (tiled, float32 scales) feeding the product at 4096 x 3072 x 3072."""
+    _case("w4a8 tiled chain 4096 x 3072 x 3072 (sampled rows)")
+    c = synth.config2()
+    qw = gpu_lib.fp4_quantize_pack(dev_bf16(c["w"]), "e2m1", tiled=True)
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(c["x"]))
+    y = host(gpu_lib.w4a8_gemm(xq, xs, qw, torch.float32))
+    wc, ws = F.quantize_fp4_groups(c["w"], "e2m1")
+    rows = np.r_[0:32, 2048:2080, 4064:4096]
+    xc, xsc = F.quantize_rows_e4m3(c["x"][rows])
+    _check_f32_product(y[rows], xc, xsc, wc, ws, F.w4a8_ref(xc, xsc, wc, ws, "e2m1"))
