@@ -11,7 +11,7 @@ Source: [FP4] the FP4DiT article (aijishu.com).
     first linear of the pointwise feed-forward network) and E1M2; weight groups
     of 128.
   - §3.2.3 / §4.1: per-token online min-max activation quantization to 8 bits
-    (W4A8).
+    (W4A8) and 6 bits (W4A6); §3.3: FP6 saves memory over FP8.
 
 Readings where the article is silent (each is repeated in the design doc):
 
@@ -39,6 +39,16 @@ R24  Tiled storage (an option of this implementation, not of the article): the
      16 j + t holds byte 32 s + 16 h + t of column 32 b + j's 64-byte slice of
      group g (rows of R21).  Blocks are ordered (b, g).  Scales: 32 floats per
      (b, g), column 32 b + j at position j.
+R25  The 6-bit activations (W4A6) are FP6, E2M3 (bias 1, largest 7.5) or E3M2
+     (bias 3, largest 28), sign + magnitude, subnormal when the exponent field
+     is 0, no infinities; per token as R20 with 7.5 or 28 in place of 448.
+R26  FP6 storage (an option of this implementation: the article fixes none):
+     rows padded to a multiple of 32 with zero codes; for row block b (32
+     rows), group g, 64-wide step s, half h (k = 128 g + 64 s + 32 h + j, j <
+     32) the 32 codes form a 192-bit little-endian string, code j at bits 6 j;
+     its 8-byte piece u (bits 64 u ..) of row 32 b + r sits at byte
+     ((s * 2 + h) * 3 + u) * 256 + 8 r of record (b, g), 3072 bytes, records
+     ordered (b, g).
 R23  Power-of-two scale mode (the scale format the matrix instructions apply
      themselves, E8M0): s = the smallest power of two >= fl32(amax / vmax), and at
      least 2^-126; then as R19 with that s.  Every code stays within the format's
@@ -50,9 +60,11 @@ import numpy as np
 
 __all__ = ["FP4_FORMATS", "fp4_values", "minifloat_value", "quantize_fp4_groups", "pack_fp4",
            "unpack_fp4", "fp4_decode", "e4m3_values", "e4m3_round", "e4m3_decode",
-           "quantize_rows_e4m3", "w4a8_ref", "tile_fp4", "untile_fp4"]
+           "quantize_rows_e4m3", "w4a8_ref", "tile_fp4", "untile_fp4", "FP6_FORMATS", "fp6_values",
+           "quantize_rows_fp6", "fp6_decode", "pack_fp6_tiled", "unpack_fp6_tiled", "w4a6_ref"]
 
 FP4_FORMATS = {"e2m1": (2, 1, 1), "e3m0": (3, 0, 3), "e1m2": (1, 2, 1)}   # ebits, mbits, bias
+FP6_FORMATS = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}
 GROUP = 128
 E4M3_MAX = 448.0
 
@@ -196,6 +208,77 @@ def w4a8_ref(xcodes, xscales, wcodes, wscales, fmt: str) -> np.ndarray:
     m, k = qx.shape
     n = vw.shape[0]
     y = np.zeros((m, n), dtype=np.float64)
+    sw = np.asarray(wscales, dtype=np.float64)
+    for g in range(k // GROUP):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        y += (qx[:, sl] @ vw[:, sl].T) * sw[None, :, g]
+    return y * np.asarray(xscales, dtype=np.float64)[:, None]
+
+
+def fp6_values(fmt: str) -> np.ndarray:
+    """The 32 magnitudes of a 6-bit format, by magnitude index (R25)."""
+    eb, mb, bias = FP6_FORMATS[fmt]
+    return np.array([minifloat_value(i, eb, mb, bias) for i in range(32)], dtype=np.float64)
+
+
+def fp6_decode(codes, fmt: str) -> np.ndarray:
+    c = np.asarray(codes)
+    mag = fp6_values(fmt)[c & 31]
+    return np.where(c & 32, -mag, mag)
+
+
+def quantize_rows_fp6(x, fmt: str):
+    """(codes m x k uint8 in 0..63, scales m float32) per token (R25)."""
+    x = np.asarray(x, dtype=np.float32)
+    levels = fp6_values(fmt)
+    vmax = np.float32(levels[-1])
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / vmax).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = (x / s[:, None]).astype(np.float32)
+    r = np.where(s[:, None] == 0, np.float32(0), r)
+    idx = _nearest_index(np.minimum(np.abs(r), vmax), levels)
+    return np.where((idx > 0) & (r < 0), idx | 32, idx).astype(np.uint8), s
+
+
+def pack_fp6_tiled(codes) -> np.ndarray:
+    """m x k codes -> the R26 storage (flat bytes, ceil(m/32) * (k/128) * 3072)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    m, k = c.shape
+    g = k // GROUP
+    nb = -(-m // 32)
+    cc = np.zeros((nb * 32, k), dtype=np.uint64)
+    cc[:m] = c
+    # the 192-bit string of each (row, group, step, half): 32 codes, code j at bits 6 j
+    units = cc.reshape(nb, 32, g, 2, 2, 32)                       # b, r, g, s, h, j
+    bits = np.zeros(units.shape[:-1] + (192,), dtype=np.uint8)
+    for j in range(32):
+        for t in range(6):
+            bits[..., 6 * j + t] = (units[..., j] >> np.uint64(t)) & np.uint64(1)
+    byts = np.packbits(bits.reshape(units.shape[:-1] + (24, 8)), axis=-1, bitorder="little")[..., 0]
+    pieces = byts.reshape(nb, 32, g, 2, 2, 3, 8)                  # b, r, g, s, h, u, byte
+    return pieces.transpose(0, 2, 3, 4, 5, 1, 6).reshape(-1).copy()
+
+
+def unpack_fp6_tiled(data, m: int, k: int) -> np.ndarray:
+    """Inverse of pack_fp6_tiled (padding rows dropped)."""
+    g = k // GROUP
+    nb = -(-m // 32)
+    pieces = np.asarray(data, dtype=np.uint8).reshape(nb, g, 2, 2, 3, 32, 8)
+    byts = pieces.transpose(0, 5, 1, 2, 3, 4, 6).reshape(nb, 32, g, 2, 2, 24)
+    bits = np.unpackbits(byts[..., None], axis=-1, bitorder="little").reshape(nb, 32, g, 2, 2, 192)
+    codes = np.zeros((nb, 32, g, 2, 2, 32), dtype=np.uint8)
+    for t in range(6):
+        codes |= (bits[..., t::6][..., :32] << t).astype(np.uint8)
+    return codes.reshape(nb * 32, k)[:m].copy()
+
+
+def w4a6_ref(xcodes, xscales, wcodes, wscales, wfmt: str, afmt: str) -> np.ndarray:
+    """R22 with FP6 activations, in float64."""
+    qx = fp6_decode(xcodes, afmt)
+    vw = fp4_decode(wcodes, wfmt)
+    m, k = qx.shape
+    y = np.zeros((m, vw.shape[0]), dtype=np.float64)
     sw = np.asarray(wscales, dtype=np.float64)
     for g in range(k // GROUP):
         sl = slice(g * GROUP, (g + 1) * GROUP)

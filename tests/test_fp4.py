@@ -176,3 +176,76 @@ def test_tiled_layout_is_a_permutation_and_inverts():
     # multiset of bytes kept, the rest zeros (padding)
     assert np.array_equal(np.sort(t[t > 0]), np.sort(packed.reshape(-1)))
     assert np.count_nonzero(t) == packed.size and np.count_nonzero(ts) == scales.size
+
+
+def test_fp6_formats_published_facts():
+    e23, e32 = F.fp6_values("e2m3"), F.fp6_values("e3m2")
+    assert len(e23) == 32 and len(e32) == 32
+    assert e23[-1] == 7.5 and e32[-1] == 28.0                  # largest finite values of the two formats
+    assert e23[1] == 0.125 and e32[1] == 0.0625                # smallest subnormals
+    assert e23[8] == 1.0 and e32[4] == 0.25                    # smallest normals
+    assert np.all(np.diff(e23) > 0) and np.all(np.diff(e32) > 0)
+    assert list(F.fp6_decode([8, 40, 31, 63], "e2m3")) == [1.0, -1.0, 7.5, -7.5]
+
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+def test_fp6_rows_quantizer(fmt):
+    lv = F.fp6_values(fmt)
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 1, size=(5, 256)).astype(np.float32)
+    x[3] = 0.0
+    codes, s = F.quantize_rows_fp6(x, fmt)
+    assert s[3] == 0 and np.all(codes[3] == 0)
+    for r in (0, 1, 2, 4):
+        assert codes[r, np.argmax(np.abs(x[r]))] & 31 == 31     # the row's amax takes the top code
+        q = (x[r] / s[r]).astype(np.float32)
+        want = _brute_nearest(np.minimum(np.abs(q), lv[-1]), lv)
+        assert np.array_equal(codes[r] & 31, want)
+    assert np.all(((codes & 32) != 0) <= (x < 0))
+    # midpoints of every pair of levels (scale 1: a row whose amax is the top level)
+    mids = np.concatenate([(lv[1:] + lv[:-1]) / 2, [lv[-1]]]).astype(np.float32)
+    c, s1 = F.quantize_rows_fp6(mids[None, :], fmt)
+    assert s1[0] == np.float32(lv[-1]) / np.float32(lv[-1])
+    assert np.array_equal(c[0] & 31, _brute_nearest(mids, lv))
+
+
+def test_fp6_tiled_positions_by_hand():
+    m, k = 40, 256                                              # two row blocks (second padded), G = 2
+    codes = np.zeros((m, k), dtype=np.uint8)
+    codes[0, 5] = 1          # row 0, g 0, s 0, h 0, j 5: bit 30 -> piece 0 byte 3 = 0x40
+    codes[0, 10] = 63        # j 10: bits 60..65 -> piece 0 byte 7 = 0xF0, piece 1 byte 0 = 0x03
+    codes[33, 223] = 1       # row 33 (b 1, r 1), k 223 = g 1, s 1, h 0, j 31: bit 186 -> piece 2 byte 7 bit 2
+    t = F.pack_fp6_tiled(codes)
+    assert t.shape == (2 * 2 * 3072,)
+    assert t[3] == 0x40 and t[7] == 0xF0 and t[256] == 0x03
+    # record (1, 1) at (1*2 + 1)*3072; piece ((1*2 + 0)*3 + 2)*256; row 1 at 8
+    assert t[9216 + 2048 + 8 + 7] == 0x04
+    assert np.count_nonzero(t) == 4
+    assert np.array_equal(F.unpack_fp6_tiled(t, m, k), codes)
+
+
+def test_fp6_tiled_round_trip_and_bijection():
+    rng = np.random.default_rng(9)
+    m, k = 70, 384
+    codes = rng.integers(0, 64, size=(m, k)).astype(np.uint8)
+    t = F.pack_fp6_tiled(codes)
+    assert t.size == 3 * 3 * 3072                               # ceil(70/32) row blocks x 3 groups
+    assert np.array_equal(F.unpack_fp6_tiled(t, m, k), codes)
+    # every set bit of the input lands once: bit counts agree
+    assert int(np.unpackbits(t).sum()) == int(np.unpackbits(codes).sum())
+
+
+def test_w4a6_reference_against_loops():
+    rng = np.random.default_rng(10)
+    m, n, k = 3, 4, 256
+    xc = rng.integers(0, 64, size=(m, k)).astype(np.uint8)
+    wc = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    sx = rng.uniform(0.01, 2, m).astype(np.float32)
+    sw = rng.uniform(0.01, 2, (n, 2)).astype(np.float32)
+    for afmt in F.FP6_FORMATS:
+        y = F.w4a6_ref(xc, sx, wc, sw, "e2m1", afmt)
+        qx, vw = F.fp6_decode(xc, afmt), F.fp4_decode(wc, "e2m1")
+        for i in range(m):
+            for j in range(n):
+                acc = sum(float(sw[j, kk // 128]) * qx[i, kk] * vw[j, kk] for kk in range(k))
+                assert abs(y[i, j] - float(sx[i]) * acc) <= 1e-9 * max(1.0, abs(y[i, j]))
