@@ -486,6 +486,13 @@ def w4a8_suite(args):
     ms_fmt = {f: burst(lambda: api.w4a8_gemm(xq, xs, q, out=y), args.steps)
               for f, q in (("e3m0", api.fp4_quantize_pack(w, "e3m0", tiled=True)),
                            ("e1m2", api.fp4_quantize_pack(w, "e1m2", tiled=True)))}
+    # W4A6: 6-bit activations (tiled E2M1 weights)
+    ms_a6 = {}
+    for f6 in ("e2m3", "e3m2"):
+        x6, s6 = api.fp6_quantize_rows(x, f6)
+        ms_a6[f6] = (burst(lambda: api.w4a6_gemm(x6, s6, f6, qt, out=y), args.steps),
+                     burst(lambda: api.w4a6_gemm(x6, s6, f6, qtp, out=y), args.steps))
+    ms_q6 = burst(lambda: api.fp6_quantize_rows(x, "e2m3"), args.steps)
     qi = api.quantize_pack(w, 4)
     ms_i = burst(lambda: api.dequant_gemm(x, qi, out=y), args.steps)
     del xcs, xqs, xss
@@ -498,6 +505,10 @@ def w4a8_suite(args):
 
     e_w4a8 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qt, torch.float32))
     e_pow2 = rel(api.w4a8_gemm(xq[:1024], xs[:1024], qtp, torch.float32))
+    e_a6 = {}
+    for f6 in ("e2m3", "e3m2"):
+        x6, s6 = api.fp6_quantize_rows(xr, f6)
+        e_a6[f6] = rel(api.w4a6_gemm(x6, s6, f6, qt, torch.float32))
     e_int4 = rel(api.dequant_gemm(xr, qi, torch.float32))
     flops = 2.0 * m * n * k
     print(json.dumps({
@@ -509,8 +520,14 @@ def w4a8_suite(args):
         "w4a8_tiled_pow2_us": round(ms_tp * 1e3, 2), "w4a8_tiled_pow2_TFLOPs": round(flops / ms_tp / 1e9, 1),
         "w4a8_rows_us": round(ms_g * 1e3, 2), "w4a8_rows_pow2_us": round(ms_p * 1e3, 2),
         "w4a8_e3m0_tiled_us": round(ms_fmt["e3m0"] * 1e3, 2), "w4a8_e1m2_tiled_us": round(ms_fmt["e1m2"] * 1e3, 2),
+        "fp6_quantize_rows_us": round(ms_q6 * 1e3, 2),
+        "w4a6_e2m3_us": round(ms_a6["e2m3"][0] * 1e3, 2), "w4a6_e2m3_TFLOPs": round(flops / ms_a6["e2m3"][0] / 1e9, 1),
+        "w4a6_e2m3_pow2_us": round(ms_a6["e2m3"][1] * 1e3, 2),
+        "w4a6_e2m3_pow2_TFLOPs": round(flops / ms_a6["e2m3"][1] / 1e9, 1),
+        "w4a6_e3m2_us": round(ms_a6["e3m2"][0] * 1e3, 2), "w4a6_e3m2_pow2_us": round(ms_a6["e3m2"][1] * 1e3, 2),
         "int4_bf16_gemm_us": round(ms_i * 1e3, 2), "int4_bf16_TFLOPs": round(flops / ms_i / 1e9, 1),
         "w4a8_rel_err_vs_f32": round(e_w4a8, 5), "w4a8_pow2_rel_err_vs_f32": round(e_pow2, 5),
+        "w4a6_e2m3_rel_err_vs_f32": round(e_a6["e2m3"], 5), "w4a6_e3m2_rel_err_vs_f32": round(e_a6["e3m2"], 5),
         "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
     }), flush=True)
 

@@ -56,11 +56,14 @@ SIGNATURES = {
     "ddg_fp4_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
     "ddg_fp8_quantize_rows": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ddg_w4a8_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
+    "ddg_fp6_quantize_rows": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
+    "ddg_w4a6_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_int, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
 }
 
 FP4_FORMATS = {"e2m1": 0, "e3m0": 1, "e1m2": 2}
 FP4_POW2 = 0x100
 FP4_TILED = 0x200
+FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
 
 ROTATE_MAX_D, ROTATE_MAX_H = 16384, 1024
 
@@ -442,3 +445,41 @@ def pd_allocate(mse, nparams, target_bpw: float, t_init, iters: int = 500,
         t_init.ctypes.data_as(dp), t_init.shape[0], iters, bits.ctypes.data_as(ctypes.POINTER(_c_int)),
         info.ctypes.data_as(dp)), "ddg_pd_allocate")
     return bits.astype(np.int64), {"mse": float(info[0]), "bpw": float(info[1]), "restart": int(info[2])}
+
+
+def fp6_quantize_rows(x: torch.Tensor, fmt: str = "e2m3"):
+    """Per-token FP6 codes of a bf16 X in the tiled 6-bit storage (flat uint8,
+    ceil(m/32) * k/128 * 3072 bytes) and the m float32 scales."""
+    _require_cuda(x, "x")
+    if fmt not in FP6_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP6_FORMATS)}")
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    x = x.contiguous()
+    m, k = x.shape
+    xq = torch.empty((-(-m // 32) * max(k // GROUP, 0) * 3072,), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(load_library().ddg_fp6_quantize_rows(x.data_ptr(), m, k, FP6_FORMATS[fmt], xq.data_ptr(), xs.data_ptr(),
+                                                _stream_ptr(x.device)), "ddg_fp6_quantize_rows")
+    return xq, xs
+
+
+def w4a6_gemm(xq: torch.Tensor, xs: torch.Tensor, fmt: str, qw: QWeightFP4, out_dtype=torch.bfloat16,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = s_x[m] * sum_g s_w[n, g] (X_q W_q^T)_g on the FP6 x FP4 matrix cores
+    (X from fp6_quantize_rows in format fmt; tiled E2M1 weights)."""
+    for t, name in ((xq, "xq"), (xs, "xs")):
+        _require_cuda(t, name)
+    if fmt not in FP6_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP6_FORMATS)}")
+    m = xs.shape[0]
+    if xq.dtype != torch.uint8 or xq.numel() != -(-m // 32) * (qw.k // GROUP) * 3072 or xs.dim() != 1:
+        raise ValueError("xq must be the tiled 6-bit storage of m x k codes, with m float32 scales")
+    y = out if out is not None else torch.empty((m, qw.n), dtype=out_dtype, device=xq.device)
+    if y.shape != (m, qw.n) or y.dtype not in (torch.bfloat16, torch.float32) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous m x n bf16 or float32 tensor")
+    _check(load_library().ddg_w4a6_gemm(xq.contiguous().data_ptr(), xs.contiguous().data_ptr(), m, qw.k,
+                                        FP6_FORMATS[fmt], qw.packed.data_ptr(), qw.scales.data_ptr(), qw.fmt_code,
+                                        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
+                                        _stream_ptr(xq.device)), "ddg_w4a6_gemm")
+    return y

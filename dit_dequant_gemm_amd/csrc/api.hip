@@ -385,6 +385,45 @@ int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, floa
                                                   xscales, stream));
 }
 
+int ddg_fp6_quantize_rows(const void* x, int64_t m, int64_t k, int fmt6, uint8_t* xq, float* xscales,
+                          hipStream_t stream) {
+  if (fmt6 != DDG_FP6_E2M3 && fmt6 != DDG_FP6_E3M2) return DDG_ERR_ARG;
+  if (m < 0 || m > kMaxDim || !k_ok(k) || !mul_ok(m + 31, k) || !mul_ok((m + 31) * k, 2)) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!x || !xq || !xscales) return DDG_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xscales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(ddg::launch_fp6_quantize_rows(static_cast<const uint16_t*>(x), m, (int)k, fmt6, xq, xscales,
+                                                  stream));
+}
+
+int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, int fmt6, const uint8_t* packed,
+                  const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
+  if (fmt6 != DDG_FP6_E2M3 && fmt6 != DDG_FP6_E3M2) return DDG_ERR_ARG;
+  if (!fp4_fmt_ok(fmt) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32)) return DDG_ERR_ARG;
+  if ((fmt & ~kFp4Flags) != DDG_FP4_E2M1 || !(fmt & DDG_FP4_TILED)) return DDG_ERR_ARG;   // tiled E2M1 only
+  if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || !mul_ok(m, n) ||
+      !mul_ok(m * n, 4) || !mul_ok(n, k))
+    return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!xq || !xscales || !packed || !wscales || !y) return DDG_ERR_ARG;
+  if (!aligned(xq, 16) || !aligned(packed, 16) || !aligned(xscales, 4) || !aligned(wscales, 4) ||
+      !aligned(y, y_dtype == DDG_F32 ? 4 : 2))
+    return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  ddg::W4A8Args a{};
+  a.xq = xq;
+  a.xscales = xscales;
+  a.packed = packed;
+  a.wscales = wscales;
+  a.y = y;
+  a.m = (int)m; a.n = (int)n; a.k = (int)k;
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return hip_status(ddg::launch_w4a6_gemm(a, fmt6, (fmt & DDG_FP4_POW2) != 0, stream));
+}
+
 int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, const uint8_t* packed,
                   const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
   if (!fp4_fmt_ok(fmt) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))

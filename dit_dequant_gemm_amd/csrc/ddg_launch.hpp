@@ -61,6 +61,12 @@ hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n, int k
 hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t* q, float* sx,
                                     hipStream_t stream);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, bool pow2, bool tiled, hipStream_t stream);
+// 6-bit activations (formats kFp6E2M3, kFp6E3M2) in the tiled 6-bit storage;
+// the product takes tiled E2M1 weights (xq of W4A8Args: the 6-bit storage)
+constexpr int kFp6E2M3 = 0, kFp6E3M2 = 1;
+hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt6, uint8_t* q, float* sx,
+                                    hipStream_t stream);
+hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream);
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);

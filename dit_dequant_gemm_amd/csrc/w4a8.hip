@@ -1,9 +1,12 @@
-// FP4 weights x FP8 activations (W4A8) on the gfx950 scaled matrix
-// instructions (the FP4DiT article: 4-bit floating-point weight formats in
-// groups of 128, §3.2.1 / §4.1; 8-bit per-token activations, §3.2.3):
+// FP4 weights x FP8 or FP6 activations (W4A8, W4A6) on the gfx950 scaled
+// matrix instructions (the FP4DiT article: 4-bit floating-point weight
+// formats in groups of 128, §3.2.1 / §4.1; 8- and 6-bit per-token
+// activations, §3.2.3 / §4.1):
 //   fp4_quantize_pack_kernel  per-group(128) scale + nearest 4-bit level, packed
 //                             two codes per byte (even index in the low nibble)
 //   fp8_quantize_rows_kernel  per-token scale + E4M3 round-to-nearest-even
+//   fp6_quantize_rows_kernel  per-token scale + E2M3 / E3M2 rounding, written
+//                             in the tiled 6-bit storage the product reads
 //   w4a8_gemm_kernel          Y = s_x[m] sum_g s_w[n,g] (X_q W_q^T)_g
 #include "ddg_launch.hpp"
 
@@ -214,6 +217,102 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const uint16_t* 
   if (lane == 0) sx[row] = zero ? 0.0f : s;
 }
 
+// FP6 (sign + EB exponent + MB mantissa bits, bias BIAS, subnormal at
+// exponent 0, no infinities): E2M3 = <2, 3, 1> (largest 7.5), E3M2 =
+// <3, 2, 3> (largest 28).
+template <int EB, int MB, int BIAS>
+struct Fp6Fmt {
+  static constexpr float vmax = (2.0f - 1.0f / (float)(1 << MB)) * (float)(1 << ((1 << EB) - 1 - BIAS));
+  static constexpr float min_normal = 1.0f / (float)(1 << (BIAS - 1));
+  static constexpr float sub_scale = (float)(1 << (BIAS - 1 + MB));    // 1 / subnormal spacing
+};
+
+// FP6 code of a finite float: clamp to the largest value, round to nearest
+// even (subnormals: multiples of the spacing; normals: MB mantissa bits).
+template <int EB, int MB, int BIAS>
+__device__ __forceinline__ uint32_t fp6_code(float r) {
+  using F = Fp6Fmt<EB, MB, BIAS>;
+  const float a = __builtin_fminf(__builtin_fabsf(r), F::vmax);
+  uint32_t mag;
+  if (a < F::min_normal) {
+    mag = (uint32_t)__builtin_rintf(a * F::sub_scale);
+  } else {
+    constexpr int sh = 23 - MB;
+    uint32_t b = __builtin_bit_cast(uint32_t, a);
+    b += ((1u << (sh - 1)) - 1u) + ((b >> sh) & 1u);
+    mag = ((((b >> 23) - 127u + BIAS) & ((1u << EB) - 1u)) << MB) | ((b >> sh) & ((1u << MB) - 1u));
+  }
+  return (mag != 0u && r < 0.0f) ? (mag | 32u) : mag;
+}
+
+// Tiled 6-bit storage: rows in blocks of 32 (padded with zero codes); the 32
+// codes of (row, group g, 64-wide step s, half h) -- k = 128 g + 64 s + 32 h
+// + j -- form a 192-bit little-endian string (code j at bits 6 j), cut into
+// three 8-byte pieces u; piece u of row 32 b + r lives at byte
+// ((2 s + h) * 3 + u) * 256 + 8 r of record (b, g), 3072 bytes, records in
+// (b, g) order.  A matrix operand (one lane half, one step) is then three
+// 8-byte reads that 32 lanes take from 256 contiguous bytes.
+constexpr int kX6Record = 3072;
+
+// One wave per row (four rows per workgroup), rows up to m_pad (padding rows
+// get zero codes and no scale): the row's abs-max, then s = amax / vmax and,
+// per 32-value unit, the codes, packed and stored as three pieces.
+template <int EB, int MB, int BIAS>
+__global__ __launch_bounds__(256) void fp6_quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
+                                                               int64_t m_pad, int k, uint8_t* __restrict__ q,
+                                                               float* __restrict__ sx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m_pad) return;
+  const int G = k / 128, units = k / 32;
+  uint8_t* rec = q + (row >> 5) * (int64_t)G * kX6Record + (row & 31) * 8;
+  if (row >= m) {
+    const u32x2 z = {0u, 0u};
+    for (int un = lane; un < units; un += 64)
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        *reinterpret_cast<u32x2*>(rec + (un >> 2) * kX6Record + ((un & 3) * 3 + u) * 256) = z;
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
+  float a = 0.0f;
+  for (int c = lane; c < k / 8; c += 64) {
+    const u32x4 t = src[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] & 0xFFFFu)));
+      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+  const float s = a / Fp6Fmt<EB, MB, BIAS>::vmax;
+  const bool zero = !(s != 0.0f);
+  for (int un = lane; un < units; un += 64) {
+    uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 t = src[un * 4 + i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * i + e;
+        const uint32_t h = (e & 1) ? (t[e >> 1] >> 16) : (t[e >> 1] & 0xFFFFu);
+        const float r = zero ? 0.0f : bf16_bits_to_f32(h) / s;
+        const uint32_t c = fp6_code<EB, MB, BIAS>(r);
+        const int bit = 6 * j;
+        w[bit >> 5] |= c << (bit & 31);
+        if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const u32x2 piece = {w[2 * u], w[2 * u + 1]};
+      *reinterpret_cast<u32x2*>(rec + (un >> 2) * kX6Record + ((un & 3) * 3 + u) * 256) = piece;
+    }
+  }
+  if (lane == 0) sx[row] = zero ? 0.0f : s;
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16e __attribute__((ext_vector_type(16)));
 
@@ -239,16 +338,27 @@ constexpr int kW8Stages = 3;
 // pair); with power-of-two scales (POW2) the instruction applies the scale
 // itself (its B block scale, E8M0 = the scale's exponent field) and
 // accumulates straight into acc.
-template <int FMT, bool POW2, bool TILED, int WM, int CB>
+//
+// AF selects the activation operand: 0 = E4M3 rows (above), 2 = E2M3 or
+// 3 = E3M2 in the tiled 6-bit storage (8 records of 3 KB per group: 24 KB
+// stages, three DMAs per wave, A read as three conflict-free 8-byte pieces).
+// FP6 and FP4 operands share one lane layout, so an FP6 A lane half h pairs
+// element j with the FP4 B element j of the same half: both carry the
+// step's k 32 h + j.
+template <int FMT, bool POW2, bool TILED, int WM, int CB, int AF>
 __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   constexpr int RB = 8 / WM;
   constexpr int TN = 32 * CB * (8 / WM);
+  constexpr bool kA6 = AF != 0;
+  static_assert(!kA6 || (FMT == kFp4E2M1 && TILED), "6-bit activations pair with tiled E2M1 weights");
+  constexpr int kStage = kA6 ? 8 * kX6Record : kW8Stage;
+  constexpr int kXDma = kA6 ? 3 : 4;                     // X DMAs per wave and group
   // one array per stage, every stage index a compile-time constant: the
   // compiler can then tell the stage being read from the one being filled
   // and keeps the fill in flight across the barrier
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kW8Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kW8Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kW8Stage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
@@ -262,7 +372,10 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   const uint32_t wrow = (uint32_t)K / 2;
   const int m_valid = min(256, args.m - m0);
   const int n_valid = min(TN, args.n - n0);
-  const rsrc_t rx = make_rsrc(args.xq + (int64_t)m0 * K, (uint32_t)m_valid * (uint32_t)K);
+  // X of this tile: 256 rows, or (6-bit) its row-block records (8 per group)
+  const int rb_valid = (m_valid + 31) / 32;
+  const rsrc_t rx = kA6 ? make_rsrc(args.xq + (int64_t)(m0 / 32) * G * kX6Record, (uint32_t)(rb_valid * G) * kX6Record)
+                        : make_rsrc(args.xq + (int64_t)m0 * K, (uint32_t)m_valid * (uint32_t)K);
   // weights and scales of this tile's columns (tiled: its whole 32-column
   // blocks, 2048 bytes and 32 scales per block and group)
   const int nblk = (n_valid + 31) / 32;
@@ -280,11 +393,20 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
     const int c = (lane & 7) ^ xswz(r);
     xoff[i] = (uint32_t)r * (uint32_t)K + (uint32_t)c * 16;
   }
+  // 6-bit: wave w copies record (row block w of the tile, group g), 3 KB
+  const uint32_t x6off = (uint32_t)wave * (uint32_t)G * kX6Record + (uint32_t)lane * 16;
   auto issue_x = [&](int g, uint8_t* stage) __attribute__((always_inline)) {
+    if constexpr (kA6) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stage + (4 * wave + i) * 1024), 16, xoff[i],
-                                               (uint32_t)g * 128, 0, 0);
+      for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stage + wave * kX6Record + i * 1024), 16,
+                                                 x6off + i * 1024, (uint32_t)g * kX6Record, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stage + (4 * wave + i) * 1024), 16, xoff[i],
+                                                 (uint32_t)g * 128, 0, 0);
+    }
   };
   // B: the lane's column of each column block; per 64-wide step ks, lane
   // half h loads the 16 bytes (codes 32 h .. 32 h + 31 of the step) at byte
@@ -329,6 +451,16 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
       sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff[cb], (uint32_t)g * kGroupS, 0));
   };
   auto read_a = [&](const uint8_t* stage, int rb, int ks) __attribute__((always_inline)) -> i32x8 {
+    if constexpr (kA6) {
+      const uint8_t* p = stage + (wm * RB + rb) * kX6Record + (ks * 2 + lh) * 3 * 256 + lr * 8;
+      const u32x2 p0 = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 p1 = *reinterpret_cast<const u32x2*>(p + 256);
+      const u32x2 p2 = *reinterpret_cast<const u32x2*>(p + 512);
+      i32x8 a;
+      a[0] = (int)p0[0]; a[1] = (int)p0[1]; a[2] = (int)p1[0]; a[3] = (int)p1[1];
+      a[4] = (int)p2[0]; a[5] = (int)p2[1]; a[6] = 0; a[7] = 0;
+      return a;
+    }
     const int r = wm * 32 * RB + rb * 32 + lr;
     const int c0 = kNative ? 4 * ks + lh : 4 * ks + 2 * lh;
     const int c1 = kNative ? c0 + 2 : c0 + 1;
@@ -410,14 +542,14 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         if constexpr (POW2) {
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], acc[rb][cb], 0, kBFmt,
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], acc[rb][cb], AF, kBFmt,
                                                                         0, 127, 0, sb[cb]);
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], acc[rb][cb], 0, kBFmt,
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], acc[rb][cb], AF, kBFmt,
                                                                         0, 127, 0, sb[cb]);
         } else {
-          f32x16e t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], zero16, 0, kBFmt,
+          f32x16e t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bop[cb][0], zero16, AF, kBFmt,
                                                                       0, 127, 0, 127);
-          t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], t, 0, kBFmt, 0, 127, 0, 127);
+          t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bop[cb][1], t, AF, kBFmt, 0, 127, 0, 127);
           if constexpr (kPipeScale) {
             if (rb * CB + cb > 0) {
               const int p = rb * CB + cb - 1;                // the previous block, scaled now
@@ -443,9 +575,9 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
       for (int i = 0; i < 16; ++i)
         acc[RB - 1][CB - 1][i] = __builtin_fmaf(tp[i], sc[CB - 1], acc[RB - 1][CB - 1][i]);
     }
-    // everything but this wave's four X DMAs of group g + 2 has landed: the
-    // next group's weights and (for every wave, after the barrier) its X
-    __builtin_amdgcn_s_waitcnt(0x0F74);
+    // everything but this wave's X DMAs of group g + 2 has landed: the next
+    // group's weights and (for every wave, after the barrier) its X
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kXDma);
     // ... and every wave is done with stage st.  A plain barrier: a release
     // fence would also wait for the X DMAs just issued.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -526,12 +658,12 @@ hipError_t launch_fp4_quant(const void* w, bool f32_in, bool pow2, bool tiled, i
               : launch_fp4_quant3<FMT, false, false>(n, k, tiled, w, packed, scales, stream);
 }
 
-template <int FMT, bool POW2, bool TILED, int WM, int CB>
+template <int FMT, bool POW2, bool TILED, int WM, int CB, int AF = 0>
 hipError_t launch_w4a8_cfg(W4A8Args a, hipStream_t stream) {
   constexpr int TN = 32 * CB * (8 / WM);
   a.tiles_m = (a.m + 255) / 256;
   a.tiles_n = (a.n + TN - 1) / TN;
-  w4a8_gemm_kernel<FMT, POW2, TILED, WM, CB><<<dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream>>>(a);
+  w4a8_gemm_kernel<FMT, POW2, TILED, WM, CB, AF><<<dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(512), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -563,6 +695,27 @@ hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n, int k
     case kFp4E3M0: return launch_fp4_quant<kFp4E3M0>(w, f32_in, pow2, tiled, n, k, packed, scales, stream);
     case kFp4E1M2: return launch_fp4_quant<kFp4E1M2>(w, f32_in, pow2, tiled, n, k, packed, scales, stream);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt6, uint8_t* q, float* sx,
+                                    hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  const int64_t m_pad = (m + 31) / 32 * 32;
+  const dim3 grid((unsigned)((m_pad + 3) / 4)), block(256);
+  if (fmt6 == kFp6E2M3) fp6_quantize_rows_kernel<2, 3, 1><<<grid, block, 0, stream>>>(x, m, m_pad, k, q, sx);
+  else if (fmt6 == kFp6E3M2) fp6_quantize_rows_kernel<3, 2, 3><<<grid, block, 0, stream>>>(x, m, m_pad, k, q, sx);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream) {
+  if (fmt6 == kFp6E2M3)
+    return pow2 ? launch_w4a8_cfg<kFp4E2M1, true, true, 4, 3, 2>(a, stream)
+                : launch_w4a8_cfg<kFp4E2M1, false, true, 4, 3, 2>(a, stream);
+  if (fmt6 == kFp6E3M2)
+    return pow2 ? launch_w4a8_cfg<kFp4E2M1, true, true, 4, 3, 3>(a, stream)
+                : launch_w4a8_cfg<kFp4E2M1, false, true, 4, 3, 3>(a, stream);
   return hipErrorInvalidValue;
 }
 

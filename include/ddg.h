@@ -345,6 +345,46 @@ int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
                   const uint8_t* packed, const float* wscales, int fmt, int64_t n, void* y,
                   int y_dtype, hipStream_t stream);
 
+/*
+ * 6-bit activations (W4A6), the FP4DiT article §3.2.3 / §4.1 (W4A6) and §3.3
+ * (FP6 saves memory over FP8).  Formats (sign + magnitude, subnormal when the
+ * exponent field is 0, no infinities):
+ *   DDG_FP6_E2M3  bias 1, largest 7.5
+ *   DDG_FP6_E3M2  bias 3, largest 28
+ */
+#define DDG_FP6_E2M3 0
+#define DDG_FP6_E3M2 1
+
+/*
+ * Per token (row) of x (m x k bf16): s_x = fl32(amax / vmax), r = fl32(x / s_x),
+ * code = the nearest FP6 value to |r| (|r| clamped to vmax, ties to the even
+ * code), sign in bit 5; an all-zero row gets s_x = 0 and zeros.  xq is the
+ * tiled 6-bit storage the product reads: rows padded to a multiple of 32 with
+ * zero codes; the 32 codes of (row, group g, 64-wide step s, half h), k =
+ * 128 g + 64 s + 32 h + j, form a 192-bit little-endian string (code j at bits
+ * 6 j) cut into three 8-byte pieces u; piece u of row 32 b + r is at byte
+ * ((2 s + h) * 3 + u) * 256 + 8 r of record (b, g), 3072 bytes, records in
+ * (b, g) order.  Size: ceil(m/32) * (k/128) * 3072 bytes.
+ *   x   device, 16-byte aligned.  xq  device, 16-byte aligned.
+ *   xscales  device, m floats.
+ * m == 0 is a no-op.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (k not a positive
+ * multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_fp6_quantize_rows(const void* x, int64_t m, int64_t k, int fmt6, uint8_t* xq, float* xscales,
+                          hipStream_t stream);
+
+/*
+ * Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k] with q_x
+ * the FP6 values of ddg_fp6_quantize_rows (format fmt6) and v_w E2M1 weights
+ * in tiled storage (fmt = DDG_FP4_E2M1 | DDG_FP4_TILED, optionally
+ * | DDG_FP4_POW2), on the FP6 x FP4 matrix instructions; float32 accumulation.
+ * Other weight formats or row storage: DDG_ERR_ARG.  Other arguments and
+ * errors as ddg_w4a8_gemm.
+ */
+int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, int fmt6,
+                  const uint8_t* packed, const float* wscales, int fmt, int64_t n, void* y,
+                  int y_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -241,6 +241,31 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     assert call(fmt=5) == E_ARG and call(ydt=3) == E_ARG
     assert call(fmt=0x103) == E_ARG and call(fmt=0x400) == E_ARG and call(fmt=0x203) == E_ARG
     assert call(fmt=0x101, m=0, xq=None) == OK and call(fmt=0x302, m=0, xq=None) == OK
+
+    r6 = lib.ddg_fp6_quantize_rows
+    assert r6(FAKE, 4, 128, 2, FAKE, FAKE, None) == E_ARG               # fp6 format
+    assert r6(FAKE, 4, 100, 0, FAKE, FAKE, None) == E_SHAPE
+    assert r6(FAKE, -1, 128, 0, FAKE, FAKE, None) == E_SHAPE
+    assert r6(None, 4, 128, 1, FAKE, FAKE, None) == E_ARG
+    assert r6(MISALIGNED, 4, 128, 0, FAKE, FAKE, None) == E_ALIGN
+    assert r6(FAKE, 4, 128, 0, FAKE + 8, FAKE, None) == E_ALIGN
+    assert r6(None, 0, 128, 0, None, None, None) == OK
+    g6 = lib.ddg_w4a6_gemm
+    base6 = [FAKE, FAKE, 4, 128, 0, FAKE, FAKE, 0x200, 32, FAKE, 0, None]
+
+    def call6(**kw):
+        a = list(base6)
+        idx = {"xq": 0, "xs": 1, "m": 2, "k": 3, "f6": 4, "packed": 5, "ws": 6, "fmt": 7, "n": 8, "y": 9, "ydt": 10}
+        for key, v in kw.items():
+            a[idx[key]] = v
+        return g6(*a)
+
+    assert call6(f6=2) == E_ARG and call6(fmt=5) == E_ARG and call6(ydt=3) == E_ARG
+    assert call6(fmt=0) == E_ARG and call6(fmt=0x201) == E_ARG and call6(fmt=0x101) == E_ARG   # tiled E2M1 only
+    assert call6(k=130) == E_SHAPE and call6(n=0) == E_SHAPE and call6(m=-1) == E_SHAPE
+    assert call6(xq=None) == E_ARG and call6(y=None) == E_ARG
+    assert call6(xq=MISALIGNED) == E_ALIGN
+    assert call6(m=0, xq=None) == OK and call6(m=0, fmt=0x300, xq=None) == OK
     assert call(k=130) == E_SHAPE and call(k=2 ** 20 + 128) == E_SHAPE
     assert call(n=0) == E_SHAPE and call(m=-1) == E_SHAPE
     assert call(xq=None) == E_ARG and call(packed=None) == E_ARG and call(y=None) == E_ARG

@@ -250,3 +250,81 @@ def test_w4a8_tiled_chain_attention_projection_sampled(gpu_lib):
     rows = np.r_[0:32, 2048:2080, 4064:4096]
     xc, xsc = F.quantize_rows_e4m3(c["x"][rows])
     _check_f32_product(y[rows], xc, xsc, wc, ws, F.w4a8_ref(xc, xsc, wc, ws, "e2m1"))
+
+
+# ---- W4A6: 6-bit activations ----
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (33, 256), (100, 3072), (64, 13824)])
+def test_fp6_rows_bit_exact(gpu_lib, fmt, m, k):
+    _case(f"fp6_quantize_rows {fmt} m={m} k={k}")
+    x = synth.to_bf16(np.random.default_rng(m * 3 + k).normal(0, 1, size=(m, k)))
+    if m > 4:
+        x[3] = 0.0                                         # a zero row
+    xq, xs = gpu_lib.fp6_quantize_rows(dev_bf16(x), fmt)
+    cq, cs = F.quantize_rows_fp6(x, fmt)
+    assert np.array_equal(host(xq), F.pack_fp6_tiled(cq))  # padding rows included: zero codes
+    assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+def test_fp6_rows_ties_and_subnormals(gpu_lib, fmt):
+    _case(f"fp6_quantize_rows {fmt}: midpoints, subnormal range")
+    lv = F.fp6_values(fmt)
+    x = np.zeros((3, 128), dtype=np.float64)
+    mids = (lv[1:] + lv[:-1]) / 2                          # scale 1: the row's amax is the top level
+    x[0, :31] = mids
+    x[0, 40:71] = -mids
+    x[0, 127] = lv[-1]
+    x[1] = np.random.default_rng(4).normal(0, 1, 128)
+    x[1, 0] = 1000.0                                       # most of the row in the subnormal range
+    x = synth.to_bf16(x)
+    xq, xs = gpu_lib.fp6_quantize_rows(dev_bf16(x), fmt)
+    cq, cs = F.quantize_rows_fp6(x, fmt)
+    assert np.array_equal(host(xq), F.pack_fp6_tiled(cq))
+    assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
+
+
+def _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt):
+    absref = F.w4a6_ref(xc & 31, xs, wc & 7, ws, "e2m1", afmt)
+    assert np.all(np.abs(y - ref) <= 2.0 ** -14 * absref + 1e-37), \
+        float(np.max(np.abs(y - ref) / (absref + 1e-37)))
+    check_product(y, ref, False, f"w4a6 f32 {afmt} k={xc.shape[1]}")
+
+
+@pytest.mark.parametrize("afmt", list(F.FP6_FORMATS))
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (300, 272, 640), (513, 300, 2048), (64, 1000, 128),
+                                   (257, 33, 384)])
+def test_w4a6_gemm(gpu_lib, m, n, k, afmt, pow2):
+    """The product on the oracle's FP6 codes (tiled by the oracle) and tiled E2M1 weights."""
+    _case(f"w4a6_gemm {afmt} pow2={pow2} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 11 + n + k)
+    w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
+    x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
+    wc, ws = F.quantize_fp4_groups(w, "e2m1", pow2=pow2)
+    xc, xs = F.quantize_rows_fp6(x, afmt)
+    t, ts = F.tile_fp4(F.pack_fp4(wc), ws)
+    qw = gpu_lib.QWeightFP4(_cuda_u8(t), _cuda_f32(ts), "e2m1", n, k, pow2=pow2, tiled=True)
+    ref = F.w4a6_ref(xc, xs, wc, ws, "e2m1", afmt)
+    xq = _cuda_u8(F.pack_fp6_tiled(xc))
+    y = host(gpu_lib.w4a6_gemm(xq, _cuda_f32(xs), afmt, qw, torch.float32))
+    _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt)
+    yb = host(gpu_lib.w4a6_gemm(xq, _cuda_f32(xs), afmt, qw, torch.bfloat16))
+    check_product(yb, ref, True, f"w4a6 bf16 {afmt} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("afmt", list(F.FP6_FORMATS))
+def test_w4a6_chain_attention_projection_sampled(gpu_lib, afmt):
+    """GPU quantizers feeding the W4A6 product at 4096 x 3072 x 3072; m = 0 is a no-op."""
+    _case(f"w4a6 chain {afmt} 4096 x 3072 x 3072 (sampled rows)")
+    c = synth.config2()
+    qw = gpu_lib.fp4_quantize_pack(dev_bf16(c["w"]), "e2m1", tiled=True)
+    xq, xs = gpu_lib.fp6_quantize_rows(dev_bf16(c["x"]), afmt)
+    y = host(gpu_lib.w4a6_gemm(xq, xs, afmt, qw, torch.float32))
+    wc, ws = F.quantize_fp4_groups(c["w"], "e2m1")
+    rows = np.r_[0:32, 2048:2080, 4064:4096]
+    xc, xsc = F.quantize_rows_fp6(c["x"][rows], afmt)
+    _check_w4a6_f32(y[rows], xc, xsc, wc, ws, F.w4a6_ref(xc, xsc, wc, ws, "e2m1", afmt), afmt)
+    empty = gpu_lib.w4a6_gemm(xq[:0], xs[:0], afmt, qw, torch.float32)
+    assert empty.shape == (0, 3072)
