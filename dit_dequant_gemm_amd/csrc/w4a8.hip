@@ -353,12 +353,22 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   static_assert(!kA6 || (FMT == kFp4E2M1 && TILED), "6-bit activations pair with tiled E2M1 weights");
   constexpr int kStage = kA6 ? 8 * kX6Record : kW8Stage;
   constexpr int kXDma = kA6 ? 3 : 4;                     // X DMAs per wave and group
+  // Several waves along M share each weight column: then the tile's weight
+  // records (tiled storage) go to LDS by DMA together with X, two groups
+  // ahead and once per workgroup, and every wave reads its B operands there.
+  constexpr bool kBLds = TILED && WM > 1;
+  constexpr int kNBlk = (8 / WM) * CB;                   // 32-column blocks per tile
+  constexpr int kBStage = kBLds ? kNBlk * 2048 : 0;
+  constexpr int kBDma = kBLds ? (2 * kNBlk + 7) / 8 : 0; // per wave; the surplus repeats the first records
   // one array per stage, every stage index a compile-time constant: the
   // compiler can then tell the stage being read from the one being filled
   // and keeps the fill in flight across the barrier
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldb0[kBLds ? kBStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldb1[kBLds ? kBStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldb2[kBLds ? kBStage : 16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
@@ -440,15 +450,31 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   constexpr uint32_t kStepOff = TILED ? 1024u : 32u;           // ks = 1
   constexpr uint32_t kGroupW = TILED ? 2048u : 64u, kGroupS = TILED ? 128u : 4u;
   auto load_w = [&](int g, u32x4 (&b)[CB][2], float (&sc)[CB]) __attribute__((always_inline)) {
+    if constexpr (!kBLds) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        b[cb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rw, woff[cb] + kStepOff * ks, (uint32_t)g * kGroupW, 0));
+        for (int ks = 0; ks < 2; ++ks)
+          b[cb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rw, woff[cb] + kStepOff * ks, (uint32_t)g * kGroupW, 0));
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff[cb], (uint32_t)g * kGroupS, 0));
+  };
+  // the tile's weight records of group g -> LDS after the X stage: DMA d
+  // (0 .. 2 kNBlk - 1) copies half d % 2 of block d / 2
+  auto issue_b = [&](int g, uint8_t* stage) __attribute__((always_inline)) {
+    if constexpr (kBLds) {
+#pragma unroll
+      for (int i = 0; i < kBDma; ++i) {
+        const int d = (kBDma * wave + i) % (2 * kNBlk);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (lds_ptr_t)(stage + d * 1024), 16,
+            (uint32_t)(d >> 1) * (uint32_t)G * 2048u + (uint32_t)(d & 1) * 1024u + (uint32_t)lane * 16u,
+            (uint32_t)g * 2048u, 0, 0);
+      }
+    }
   };
   auto read_a = [&](const uint8_t* stage, int rb, int ks) __attribute__((always_inline)) -> i32x8 {
     if constexpr (kA6) {
@@ -490,25 +516,32 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   // into the stage read in g - 1 (fill), multiply stage st with (bc, sc).
   // The last groups fetch themselves again into idle stages (never read), so
   // that the body stays one straight block.
-  auto step = [&](int g, const uint8_t* st, uint8_t* fill) __attribute__((always_inline)) {
+  auto step = [&](int g, const uint8_t* st, uint8_t* fill, const uint8_t* stb, uint8_t* fillb)
+                  __attribute__((always_inline)) {
     load_w(min(g + 1, G - 1), bn, sn);
     __builtin_amdgcn_sched_barrier(0);           // weights before X: the wait below counts on it
     issue_x(min(g + 2, G - 1), fill);
+    issue_b(min(g + 2, G - 1), fillb);
     i32x8 bop[CB][2];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        u32x4 braw;
+        if constexpr (kBLds)
+          braw = *reinterpret_cast<const u32x4*>(stb + (wn * CB + cb) * 2048 + ks * 1024 + lh * 512 + lr * 16);
+        else
+          braw = bc[cb][ks];
         if constexpr (kNative) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            bop[cb][ks][j] = (int)bc[cb][ks][j];
+            bop[cb][ks][j] = (int)braw[j];
             bop[cb][ks][j + 4] = 0;
           }
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const u32x2 c = fp4_codes_to_e4m3<FMT>(bc[cb][ks][j]);
+            const u32x2 c = fp4_codes_to_e4m3<FMT>(braw[j]);
             bop[cb][ks][2 * j] = (int)c[0];
             bop[cb][ks][2 * j + 1] = (int)c[1];
           }
@@ -521,12 +554,12 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
     // with power-of-two scales row block rb's A reads are issued one row
     // block earlier; with float32 scales (16 more registers live for the
     // rescale) at the top of the row block, behind the previous MFMAs
-    constexpr bool kPrefetchA = POW2;
+    constexpr bool kPrefetchA = POW2 || kBLds;
     // float32 scales: a block's partial sum is scaled into acc while the next
     // block's MFMAs run (kPipeScale), or right after its own MFMAs where the
     // tile leaves too few registers for the second partial sum (the other
     // wave on the SIMD covers the wait)
-    constexpr bool kPipeScale = RB * CB <= 4;
+    constexpr bool kPipeScale = RB * CB <= 4 || kBLds;
     i32x8 a0 = read_a(st, 0, 0), a1 = read_a(st, 0, 1);
     f32x16e tp;
 #pragma unroll
@@ -575,9 +608,11 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
       for (int i = 0; i < 16; ++i)
         acc[RB - 1][CB - 1][i] = __builtin_fmaf(tp[i], sc[CB - 1], acc[RB - 1][CB - 1][i]);
     }
-    // everything but this wave's X DMAs of group g + 2 has landed: the next
+    // everything but this wave's DMAs of group g + 2 has landed: the next
     // group's weights and (for every wave, after the barrier) its X
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kXDma);
+    constexpr int kAhead = kXDma + kBDma;
+    static_assert(kAhead < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kAhead);
     // ... and every wave is done with stage st.  A plain barrier: a release
     // fence would also wait for the X DMAs just issued.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -590,19 +625,21 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   };
 
   issue_x(0, lds0);
+  issue_b(0, ldb0);
   issue_x(min(1, G - 1), lds1);
+  issue_b(min(1, G - 1), ldb1);
   load_w(0, bc, sc);
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
   // three groups per trip: group g reads stage g % 3
   int g = 0;
   for (; g + 2 < G; g += 3) {
-    step(g, lds0, lds2);
-    step(g + 1, lds1, lds0);
-    step(g + 2, lds2, lds1);
+    step(g, lds0, lds2, ldb0, ldb2);
+    step(g + 1, lds1, lds0, ldb1, ldb0);
+    step(g + 2, lds2, lds1, ldb2, ldb1);
   }
-  if (g < G) step(g, lds0, lds2);
-  if (g + 1 < G) step(g + 1, lds1, lds0);
+  if (g < G) step(g, lds0, lds2, ldb0, ldb2);
+  if (g + 1 < G) step(g + 1, lds1, lds0, ldb1, ldb0);
   __builtin_amdgcn_s_waitcnt(0);                 // the idle stages' DMAs, before the workgroup ends
 
   // Epilogue: lane holds rows 8(r/4) + 4h + r%4 of column lane%32, r = 0..15.
