@@ -216,6 +216,75 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            kBufferFlags);
 }
 
+// Epilogue store of one 32 x 32 fp32 block held in the 32x32 MFMA output
+// layout (lane: column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4,
+// r = 0..15) into row-major Y (m x n, bf16 or fp32).  The block goes through
+// a per-wave LDS scratch (32 rows x 40 floats: the 8-float pad puts the two
+// lane halves' rows, 4 apart, on different banks) and leaves as 16-byte
+// pieces of rows: 2 (bf16) or 4 (fp32) stores per lane instead of 16 two-
+// or four-byte ones.  Rows >= m and columns >= n are not written.  vec: n
+// and y allow 16-byte stores (n a multiple of 8 for bf16, 4 for fp32, y
+// 16-byte aligned); otherwise element stores.  bf16 is the round to nearest
+// even of the fp32 value, as a direct store.  The scratch belongs to the
+// calling wave alone; LDS serves one wave's accesses in order, so the reads
+// see the writes once lgkmcnt is 0.
+constexpr int kEpiStride = 40;
+constexpr int kEpiScratch = 32 * kEpiStride * 4;          // bytes per wave
+
+template <bool BF16, typename V>
+__device__ __forceinline__ void store_block32(const V& v, float* scratch, void* y, int m, int n, int row0,
+                                              int col0, bool vec) {
+  const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) scratch[(8 * (r >> 2) + 4 * lh + (r & 3)) * kEpiStride + lr] = v[r];
+  __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int W = BF16 ? 8 : 4;                          // values per 16-byte piece
+  constexpr int PER_ROW = 32 / W;
+#pragma unroll
+  for (int i = 0; i < 32 * PER_ROW / 64; ++i) {
+    const int q = lane + 64 * i;
+    const int row = q / PER_ROW, c = (q % PER_ROW) * W;
+    float f[W];
+#pragma unroll
+    for (int j = 0; j < W / 4; ++j) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(scratch + row * kEpiStride + c + 4 * j);
+      f[4 * j] = t[0]; f[4 * j + 1] = t[1]; f[4 * j + 2] = t[2]; f[4 * j + 3] = t[3];
+    }
+    const int gr = row0 + row, gc = col0 + c;
+    if (gr < m) {
+      const int64_t base = (int64_t)gr * n + gc;
+      if (vec && gc + W <= n) {
+        if constexpr (BF16) {
+          __bf16 b[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = (__bf16)f[e];
+          *reinterpret_cast<u32x4*>(static_cast<__bf16*>(y) + base) = __builtin_bit_cast(u32x4, b);
+        } else {
+          f32x4 t = {f[0], f[1], f[2], f[3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base) = t;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+          if (gc + e < n) {
+            if constexpr (BF16)
+              static_cast<__bf16*>(y)[base + e] = (__bf16)f[e];
+            else
+              static_cast<float*>(y)[base + e] = f[e];
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// 16-byte stores are possible for every row of an m x n output at y.
+__device__ __forceinline__ bool epi_vec_ok(const void* y, int n, bool bf16) {
+  return ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && (n % (bf16 ? 8 : 4) == 0);
+}
+
 // Workgroup barrier that orders LDS only (waits on lgkmcnt, not vmcnt):
 // global loads and stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

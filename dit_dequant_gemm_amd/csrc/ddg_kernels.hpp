@@ -383,22 +383,18 @@ __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
     group(g + 1, I1{});
   }
 
-  // Epilogue: lane holds rows 8(r/4) + 4h + r%4 of column lane%32, r = 0..15.
-  const int col = nw0 + wave * 32 + lr;
-  if (col < args.n) {
+  // Epilogue: every wave is done with LDS (the last group's reads run past
+  // its barrier); each 32 x 32 block leaves through a 5 KB scratch per wave
+  // as 16-byte pieces of rows.
+  __syncthreads();
+  float* scratch = reinterpret_cast<float*>(lds + wave * kEpiScratch);
+  const bool vec = epi_vec_ok(args.y, args.n, args.out_bf16 != 0);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < args.m) {
-          if (args.out_bf16)
-            static_cast<__bf16*>(args.y)[(int64_t)row * args.n + col] = (__bf16)acc[rb][r];
-          else
-            static_cast<float*>(args.y)[(int64_t)row * args.n + col] = acc[rb][r];
-        }
-      }
-    }
+  for (int rb = 0; rb < RB; ++rb) {
+    if (args.out_bf16)
+      store_block32<true>(acc[rb], scratch, args.y, args.m, args.n, m0 + rb * 32, nw0 + wave * 32, vec);
+    else
+      store_block32<false>(acc[rb], scratch, args.y, args.m, args.n, m0 + rb * 32, nw0 + wave * 32, vec);
   }
 }
 

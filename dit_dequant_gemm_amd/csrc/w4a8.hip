@@ -640,33 +640,33 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   }
   if (g < G) step(g, lds0, lds2, ldb0, ldb2);
   if (g + 1 < G) step(g + 1, lds1, lds0, ldb1, ldb0);
-  __builtin_amdgcn_s_waitcnt(0);                 // the idle stages' DMAs, before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);                 // this wave's DMAs into the idle stages landed
+  __syncthreads();                               // ... every wave's, and every read is done
 
-  // Epilogue: lane holds rows 8(r/4) + 4h + r%4 of column lane%32, r = 0..15.
+  // Epilogue: each 32 x 32 block, scaled by its rows' token scales, leaves
+  // through a 5 KB LDS scratch per wave (waves 0-3 in stage 0, 4-7 in stage 1)
+  static_assert(4 * kEpiScratch <= kStage, "epilogue scratch");
+  float* scratch = reinterpret_cast<float*>((wave < 4 ? lds0 : lds1) + (wave & 3) * kEpiScratch);
+  const bool vec = epi_vec_ok(args.y, args.n, args.out_bf16 != 0);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    const int row0 = m0 + wm * 32 * RB + rb * 32;
     float xs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 32 * RB + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int row = row0 + 8 * (r >> 2) + 4 * lh + (r & 3);
       xs[r] = row < args.m ? args.xscales[row] : 0.0f;
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int col = n0 + wn * 32 * CB + cb * 32 + lr;
-      if (col < args.n) {
+      f32x16e v;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 32 * RB + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (row < args.m) {
-            const float v = acc[rb][cb][r] * xs[r];
-            if (args.out_bf16)
-              static_cast<__bf16*>(args.y)[(int64_t)row * args.n + col] = (__bf16)v;
-            else
-              static_cast<float*>(args.y)[(int64_t)row * args.n + col] = v;
-          }
-        }
-      }
+      for (int r = 0; r < 16; ++r) v[r] = acc[rb][cb][r] * xs[r];
+      const int col0 = n0 + wn * 32 * CB + cb * 32;
+      if (args.out_bf16)
+        store_block32<true>(v, scratch, args.y, args.m, args.n, row0, col0, vec);
+      else
+        store_block32<false>(v, scratch, args.y, args.m, args.n, row0, col0, vec);
     }
   }
 }
