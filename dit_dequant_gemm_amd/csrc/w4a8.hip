@@ -178,8 +178,102 @@ __device__ __forceinline__ uint32_t e4m3_code(float r) {
   return (mag != 0u && r < 0.0f) ? (mag | 0x80u) : mag;
 }
 
-// One wave per row (four rows per workgroup): the row's abs-max, then
-// r = x / s and its E4M3 code, eight codes per lane and step.
+// x / s correctly rounded without a division, by Markstein's correction
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", 1990): if y = RN(1/s) and q is within an ulp of
+// x / s, then with the residual r = x - q s (exact through the FMA),
+// RN(q + r y) = RN(x / s), barring over- and underflow.  One correction
+// brings the plain product RN(x y) within half an ulp (plus a term of
+// relative size 2^-24), the second one then rounds correctly.  The callers
+// use it for scales in [2^-60, 2^100] and |x / s| at most the format's
+// largest value: for |x| >= 2^-96 the residual stays a normal number, and
+// smaller x give quotients below 2^-36, code 0 in every format here.
+// (Checked against exact rational division on 144,000 bf16 x and random s.)
+__device__ __forceinline__ float div_markstein(float x, float s, float y) {
+  float q = x * y;
+  float r = __builtin_fmaf(-q, s, x);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-q, s, x);
+  return __builtin_fmaf(r, y, q);
+}
+__device__ __forceinline__ bool markstein_ok(float s) { return s >= 0x1p-60f && s <= 0x1p100f; }
+
+// E4M3 codes of two floats of magnitude <= 448 through the conversion
+// instruction (OCP E4M3, round to nearest even), into byte pair P of w; a
+// value that rounds to zero gets code 0 (the instruction keeps the sign).
+__device__ __forceinline__ uint32_t e4m3_zero_fix(uint32_t w) {
+  const uint32_t mag = w & 0x7F7F7F7Fu;
+  const uint32_t nz = ((mag + 0x7F7F7F7Fu) | mag) & 0x80808080u;     // bit 7 of a byte: magnitude != 0
+  return w & (0x7F7F7F7Fu | nz);
+}
+
+// E4M3 codes of eight values (one 16-byte bf16 chunk), r = x / s correctly
+// rounded (see div_markstein) and clamped to +-448.
+__device__ __forceinline__ u32x2 e4m3_chunk(u32x4 t, bool zero, bool fast, float s, float y) {
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t h = (j & 1) ? (t[j >> 1] >> 16) : (t[j >> 1] & 0xFFFFu);
+    const float v = bf16_bits_to_f32(h);
+    const float d = zero ? 0.0f : (fast ? div_markstein(v, s, y) : v / s);
+    r[j] = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  }
+  u32x2 o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w], r[4 * w + 1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w + 2], r[4 * w + 3], p, true);
+    o[w] = e4m3_zero_fix((uint32_t)p);
+  }
+  return o;
+}
+
+// One workgroup of 256 lanes per row for rows up to 2048 * NCH wide: lane i
+// reads chunks i, i + 256, ... (at most NCH of them) once, keeps them in
+// registers for the abs-max (wave butterfly, then the four waves through
+// LDS) and converts them.
+template <int NCH>
+__global__ __launch_bounds__(256) void fp8_quantize_rows_reg_kernel(const uint16_t* __restrict__ x, int k,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ sx) {
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
+  const int chunks = k / 8;
+  u32x4 t[NCH];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    t[i] = c < chunks ? src[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[i][j] & 0xFFFFu)));
+      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[i][j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+  if (lane == 0) part[wave] = a;
+  __syncthreads();
+  a = __builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3]));
+  const float s = a / 448.0f;
+  const bool zero = !(s != 0.0f);
+  const bool fast = markstein_ok(s);
+  const float y = fast ? 1.0f / s : 0.0f;
+  u32x2* dst = reinterpret_cast<u32x2*>(q + row * k);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    if (c < chunks) dst[c] = e4m3_chunk(t[i], zero, fast, s, y);
+  }
+  if (tid == 0) sx[row] = zero ? 0.0f : s;
+}
+
+// Wider rows: one wave per row (four rows per workgroup), two passes over
+// the row: the row's abs-max, then r = x / s and its E4M3 code, eight codes
+// per lane and step.
 __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                int64_t m, int k,
                                                                uint8_t* __restrict__ q,
@@ -190,6 +284,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const uint16_t* 
   const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
   const int chunks = k / 8;
   float a = 0.0f;
+#pragma unroll 4
   for (int c = lane; c < chunks; c += 64) {
     const u32x4 t = src[c];
 #pragma unroll
@@ -202,18 +297,11 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const uint16_t* 
   for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
   const float s = a / 448.0f;
   const bool zero = !(s != 0.0f);
+  const bool fast = markstein_ok(s);
+  const float y = fast ? 1.0f / s : 0.0f;
   u32x2* dst = reinterpret_cast<u32x2*>(q + row * k);
-  for (int c = lane; c < chunks; c += 64) {
-    const u32x4 t = src[c];
-    u32x2 o = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t h = (j & 1) ? (t[j >> 1] >> 16) : (t[j >> 1] & 0xFFFFu);
-      const float r = zero ? 0.0f : bf16_bits_to_f32(h) / s;
-      o[j >> 2] |= e4m3_code(r) << (8 * (j & 3));
-    }
-    dst[c] = o;
-  }
+#pragma unroll 4
+  for (int c = lane; c < chunks; c += 64) dst[c] = e4m3_chunk(src[c], zero, fast, s, y);
   if (lane == 0) sx[row] = zero ? 0.0f : s;
 }
 
@@ -223,27 +311,9 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const uint16_t* 
 template <int EB, int MB, int BIAS>
 struct Fp6Fmt {
   static constexpr float vmax = (2.0f - 1.0f / (float)(1 << MB)) * (float)(1 << ((1 << EB) - 1 - BIAS));
-  static constexpr float min_normal = 1.0f / (float)(1 << (BIAS - 1));
   static constexpr float sub_scale = (float)(1 << (BIAS - 1 + MB));    // 1 / subnormal spacing
+  static constexpr float zero_below = 0.5f / sub_scale;                  // half the smallest subnormal
 };
-
-// FP6 code of a finite float: clamp to the largest value, round to nearest
-// even (subnormals: multiples of the spacing; normals: MB mantissa bits).
-template <int EB, int MB, int BIAS>
-__device__ __forceinline__ uint32_t fp6_code(float r) {
-  using F = Fp6Fmt<EB, MB, BIAS>;
-  const float a = __builtin_fminf(__builtin_fabsf(r), F::vmax);
-  uint32_t mag;
-  if (a < F::min_normal) {
-    mag = (uint32_t)__builtin_rintf(a * F::sub_scale);
-  } else {
-    constexpr int sh = 23 - MB;
-    uint32_t b = __builtin_bit_cast(uint32_t, a);
-    b += ((1u << (sh - 1)) - 1u) + ((b >> sh) & 1u);
-    mag = ((((b >> 23) - 127u + BIAS) & ((1u << EB) - 1u)) << MB) | ((b >> sh) & ((1u << MB) - 1u));
-  }
-  return (mag != 0u && r < 0.0f) ? (mag | 32u) : mag;
-}
 
 // Tiled 6-bit storage: rows in blocks of 32 (padded with zero codes); the 32
 // codes of (row, group g, 64-wide step s, half h) -- k = 128 g + 64 s + 32 h
@@ -254,63 +324,106 @@ __device__ __forceinline__ uint32_t fp6_code(float r) {
 // 8-byte reads that 32 lanes take from 256 contiguous bytes.
 constexpr int kX6Record = 3072;
 
-// One wave per row (four rows per workgroup), rows up to m_pad (padding rows
-// get zero codes and no scale): the row's abs-max, then s = amax / vmax and,
-// per 32-value unit, the codes, packed and stored as three pieces.
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6v __attribute__((ext_vector_type(6)));
+
+// The three 8-byte pieces of one 32-value unit (bf16 values in t) at rec.
+// r = x / s (correctly rounded) goes through the packed FP6 conversion
+// instruction (unit scale; round to nearest even, saturating at the largest
+// value), which packs its two 16-value operands interleaved (output j from
+// operand j % 2, element j / 2): even values in the first, odd in the
+// second give code j at bits 6 j.  Values that round to zero are set to +0
+// first (the instruction keeps the sign of zero).
 template <int EB, int MB, int BIAS>
-__global__ __launch_bounds__(256) void fp6_quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
-                                                               int64_t m_pad, int k, uint8_t* __restrict__ q,
-                                                               float* __restrict__ sx) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= m_pad) return;
+__device__ __forceinline__ void fp6_unit(const u32x4 (&t)[4], bool zero, bool fast, float s, float y,
+                                         uint8_t* rec, int un) {
+  f32x16v ev, od;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * i + e;
+      const uint32_t h = (e & 1) ? (t[i][e >> 1] >> 16) : (t[i][e >> 1] & 0xFFFFu);
+      const float v = bf16_bits_to_f32(h);
+      float r = zero ? 0.0f : (fast ? div_markstein(v, s, y) : v / s);
+      r = __builtin_fabsf(r) <= Fp6Fmt<EB, MB, BIAS>::zero_below ? 0.0f : r;
+      if (j & 1) od[j >> 1] = r; else ev[j >> 1] = r;
+    }
+  }
+  u32x6v w;
+  if constexpr (EB == 2)
+    w = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f));
+  else
+    w = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f));
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const u32x2 piece = {w[2 * u], w[2 * u + 1]};
+    *reinterpret_cast<u32x2*>(rec + (un >> 2) * kX6Record + ((un & 3) * 3 + u) * 256) = piece;
+  }
+}
+
+// Sixteen rows per workgroup of 16 waves (rows up to m_pad; padding rows
+// get zero codes and no scale).  The storage interleaves 32 rows at 8-byte
+// granularity, so the unit of work that writes whole cache lines is one
+// 32-value unit of 16 consecutive rows (128 bytes per piece).  Pass 1: wave w
+// reads row w (coalesced) for its abs-max and scale and, for rows of up to
+// kRow6Lds values, parks it in LDS.  Pass 2: lane t converts unit t / 16
+// (+ 64 j) of row t % 16 -- from LDS, or for wider rows again from memory
+// (the rows were just read) -- and stores its pieces.
+constexpr int kRow6Lds = 4096;
+template <int EB, int MB, int BIAS, bool IN_LDS>
+__global__ __launch_bounds__(1024) void fp6_quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t m, int k,
+                                                                uint8_t* __restrict__ q, float* __restrict__ sx) {
+  __shared__ float srow[16], yrow[16];
+  __shared__ __attribute__((aligned(16))) uint16_t buf[IN_LDS ? 16 : 1][IN_LDS ? kRow6Lds + 8 : 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int G = k / 128, units = k / 32;
-  uint8_t* rec = q + (row >> 5) * (int64_t)G * kX6Record + (row & 31) * 8;
-  if (row >= m) {
-    const u32x2 z = {0u, 0u};
-    for (int un = lane; un < units; un += 64)
+  {
+    const int64_t row = row0 + wave;
+    float a = 0.0f;
+    if (row < m) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
+#pragma unroll 4
+      for (int c = lane; c < k / 8; c += 64) {
+        const u32x4 t = src[c];
+        if constexpr (IN_LDS) *reinterpret_cast<u32x4*>(&buf[wave][c * 8]) = t;
 #pragma unroll
-      for (int u = 0; u < 3; ++u)
-        *reinterpret_cast<u32x2*>(rec + (un >> 2) * kX6Record + ((un & 3) * 3 + u) * 256) = z;
-    return;
-  }
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
-  float a = 0.0f;
-  for (int c = lane; c < k / 8; c += 64) {
-    const u32x4 t = src[c];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] & 0xFFFFu)));
-      a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] >> 16)));
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
-  const float s = a / Fp6Fmt<EB, MB, BIAS>::vmax;
-  const bool zero = !(s != 0.0f);
-  for (int un = lane; un < units; un += 64) {
-    uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 t = src[un * 4 + i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * i + e;
-        const uint32_t h = (e & 1) ? (t[e >> 1] >> 16) : (t[e >> 1] & 0xFFFFu);
-        const float r = zero ? 0.0f : bf16_bits_to_f32(h) / s;
-        const uint32_t c = fp6_code<EB, MB, BIAS>(r);
-        const int bit = 6 * j;
-        w[bit >> 5] |= c << (bit & 31);
-        if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+        for (int j = 0; j < 4; ++j) {
+          a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] & 0xFFFFu)));
+          a = __builtin_fmaxf(a, __builtin_fabsf(bf16_bits_to_f32(t[j] >> 16)));
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const u32x2 piece = {w[2 * u], w[2 * u + 1]};
-      *reinterpret_cast<u32x2*>(rec + (un >> 2) * kX6Record + ((un & 3) * 3 + u) * 256) = piece;
+      for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+    } else if constexpr (IN_LDS) {
+      for (int c = lane; c < k / 8; c += 64) *reinterpret_cast<u32x4*>(&buf[wave][c * 8]) = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (lane == 0) {
+      const float sc = a / Fp6Fmt<EB, MB, BIAS>::vmax;
+      srow[wave] = sc;
+      yrow[wave] = markstein_ok(sc) ? 1.0f / sc : 0.0f;
+      if (row < m) sx[row] = sc;
     }
   }
-  if (lane == 0) sx[row] = zero ? 0.0f : s;
+  __syncthreads();
+  const int r = tid & 15;
+  const float s = srow[r], y = yrow[r];
+  const bool zero = !(s != 0.0f), fast = markstein_ok(s);
+  const int64_t row = row0 + r;
+  uint8_t* rec = q + (row >> 5) * (int64_t)G * kX6Record + (row & 31) * 8;
+  for (int un = tid >> 4; un < units; un += 64) {
+    u32x4 t[4];
+    if constexpr (IN_LDS) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t[c] = *reinterpret_cast<const u32x4*>(&buf[r][un * 32 + c * 8]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        t[c] = row < m ? *reinterpret_cast<const u32x4*>(x + row * k + un * 32 + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    fp6_unit<EB, MB, BIAS>(t, zero, fast, s, y, rec, un);
+  }
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -738,11 +851,17 @@ hipError_t launch_fp4_quantize_pack(const void* w, bool f32_in, int64_t n, int k
 hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt6, uint8_t* q, float* sx,
                                     hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  const int64_t m_pad = (m + 31) / 32 * 32;
-  const dim3 grid((unsigned)((m_pad + 3) / 4)), block(256);
-  if (fmt6 == kFp6E2M3) fp6_quantize_rows_kernel<2, 3, 1><<<grid, block, 0, stream>>>(x, m, m_pad, k, q, sx);
-  else if (fmt6 == kFp6E3M2) fp6_quantize_rows_kernel<3, 2, 3><<<grid, block, 0, stream>>>(x, m, m_pad, k, q, sx);
-  else return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((m + 31) / 32 * 2)), block(1024);    // 16 rows each, up to the padded count
+  const bool lds = k <= kRow6Lds;
+  if (fmt6 == kFp6E2M3) {
+    if (lds) fp6_quantize_rows_kernel<2, 3, 1, true><<<grid, block, 0, stream>>>(x, m, k, q, sx);
+    else fp6_quantize_rows_kernel<2, 3, 1, false><<<grid, block, 0, stream>>>(x, m, k, q, sx);
+  } else if (fmt6 == kFp6E3M2) {
+    if (lds) fp6_quantize_rows_kernel<3, 2, 3, true><<<grid, block, 0, stream>>>(x, m, k, q, sx);
+    else fp6_quantize_rows_kernel<3, 2, 3, false><<<grid, block, 0, stream>>>(x, m, k, q, sx);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -759,7 +878,18 @@ hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t 
 hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t* q, float* sx,
                                     hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  fp8_quantize_rows_kernel<<<dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream>>>(x, m, k, q, sx);
+  const int nch = (k / 8 + 255) / 256;                 // chunks per lane with one workgroup per row
+  const dim3 rows((unsigned)m), block(256);
+  switch (nch) {
+    case 1: fp8_quantize_rows_reg_kernel<1><<<rows, block, 0, stream>>>(x, k, q, sx); break;
+    case 2: fp8_quantize_rows_reg_kernel<2><<<rows, block, 0, stream>>>(x, k, q, sx); break;
+    case 3: fp8_quantize_rows_reg_kernel<3><<<rows, block, 0, stream>>>(x, k, q, sx); break;
+    case 4: fp8_quantize_rows_reg_kernel<4><<<rows, block, 0, stream>>>(x, k, q, sx); break;
+    case 5: case 6: case 7: case 8:
+      fp8_quantize_rows_reg_kernel<8><<<rows, block, 0, stream>>>(x, k, q, sx); break;
+    default:
+      fp8_quantize_rows_kernel<<<dim3((unsigned)((m + 3) / 4)), dim3(256), 0, stream>>>(x, m, k, q, sx);
+  }
   return hipGetLastError();
 }
 

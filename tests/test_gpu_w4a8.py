@@ -62,7 +62,7 @@ def test_fp4_quantize_ties_zero_and_tiny_groups(gpu_lib, fmt):
     assert np.array_equal(host(qw.scales).view(np.uint32), s.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (64, 3072), (3, 13824)])
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (64, 3072), (3, 13824), (2, 20480)])
 def test_fp8_rows_bit_exact(gpu_lib, m, k):
     _case(f"fp8_quantize_rows m={m} k={k}")
     x = synth.to_bf16(np.random.default_rng(m + k).normal(0, 1, size=(m, k)))
@@ -255,7 +255,7 @@ def test_w4a8_tiled_chain_attention_projection_sampled(gpu_lib):
 # ---- W4A6: 6-bit activations ----
 
 @pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
-@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (33, 256), (100, 3072), (64, 13824)])
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (33, 256), (100, 3072), (64, 13824), (3, 20480)])
 def test_fp6_rows_bit_exact(gpu_lib, fmt, m, k):
     _case(f"fp6_quantize_rows {fmt} m={m} k={k}")
     x = synth.to_bf16(np.random.default_rng(m * 3 + k).normal(0, 1, size=(m, k)))
@@ -328,3 +328,25 @@ def test_w4a6_chain_attention_projection_sampled(gpu_lib, afmt):
     _check_w4a6_f32(y[rows], xc, xsc, wc, ws, F.w4a6_ref(xc, xsc, wc, ws, "e2m1", afmt), afmt)
     empty = gpu_lib.w4a6_gemm(xq[:0], xs[:0], afmt, qw, torch.float32)
     assert empty.shape == (0, 3072)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3"] + list(F.FP6_FORMATS))
+def test_rows_quantizers_extreme_scales(gpu_lib, fmt):
+    """Rows whose scale falls below 2^-60 (the quantizers' exact-division
+    path), just above it (the multiply-and-correct path with the tiniest
+    elements), and far above 1: bit for bit against the oracle."""
+    _case(f"row quantizer {fmt}: extreme row scales")
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 1, size=(6, 384))
+    for r, e in enumerate((-80, -68, -52, -40, 40, 100)):
+        x[r] *= 2.0 ** e
+    x = synth.to_bf16(x)
+    if fmt == "e4m3":
+        xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(x))
+        cq, cs = F.quantize_rows_e4m3(x)
+        assert np.array_equal(host(xq), cq)
+    else:
+        xq, xs = gpu_lib.fp6_quantize_rows(dev_bf16(x), fmt)
+        cq, cs = F.quantize_rows_fp6(x, fmt)
+        assert np.array_equal(host(xq), F.pack_fp6_tiled(cq))
+    assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
