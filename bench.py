@@ -426,11 +426,12 @@ def rotate_suite(args):
 
 
 def w4a8_suite(args):
-    """FP4 (E2M1) weights x per-token FP8 (E4M3) activations at the attention
-    projection (4096 x 3072 x 3072): the activation quantizer against HBM, the
-    product against the dense FP8 matrix peak, the 4-bit bf16 product beside
-    it, and each path's error against the float32 product of the unquantized
-    weight."""
+    """FP4 (E2M1) weights x per-token FP8 (E4M3) or FP6 (E2M3, E3M2)
+    activations at the attention projection (4096 x 3072 x 3072): the
+    activation quantizers against HBM, the products (row and tiled weight
+    storage, float32 and power-of-two scales) against the dense matrix peaks,
+    the 4-bit bf16 product beside them, and each path's error against the
+    float32 product of the unquantized weight."""
     import torch
 
     from dit_dequant_gemm_amd import api, synth
