@@ -22,9 +22,10 @@ namespace ddg {
 // ---------------------------------------------------------------------------
 // K1: quantize + pack.  One lane per 32-weight chunk; the 4 lanes of a group
 // are adjacent, so the group abs-max is a 2-step butterfly inside the quad.
-// IEEE float32 throughout: correctly rounded multiply and divide, round half
-// to even, no fused operations (the file is compiled with -ffp-contract=off),
-// subnormals kept.
+// IEEE float32 throughout: correctly rounded multiply and divide (w / step by
+// Markstein's correction, see div_markstein), round half to even, no other
+// fused operations (the file is compiled with -ffp-contract=off), subnormals
+// kept.
 // ---------------------------------------------------------------------------
 template <int B, bool F32_IN>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(const void* __restrict__ w,
@@ -67,13 +68,18 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const void* __restri
   const float step = (2.0f * a1) / (float)((1 << B) - 1);
   const bool zero_group = !(step != 0.0f);
   constexpr float nh = (float)Bits<B>::n_half;
+  const bool fast = markstein_ok(step);
+  float r[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r[i] = v[i];
+  quotients<32>(r, zero_group, fast, step, fast ? 1.0f / step : 0.0f);
 
   uint32_t out[B];
   uint64_t acc = 0;
   int nbits = 0, wo = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    float q = __builtin_rintf(v[i] / step);
+    float q = __builtin_rintf(r[i]);
     q = __builtin_fminf(__builtin_fmaxf(q, -nh), nh);
     const uint32_t u = zero_group ? (uint32_t)Bits<B>::n_half
                                   : (uint32_t)((int)q + Bits<B>::n_half);

@@ -70,10 +70,15 @@ __global__ __launch_bounds__(256) void quant_sse_kernel(const void* __restrict__
         constexpr float nh = (float)Bits<B>::n_half;
         const float step = (2.0f * a1) / (float)((1 << B) - 1);
         const bool zero_group = !(step != 0.0f);
+        const bool fast = markstein_ok(step);
+        float r[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) r[i] = v[i];
+        quotients<32>(r, zero_group, fast, step, fast ? 1.0f / step : 0.0f);
         double s = 0.0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          float q = __builtin_rintf(v[i] / step);
+          float q = __builtin_rintf(r[i]);
           q = __builtin_fminf(__builtin_fmaxf(q, -nh), nh);
           const float wh = zero_group ? 0.0f : q * step;
           const double d = (double)v[i] - (double)wh;

@@ -178,25 +178,7 @@ __device__ __forceinline__ uint32_t e4m3_code(float r) {
   return (mag != 0u && r < 0.0f) ? (mag | 0x80u) : mag;
 }
 
-// x / s correctly rounded without a division, by Markstein's correction
-// (P. Markstein, "Computation of elementary functions on the IBM RISC
-// System/6000 processor", 1990): if y = RN(1/s) and q is within an ulp of
-// x / s, then with the residual r = x - q s (exact through the FMA),
-// RN(q + r y) = RN(x / s), barring over- and underflow.  One correction
-// brings the plain product RN(x y) within half an ulp (plus a term of
-// relative size 2^-24), the second one then rounds correctly.  The callers
-// use it for scales in [2^-60, 2^100] and |x / s| at most the format's
-// largest value: for |x| >= 2^-96 the residual stays a normal number, and
-// smaller x give quotients below 2^-36, code 0 in every format here.
-// (Checked against exact rational division on 144,000 bf16 x and random s.)
-__device__ __forceinline__ float div_markstein(float x, float s, float y) {
-  float q = x * y;
-  float r = __builtin_fmaf(-q, s, x);
-  q = __builtin_fmaf(r, y, q);
-  r = __builtin_fmaf(-q, s, x);
-  return __builtin_fmaf(r, y, q);
-}
-__device__ __forceinline__ bool markstein_ok(float s) { return s >= 0x1p-60f && s <= 0x1p100f; }
+
 
 // E4M3 codes of two floats of magnitude <= 448 through the conversion
 // instruction (OCP E4M3, round to nearest even), into byte pair P of w; a
@@ -212,12 +194,10 @@ __device__ __forceinline__ uint32_t e4m3_zero_fix(uint32_t w) {
 __device__ __forceinline__ u32x2 e4m3_chunk(u32x4 t, bool zero, bool fast, float s, float y) {
   float r[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t h = (j & 1) ? (t[j >> 1] >> 16) : (t[j >> 1] & 0xFFFFu);
-    const float v = bf16_bits_to_f32(h);
-    const float d = zero ? 0.0f : (fast ? div_markstein(v, s, y) : v / s);
-    r[j] = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
-  }
+  for (int j = 0; j < 8; ++j) r[j] = bf16_bits_to_f32((j & 1) ? (t[j >> 1] >> 16) : (t[j >> 1] & 0xFFFFu));
+  quotients<8>(r, zero, fast, s, y);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = __builtin_fminf(__builtin_fmaxf(r[j], -448.0f), 448.0f);
   u32x2 o;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
@@ -337,18 +317,17 @@ typedef uint32_t u32x6v __attribute__((ext_vector_type(6)));
 template <int EB, int MB, int BIAS>
 __device__ __forceinline__ void fp6_unit(const u32x4 (&t)[4], bool zero, bool fast, float s, float y,
                                          uint8_t* rec, int un) {
+  float r[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[8 * i + e] = bf16_bits_to_f32((e & 1) ? (t[i][e >> 1] >> 16) : (t[i][e >> 1] & 0xFFFFu));
+  quotients<32>(r, zero, fast, s, y);
   f32x16v ev, od;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * i + e;
-      const uint32_t h = (e & 1) ? (t[i][e >> 1] >> 16) : (t[i][e >> 1] & 0xFFFFu);
-      const float v = bf16_bits_to_f32(h);
-      float r = zero ? 0.0f : (fast ? div_markstein(v, s, y) : v / s);
-      r = __builtin_fabsf(r) <= Fp6Fmt<EB, MB, BIAS>::zero_below ? 0.0f : r;
-      if (j & 1) od[j >> 1] = r; else ev[j >> 1] = r;
-    }
+  for (int j = 0; j < 32; ++j) {
+    const float v = __builtin_fabsf(r[j]) <= Fp6Fmt<EB, MB, BIAS>::zero_below ? 0.0f : r[j];
+    if (j & 1) od[j >> 1] = v; else ev[j >> 1] = v;
   }
   u32x6v w;
   if constexpr (EB == 2)
