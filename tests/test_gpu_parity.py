@@ -126,12 +126,11 @@ def test_gemm_ragged_shapes(gpu_lib, bits, m):
 # M <= 16 with a wide output (N >= 12800) runs the weight-streaming kernel:
 # K from one group (7 of 8 K-split waves idle) to 108 groups (several chunks
 # per wave, a short last chunk), N with a partial last workgroup, M < 16.
-@pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("m,n,k", [(16, 12800, 128), (1, 12816, 640), (7, 12816, 3328),
-                                   (16, 12864, 5120), (16, 12816, 13824)])
+# (the 108-group case runs at the narrowest and widest code only)
+@pytest.mark.parametrize("bits,m,n,k", [(b, m, n, k) for (m, n, k) in [(16, 12800, 128), (1, 12816, 640),
+                                                                       (7, 12816, 3328), (16, 12864, 5120)]
+                                        for b in BITS] + [(3, 16, 12816, 13824), (7, 16, 12816, 13824)])
 def test_gemm_wide_small_m(gpu_lib, bits, m, n, k):
-    if k == 13824 and bits not in (3, 7):
-        pytest.skip("the 108-group case runs at the narrowest and widest code")
     _case(f"dequant_gemm wide small-M m={m} n={n} k={k} bits={bits}")
     c = synth.random_case(m * 131 + n + k + bits, m, n, k)
     qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
