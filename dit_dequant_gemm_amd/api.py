@@ -108,7 +108,16 @@ def _check(status: int, where: str) -> None:
         raise DDGError(status, where)
 
 
+# The raw handle of torch's current stream, without building a Stream object
+# (that costs several microseconds per call, more than a 16-token product
+# takes on the GPU).
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(device: torch.device) -> int:
+    if _RAW_STREAM is not None:
+        idx = device.index
+        return _RAW_STREAM(torch.cuda.current_device() if idx is None else idx)
     return torch.cuda.current_stream(device).cuda_stream
 
 

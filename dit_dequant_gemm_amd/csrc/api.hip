@@ -113,7 +113,7 @@ int skinny_chunk(int g) {
 }
 
 // Kernel choice for the product; fills a.tiles_* for the large kernel.
-hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t stream) {
+hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream) {
   if (a.m <= 16) {
     // Wide outputs (at least 200 workgroups of 64 columns): the
     // weight-streaming kernel with an 8-way K split and X in registers.  Below
@@ -134,16 +134,15 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, int cus, hipStream_t strea
   }
   if (a.m <= 64) {
     const int rb = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
-    // Column waves x K-split waves per workgroup, from timings of the
-    // 16-token products: four column waves where that still leaves about 200+
-    // workgroups (wide outputs), two where 128+ remain, else one column wave
-    // and an 8-way K split.
+    // Column waves x K-split waves per workgroup, from timings of the 16-,
+    // 32- and 64-token products: four column waves where that still leaves
+    // about 200+ workgroups (wide outputs; 16 tokens), two where 128+ remain,
+    // else one column wave and an 8-way (16 tokens) or 4-way K split.
     const int64_t nb = ((int64_t)a.n + 15) / 16;
     int nc = 1, nk = rb == 1 ? 8 : 4;
-    if (rb == 1) {
-      if (nb / 4 >= 200) { nc = 4; nk = 2; }
-      else if (nb / 2 >= 128) { nc = 2; nk = 2; }
-    } else if ((nb + 1) / 2 >= cus) {
+    if (rb == 1 && nb / 4 >= 200) {
+      nc = 4; nk = 2;
+    } else if (nb / 2 >= 128) {
       nc = 2; nk = 2;
     }
     return by_bits<SmallF>(bits, a, rb, nc, nk, stream);
@@ -224,7 +223,7 @@ int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
   a.lora_up = nullptr;
   a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = 0;
   a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(launch_product(a, bits, cus, stream));
+  return hip_status(launch_product(a, bits, stream));
 }
 
 int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream) {
@@ -263,7 +262,7 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
       small[n_small++] = i;
     } else {
       ddg::GemmArgs a = args_of(descs[i]);
-      if (hipError_t e = launch_product(a, descs[i].bits, cus, stream)) return hip_status(e);
+      if (hipError_t e = launch_product(a, descs[i].bits, stream)) return hip_status(e);
     }
   }
   std::stable_sort(small, small + n_small, [&](int p, int q) {
@@ -324,7 +323,7 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
   a.lora_up = static_cast<const __bf16*>(lora_up);
   a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = r;
   a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(launch_product(a, bits, cus, stream));
+  return hip_status(launch_product(a, bits, stream));
 }
 
 int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,

@@ -427,9 +427,14 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
   // for the X of step j never waits for a later step's packed weights.
   constexpr int XSLOT = RB * 16 * 256;        // one group's X slice: 16*RB rows x 256 bytes
   constexpr int RED_BYTES = (NK > 1 ? NK - 1 : 1) * NC * RB * 64 * 16;
-  // ring slots: up to 6, as many as fit in the 160 KB of LDS
+  // Ring slots: 3 with a two-way K split, else 2 (both within the 160 KB of
+  // LDS).  Deeper rings measured slower on the 16- to 64-token products
+  // (16 x 3072 x 3072: 5.1 us with 2 slots, 5.6 with 4): they hold more LDS
+  // per workgroup, and near the end of a K range they fetch clamped groups
+  // that are never used.
   constexpr int S_FIT = (160 * 1024 - RED_BYTES) / (NK * XSLOT);
-  constexpr int S = S_FIT > 6 ? 6 : S_FIT;
+  constexpr int S_WANT = NK <= 2 ? 3 : 2;
+  constexpr int S = S_FIT > S_WANT ? S_WANT : S_FIT;
   static_assert(S >= 2, "X ring needs two slots");
   constexpr int D = S - 1;                    // steps in flight
   constexpr int DMA_SLOT = XSLOT / 1024;      // 1 KB DMA instructions per slice
@@ -439,7 +444,6 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
   // issued after X(j) (at step j - D): W(j), then D - 1 steps of X + W
   constexpr int VM_AHEAD = NWL + (D - 1) * (ND + NWL);
   static_assert(VM_AHEAD < 64, "vmcnt field");
-  constexpr int WAIT_IMM = (VM_AHEAD & 15) | ((VM_AHEAD >> 4) << 14) | (7 << 4) | (15 << 8);
   // One LDS array per ring slot: the compiler can then see that a DMA into
   // one slot does not alias reads of another, and does not make the reads
   // wait for it.
@@ -516,12 +520,14 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
     for (int rb = 0; rb < RB; ++rb) acc4[s][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const uint8_t* base, int ws) {
-    uint32_t be[B];
-    byteswap_chunk<B>(raw[ws], be);
-    const float ns64 = -64.0f * sc[ws];
+    // plus-one dequantization (see dequant8_p1)
+    uint32_t be1[B];
+    if constexpr (B != 4) plus_one_words<B>(raw[ws], be1);
+    const float nsh = -(float)(1 << (B - 1)) * sc[ws];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 bf = dequant8<B>(raw[ws], be, s, sc[ws], ns64);
+      const uint32_t x1 = B == 4 ? raw[ws][s] + 0x11111111u : 0u;
+      const bf16x8 bf = dequant8_p1<B>(be1, x1, s, sc[ws], nsh);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + rb * 4096 + aoff[s]);
@@ -532,36 +538,54 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
 
   // Step j (ring slot j % S for both rings): wait for X(j), barrier, issue
   // X(j+D) and W(j+D) into slot (j-1) % S, compute step j.
+  //
+  // The wait leaves in flight exactly the loads issued after X(j): W(j), then
+  // X and W of every later step issued so far.  In the main loop that is D - 1
+  // steps; at tail step U (which issues nothing: its loads would be for steps
+  // past the end) it is D - 1 - U.  The count must be exact, not an upper
+  // bound: with fewer loads in flight than it allows, the wait would pass with
+  // this wave's share of X(j) still landing, and the barrier would hand the
+  // slot to the other column waves too early.  (A tail that issued loads would
+  // break it: their registers are never read, so the compiler drops the weight
+  // loads and keeps only the DMAs.)
   using std::integral_constant;
-  auto step = [&]<int U>(integral_constant<int, U>, int j) {
+  constexpr auto vm_imm = [](int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); };
+  auto step = [&]<int U, bool TAIL>(integral_constant<int, U>, std::bool_constant<TAIL>, int j) {
     // own X DMA of step j landed; then every wave's has, and every wave is
     // done with slot (j-1) % S.  A bare s_barrier: a fenced barrier would
     // also wait for the loads of later steps still in flight.
-    __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    constexpr int AHEAD = TAIL ? NWL + (D - 1 - U) * (ND + NWL) : VM_AHEAD;
+    static_assert(AHEAD >= NWL && AHEAD < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(vm_imm(AHEAD));
     asm volatile("s_barrier" ::: "memory");
-    issue_x(xslot(integral_constant<int, (U + D) % S>{}), j + D);
-    load_w((U + D) % S, j + D);
+    if constexpr (!TAIL) {
+      issue_x(xslot(integral_constant<int, (U + D) % S>{}), j + D);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w((U + D) % S, j + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (j < cnt) compute(xslot(integral_constant<int, U % S>{}), U % S);
   };
   // prologue: steps 0..D-1, X then W per step (the order of the steady state)
   [&]<int... J>(std::integer_sequence<int, J...>) {
-    // (sched_barrier: the scheduler would otherwise sink the scale loads to
-    // the end, and the wait counts merged at the loop head would follow them)
-    ((issue_x(xslot(integral_constant<int, J>{}), J), load_w(J, J),
-      __builtin_amdgcn_sched_barrier(0)), ...);
+    // (sched_barrier on both sides of the weight loads: the scheduler would
+    // otherwise move them among or ahead of the X DMAs, or sink the scale
+    // loads to the end, and the counted waits above assume this order)
+    ((issue_x(xslot(integral_constant<int, J>{}), J), __builtin_amdgcn_sched_barrier(0),
+      load_w(J, J), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
   // main loop: whole blocks of S steps, every load unconditional (so the
-  // compiler's wait counts stay exact across the loop)
+  // compiler's wait counts stay exact across the loop, and no load is dead)
   const int full = steps / S * S;
   for (int j0 = 0; j0 < full; j0 += S) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
-      (step(integral_constant<int, U>{}, j0 + U), ...);
+      (step(integral_constant<int, U>{}, std::false_type{}, j0 + U), ...);
     }(std::make_integer_sequence<int, S>{});
   }
-  // tail: the remaining steps (fewer than S)
+  // tail: the remaining steps (at most S - 1 = D)
   [&]<int... U>(std::integer_sequence<int, U...>) {
-    ([&] { if (full + U < steps) step(integral_constant<int, U>{}, full + U); }(), ...);
-  }(std::make_integer_sequence<int, S>{});
+    ([&] { if (full + U < steps) step(integral_constant<int, U>{}, std::true_type{}, full + U); }(), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
   __syncthreads();
 
   f32x4 acc[RB];

@@ -21,7 +21,9 @@
  *       a = max |w| over the group;  step = (2 * fl(a * 1.01f)) / (2^bits - 1);
  *       q = clamp(round_half_even(fl(w / step)), -n_half, n_half),
  *       n_half = 2^(bits-1) - 1;  code q_u = q + n_half in [0, 2^bits - 2];
- *       scale = step.  An all-zero group gets q = 0 and scale 0.
+ *       scale = step.  An all-zero group gets q = 0 and scale 0.  The
+ *       products rely on that code range: a record holding the all-ones code
+ *       2^bits - 1 (which the quantizer never writes) gives undefined outputs.
  *   - Packed layout ([WDQ] §3.3): the row-major codes form one continuous
  *     bitstream, each code written with `bits` bits, most significant bit
  *     first; stream bit 0 is the MSB of byte 0.  A row takes K*bits/8 bytes,

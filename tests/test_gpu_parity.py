@@ -7,6 +7,8 @@ Full-size workloads compare sampled rows that the oracle computes one by one
 (first rows, random rows, the ragged last rows); small shapes compare every
 element.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -136,6 +138,34 @@ def test_gemm_wide_small_m(gpu_lib, bits, m, n, k):
     qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
     y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], bits))
     xd = dev_bf16(c["x"])
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32)), y_ref, False, "f32")
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
+
+
+# The small-M kernel's launch shapes (column waves x K-split waves): (1, 8) at
+# M <= 16 and (1, 4) above for narrow outputs, (2, 2) from 4096 columns.  Each
+# K is chosen so that the K ranges end part-way through the ring of X slots:
+# 2560 (20 groups: 3 steps with an 8-way split, 5 with a 4-way one, ring of
+# 2), 1280 (10 groups: 5 steps, ring of 3) and 512 (4 groups: 2 steps, shorter
+# than the ring, so only the prologue issues loads).  Ragged M included.
+_SMALL_SHAPES = [(3072, 2560), (5120, 1280), (4096, 512)]
+
+
+@functools.lru_cache(maxsize=None)
+def _small_shape_case(n, k, bits):
+    c = synth.random_case(n + k + bits, 64, n, k)
+    return c["x"], c["w"], _oracle_w16(c["w"], bits)
+
+
+@pytest.mark.parametrize("bits", (3, 4, 7))
+@pytest.mark.parametrize("n,k", _SMALL_SHAPES)
+@pytest.mark.parametrize("m", [16, 23, 32, 50, 64])
+def test_gemm_small_m_launch_shapes(gpu_lib, m, n, k, bits):
+    _case(f"dequant_gemm small-M launch shape m={m} n={n} k={k} bits={bits}")
+    x, w, w16 = _small_shape_case(n, k, bits)
+    qw = gpu_lib.quantize_pack(dev_bf16(w), bits)
+    xd = dev_bf16(np.ascontiguousarray(x[:m]))
+    y_ref = O.gemm_ref(x[:m], w16)
     check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.float32)), y_ref, False, "f32")
     check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
 
