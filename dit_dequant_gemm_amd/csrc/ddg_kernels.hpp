@@ -417,8 +417,9 @@ __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
 //     ring; the X slice and the weights of step j + D are issued together at
 //     step j.
 //   * the NK partial tiles of a column block are summed through LDS.
-// Ring slots are static (the step loop is unrolled by the ring size); group
-// indices past a wave's range are clamped, loaded and never used.
+// Ring slots are static (the step loop is unrolled by the ring size).  In the
+// main loop, group indices past a wave's range are clamped, loaded and never
+// used; the last steps (the tail) issue nothing.
 // ---------------------------------------------------------------------------
 template <int B, int RB, int NC, int NK>
 __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args) {
