@@ -533,6 +533,70 @@ def w4a8_suite(args):
     }), flush=True)
 
 
+def _sysfs_clock_power():
+    """Current shader clock (MHz: the starred line of the DPM table) and board
+    power with its cap (W) from the amdgpu sysfs files; None where missing."""
+    import glob
+    mhz = power = cap = None
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    line = line.strip()
+                    if line.endswith("*") and ":" in line:
+                        v = line.split(":", 1)[1].rstrip("*").strip().lower().replace("mhz", "")
+                        mhz = max(mhz or 0, int(float(v)))
+        except (OSError, ValueError):
+            pass
+    for name in ("power1_input", "power1_cap"):
+        for path in glob.glob(f"/sys/class/drm/card*/device/hwmon/hwmon*/{name}"):
+            try:
+                with open(path) as fh:
+                    w = int(fh.read().strip()) / 1e6
+            except (OSError, ValueError):
+                continue
+            if name == "power1_input":
+                power = max(power or 0.0, w)
+            else:
+                cap = max(cap or 0.0, w)
+    return mhz, power, cap
+
+
+def sample_under_load(torch, fn, seconds=0.3):
+    """Median shader clock and board power read from sysfs by a thread while
+    fn(i) runs back to back for about `seconds` (outside the timed region)."""
+    import threading
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append(_sysfs_clock_power())
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    stream = torch.cuda.current_stream()
+    i = 0
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        stream.synchronize()
+    stop.set()
+    th.join()
+    import statistics
+    med = lambda vals: float(statistics.median(vals)) if vals else None
+    mhz = [m for m, _, _ in samples if m]
+    pw = [p for _, p, _ in samples if p]
+    caps = [c for _, _, c in samples if c]
+    return {"launches": i, "samples": len(samples),
+            "gfx_clock_mhz_median": med(mhz),
+            "board_power_w_median": None if not pw else round(med(pw), 1),
+            "power_cap_w": None if not caps else round(max(caps), 1)}
+
+
 def system_info(torch):
     """GPU name, clock and ROCm build; host CPU model."""
     info = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
@@ -725,6 +789,12 @@ def main():
     gbps_q = (w_bytes + p_bytes + s_bytes) / (t_q * 1e-3) / 1e9
 
     traffic = measured_traffic(args.traffic)
+    # shader clock and board power during a burst of the 4096-token product
+    # (sysfs, read by a thread; not part of any timed figure)
+    try:
+        under_load = sample_under_load(torch, gemm_big)
+    except Exception as e:                              # pragma: no cover
+        under_load = {"error": repr(e)[:200]}
 
     out = {
         "metric": "dequant-GEMM TFLOP/s (M=4096) + packed-weight GB/s (M=16), % of roofline",
@@ -752,6 +822,7 @@ def main():
                                              ("dequant_gemm_m16", "s"))},
         "context_torch_matmul_bf16_dense_TFLOPs": round(flops / (t_dense * 1e-3) / 1e12, 1),
         "system": system_info(torch),
+        "clock_power_under_load": dict(under_load, kernel="dequant_gemm_m4096"),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "m16_packed_weight_GBps": round(gbps_small, 2),
         "m16_frac_of_hbm_peak": round(gbps_small / PEAK_HBM_GBPS, 4),
