@@ -24,6 +24,7 @@ sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --suite block16     (the four linears of a DiT block at M=16)
+    python bench.py --suite block --tokens 1024   (the same at M > 64, one by one and grouped)
 """
 from __future__ import annotations
 
@@ -57,7 +58,9 @@ def parse():
                                                       "dequant_gemm_attnproj3072_traffic.md"),
                     help="profile summary holding the measured HBM bytes per launch of the "
                          "dominant kernel (used only while the kernel sources are unchanged)")
-    ap.add_argument("--suite", choices=["block16", "alloc", "rotate", "w4a8"], default=None,
+    ap.add_argument("--tokens", type=int, default=1024,
+                    help="block: tokens per product (M > 64: the large-M kernel)")
+    ap.add_argument("--suite", choices=["block16", "block", "alloc", "rotate", "w4a8"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
                          "one by one and grouped, one JSON line each; alloc: error tables of a "
@@ -107,6 +110,55 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 3}), flush=True)
+
+
+def block_suite(tokens, steps, warmup):
+    """The four linears of one DiT block (Wan-14B shapes, drawn widths) at
+    `tokens` > 64 tokens: each product alone, the four one by one, and the four
+    as one grouped call (one launch of the large-M kernel's tiles)."""
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    bits_of = synth.config5_bits()
+    lins = []
+    for name in ("qkv", "o", "up", "down"):
+        w = torch.from_numpy(synth.config5_weights(name)).to(dev, torch.bfloat16)
+        qw = api.quantize_pack(w, bits_of[name])
+        del w
+        x = torch.from_numpy(synth.config5_x(name, tokens)).to(dev, torch.bfloat16)
+        y = torch.empty((tokens, qw.n), dtype=torch.bfloat16, device=dev)
+        lins.append({"name": name, "qw": qw, "x": x, "y": y})
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def line(name, ls, ms):
+        flops = sum(2.0 * tokens * L["qw"].n * L["qw"].k for L in ls)
+        tf = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"suite": "dit-block", "tokens": tokens, "linear": name,
+                          "shapes": [f"{L['qw'].n}x{L['qw'].k}@{L['qw'].bits}b" for L in ls],
+                          "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": steps}),
+              flush=True)
+
+    for L in lins:
+        line(L["name"], [L], timed(lambda L=L: api.dequant_gemm(L["x"], L["qw"], out=L["y"])))
+    line("qkv+o+up+down one by one", lins,
+         timed(lambda: [api.dequant_gemm(L["x"], L["qw"], out=L["y"]) for L in lins]))
+    line("qkv+o+up+down grouped", lins,
+         timed(lambda: api.dequant_gemm_grouped([(L["x"], L["qw"], L["y"]) for L in lins])))
 
 
 def block16_suite(steps, warmup):
@@ -692,6 +744,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.suite == "block16":
         block16_suite(args.steps, args.warmup)
+        return
+    if args.suite == "block":
+        block_suite(args.tokens, args.steps, args.warmup)
         return
     if args.suite == "alloc":
         alloc_suite(args)

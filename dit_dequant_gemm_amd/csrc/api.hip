@@ -254,16 +254,37 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
   };
   // Products with M <= 16 share launches, longest workgroups first (their
   // work is about K * bits per workgroup) so that the short ones fill in.
-  int small[DDG_MAX_GROUPED];
-  int n_small = 0;
+  // Products with M > 64 share launches of the large kernel's tiles, deepest
+  // K first.  The others (16 < M <= 64) launch one by one.
+  int small[DDG_MAX_GROUPED], large[DDG_MAX_GROUPED];
+  int n_small = 0, n_large = 0;
   for (int i = 0; i < count; ++i) {
     if (descs[i].m == 0) continue;
     if (descs[i].m <= 16) {
       small[n_small++] = i;
+    } else if (descs[i].m > 64) {
+      large[n_large++] = i;
     } else {
       ddg::GemmArgs a = args_of(descs[i]);
       if (hipError_t e = launch_product(a, descs[i].bits, stream)) return hip_status(e);
     }
+  }
+  std::stable_sort(large, large + n_large, [&](int p, int q) { return descs[p].k > descs[q].k; });
+  for (int s0 = 0; s0 < n_large; s0 += ddg::kMaxGroup) {
+    ddg::GroupLargeArgs ga{};
+    ga.count = std::min(ddg::kMaxGroup, n_large - s0);
+    ga.tile_start[0] = 0;
+    for (int j = 0; j < ga.count; ++j) {
+      const ddg_gemm_desc& d = descs[large[s0 + j]];
+      ga.g[j] = args_of(d);
+      ga.g[j].tiles_m = (int)((d.m + ddg::kBM - 1) / ddg::kBM);
+      ga.g[j].tiles_n = (int)((d.n + ddg::kBN - 1) / ddg::kBN);
+      ga.bits[j] = d.bits;
+      const int64_t tiles = (int64_t)ga.g[j].tiles_m * ga.g[j].tiles_n;
+      if (ga.tile_start[j] + tiles > kMaxDim) return DDG_ERR_SHAPE;
+      ga.tile_start[j + 1] = ga.tile_start[j] + (int)tiles;
+    }
+    if (hipError_t e = ddg::launch_gemm_grouped_large(ga, stream)) return hip_status(e);
   }
   std::stable_sort(small, small + n_small, [&](int p, int q) {
     return descs[p].k * descs[p].bits > descs[q].k * descs[q].bits;

@@ -207,21 +207,22 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// One 256 x 256 output tile (tile index `tile` of the product `args`); `lds`
+// is the workgroup's 128 KB LDS block.  Kernels: gemm_large_kernel (one
+// product) and gemm_grouped_large_kernel (several products in one launch).
 template <int B>
-__global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
+__device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8_t* lds) {
   constexpr int RB = kBM / 32;          // 8 row blocks of 32
   constexpr int LA = 4;                 // A-operand look-ahead, in MFMA steps
   constexpr int RING = 8;               // A-operand ring (64 steps per group = 8 laps)
   constexpr int STEPS = 8 * RB;         // 8 k-steps x 8 row blocks
   constexpr int HAND = STEPS - LA;      // step of the group hand-over (barrier)
   constexpr int CW = 2 * B;             // packed dwords per lane per group
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
-
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
   int tm, tn;
-  tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+  tile_coords(tile, args.tiles_m, args.tiles_n, tm, tn);
   const int m0 = tm * kBM;
   const int nw0 = tn * kBN;
   const int K = args.k;
@@ -402,6 +403,12 @@ __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
     else
       store_block32<false>(acc[rb], scratch, args.y, args.m, args.n, m0 + rb * 32, nw0 + wave * 32, vec);
   }
+}
+
+template <int B>
+__global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
+  large_tile<B>(args, blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,7 +909,18 @@ struct GroupArgs {
   int count;
 };
 
-// gemm_grouped_skinny_kernel(GroupArgs) is defined in grouped.hip.
+// Up to kMaxGroup products with M > 64 in one launch of K2 tiles:
+// tile_start is the prefix sum of the products' tile counts (tiles_m x
+// tiles_n of each GemmArgs).
+struct GroupLargeArgs {
+  GemmArgs g[kMaxGroup];
+  int tile_start[kMaxGroup + 1];
+  int bits[kMaxGroup];
+  int count;
+};
+
+// gemm_grouped_skinny_kernel(GroupArgs) and gemm_grouped_large_kernel
+// (GroupLargeArgs) are defined in grouped.hip.
 
 // ---------------------------------------------------------------------------
 // K4: T = bf16(X * L1), with L1^T = lora_down (R x K) -- computed as

@@ -31,6 +31,32 @@ __global__ __launch_bounds__(512) void gemm_grouped_skinny_kernel(GroupArgs ga) 
 }
 
 
+// Several M > 64 products: workgroup i runs tile i - tile_start[j] of product
+// j with that product's bit width.
+__global__ __launch_bounds__(512, 1) void gemm_grouped_large_kernel(GroupLargeArgs ga) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
+  const int bid = blockIdx.x;
+  int j = 0;
+  while (j + 1 < ga.count && bid >= ga.tile_start[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const int t = bid - ga.tile_start[j];
+  switch (ga.bits[j]) {
+    case 3: large_tile<3>(ga.g[j], t, lds); break;
+    case 4: large_tile<4>(ga.g[j], t, lds); break;
+    case 5: large_tile<5>(ga.g[j], t, lds); break;
+    case 6: large_tile<6>(ga.g[j], t, lds); break;
+    case 7: large_tile<7>(ga.g[j], t, lds); break;
+  }
+}
+
+hipError_t launch_gemm_grouped_large(const GroupLargeArgs& ga, hipStream_t stream) {
+  if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
+  const int tiles = ga.tile_start[ga.count];
+  if (tiles <= 0) return hipSuccess;
+  gemm_grouped_large_kernel<<<dim3((unsigned)tiles), dim3(512), 0, stream>>>(ga);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream) {
   if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
   const int wgs = ga.wg_start[ga.count];

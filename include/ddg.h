@@ -150,7 +150,10 @@ typedef struct ddg_gemm_desc {
  * projections of a block cannot share one packed tensor).  Equivalent to
  * ddg_dequant_gemm on every descriptor, with every requirement of that call.
  * Products with M <= 16 go into one launch per 16 products (mixed bit widths
- * and shapes); the others are launched one by one on the same stream.
+ * and shapes); so do products with M > 64 (the large-M kernel's 256 x 256
+ * tiles of up to 16 products, deepest K first; their results equal those of
+ * separate calls bit for bit).  Products with 16 < M <= 64 are launched one
+ * by one on the same stream.
  *   descs   host array of `count` descriptors, read during the call only.
  *   count   0 .. DDG_MAX_GROUPED (0 is a no-op).
  * No y may overlap another product's inputs or output.  Results equal those

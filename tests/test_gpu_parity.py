@@ -207,6 +207,45 @@ def test_gemm_grouped_more_than_one_launch(gpu_lib):
     _run_group(gpu_lib, cases, 2)
 
 
+# Products with M > 64 share launches of the large-M kernel's tiles: mixed
+# widths, one and several tiles, ragged M and N, K from one to ten groups,
+# beside small products of the same call.
+_GROUP_LARGE_CASES = [
+    (65, 192, 128, 3, torch.float32),        # one tile, one group
+    (300, 528, 384, 4, torch.bfloat16),      # 2 x 3 tiles, ragged M and N
+    (257, 256, 1280, 5, torch.float32),      # ten groups, a 1-row last row tile
+    (130, 1024, 640, 6, torch.bfloat16),
+    (96, 304, 896, 7, torch.float32),
+    (16, 272, 640, 6, torch.float32),        # a small product in the same call
+]
+
+
+def test_gemm_grouped_large(gpu_lib):
+    _case("dequant_gemm_grouped products with M > 64 (grouped large tiles)")
+    _run_group(gpu_lib, _GROUP_LARGE_CASES, 3)
+
+
+def test_gemm_grouped_large_more_than_one_launch(gpu_lib):
+    _case("dequant_gemm_grouped 18 products with M > 64 (two launches)")
+    cases = [(65 + 37 * (i % 4), 64 * (1 + i % 5), 128 * (1 + i % 3), 3 + i % 5,
+              torch.float32 if i % 2 else torch.bfloat16) for i in range(18)]
+    _run_group(gpu_lib, cases, 4)
+
+
+def test_gemm_grouped_large_equals_single_calls(gpu_lib):
+    _case("dequant_gemm_grouped M > 64 against separate dequant_gemm calls (bit for bit)")
+    c = synth.random_case(6, 300, 528, 1280)
+    outs_single, items = [], []
+    for bits in (3, 4, 7):
+        qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+        x = dev_bf16(c["x"])
+        outs_single.append(host(gpu_lib.dequant_gemm(x, qw, torch.float32)))
+        items.append((x, qw))
+    outs = gpu_lib.dequant_gemm_grouped(items, out_dtype=torch.float32)
+    for a, b in zip(outs, outs_single):
+        assert np.array_equal(host(a), b), "grouped large tiles differ from the single call"
+
+
 def test_gemm_grouped_matches_single_calls(gpu_lib):
     _case("dequant_gemm_grouped against separate dequant_gemm calls")
     c = synth.random_case(5, 16, 1024, 1280)
