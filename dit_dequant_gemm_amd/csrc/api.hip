@@ -255,20 +255,40 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
   // Products with M <= 16 share launches, longest workgroups first (their
   // work is about K * bits per workgroup) so that the short ones fill in.
   // Products with M > 64 share launches of the large kernel's tiles, deepest
-  // K first.  The others (16 < M <= 64) launch one by one.
-  int small[DDG_MAX_GROUPED], large[DDG_MAX_GROUPED];
-  int n_small = 0, n_large = 0;
+  // K first; products with 16 < M <= 32 and 32 < M <= 64 share launches of
+  // the small-M kernel's body (two column waves x a two-way K split), longest
+  // workgroups first.
+  int small[DDG_MAX_GROUPED], large[DDG_MAX_GROUPED], mid2[DDG_MAX_GROUPED], mid4[DDG_MAX_GROUPED];
+  int n_small = 0, n_large = 0, n_mid2 = 0, n_mid4 = 0;
   for (int i = 0; i < count; ++i) {
     if (descs[i].m == 0) continue;
-    if (descs[i].m <= 16) {
-      small[n_small++] = i;
-    } else if (descs[i].m > 64) {
-      large[n_large++] = i;
-    } else {
-      ddg::GemmArgs a = args_of(descs[i]);
-      if (hipError_t e = launch_product(a, descs[i].bits, stream)) return hip_status(e);
-    }
+    if (descs[i].m <= 16) small[n_small++] = i;
+    else if (descs[i].m <= 32) mid2[n_mid2++] = i;
+    else if (descs[i].m <= 64) mid4[n_mid4++] = i;
+    else large[n_large++] = i;
   }
+  auto launch_mid = [&](int* list, int n_list, int rb) -> int {
+    std::stable_sort(list, list + n_list, [&](int p, int q) {
+      return descs[p].k * descs[p].bits > descs[q].k * descs[q].bits;
+    });
+    for (int s0 = 0; s0 < n_list; s0 += ddg::kMaxGroup) {
+      ddg::GroupArgs ga{};
+      ga.count = std::min(ddg::kMaxGroup, n_list - s0);
+      ga.wg_start[0] = 0;
+      for (int j = 0; j < ga.count; ++j) {
+        const ddg_gemm_desc& d = descs[list[s0 + j]];
+        ga.g[j] = args_of(d);
+        ga.bits[j] = d.bits;
+        const int64_t wgs = (d.n + 31) / 32;
+        if (ga.wg_start[j] + wgs > kMaxDim) return DDG_ERR_SHAPE;
+        ga.wg_start[j + 1] = ga.wg_start[j] + (int)wgs;
+      }
+      if (hipError_t e = ddg::launch_gemm_grouped_small(ga, rb, stream)) return hip_status(e);
+    }
+    return DDG_OK;
+  };
+  if (int st = launch_mid(mid2, n_mid2, 2)) return st;
+  if (int st = launch_mid(mid4, n_mid4, 4)) return st;
   std::stable_sort(large, large + n_large, [&](int p, int q) { return descs[p].k > descs[q].k; });
   for (int s0 = 0; s0 < n_large; s0 += ddg::kMaxGroup) {
     ddg::GroupLargeArgs ga{};

@@ -428,22 +428,41 @@ __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
 // main loop, group indices past a wave's range are clamped, loaded and never
 // used; the last steps (the tail) issue nothing.
 // ---------------------------------------------------------------------------
-template <int B, int RB, int NC, int NK>
-__global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args) {
-  // X slices and packed weights of step j + D are issued together at step j
-  // (ring of S = D + 1 slots each).  Loads finish in issue order, so waiting
-  // for the X of step j never waits for a later step's packed weights.
-  constexpr int XSLOT = RB * 16 * 256;        // one group's X slice: 16*RB rows x 256 bytes
-  constexpr int RED_BYTES = (NK > 1 ? NK - 1 : 1) * NC * RB * 64 * 16;
+// LDS of the small-M kernel for a (RB, NC, NK) shape: the X ring (one array
+// per slot, so that the compiler can see that a DMA into one slot does not
+// alias reads of another, and does not make the reads wait for it) and the
+// partial tiles of the K-split reduction.  A kernel declares it __shared__.
+template <int RB, int NC, int NK>
+struct SmallLds {
+  static constexpr int XSLOT = RB * 16 * 256;        // one group's X slice: 16*RB rows x 256 bytes
+  static constexpr int RED_BYTES = (NK > 1 ? NK - 1 : 1) * NC * RB * 64 * 16;
   // Ring slots: 3 with a two-way K split, else 2 (both within the 160 KB of
   // LDS).  Deeper rings measured slower on the 16- to 64-token products
   // (16 x 3072 x 3072: 5.1 us with 2 slots, 5.6 with 4): they hold more LDS
   // per workgroup, and near the end of a K range they fetch clamped groups
   // that are never used.
-  constexpr int S_FIT = (160 * 1024 - RED_BYTES) / (NK * XSLOT);
-  constexpr int S_WANT = NK <= 2 ? 3 : 2;
-  constexpr int S = S_FIT > S_WANT ? S_WANT : S_FIT;
+  static constexpr int S_FIT = (160 * 1024 - RED_BYTES) / (NK * XSLOT);
+  static constexpr int S_WANT = NK <= 2 ? 3 : 2;
+  static constexpr int S = S_FIT > S_WANT ? S_WANT : S_FIT;
   static_assert(S >= 2, "X ring needs two slots");
+  __attribute__((aligned(1024))) uint8_t xs0[NK][XSLOT];
+  __attribute__((aligned(1024))) uint8_t xs1[NK][XSLOT];
+  __attribute__((aligned(1024))) uint8_t xs2[S > 2 ? NK : 1][S > 2 ? XSLOT : 16];
+  __attribute__((aligned(1024))) uint8_t xs3[S > 3 ? NK : 1][S > 3 ? XSLOT : 16];
+  __attribute__((aligned(1024))) uint8_t xs4[S > 4 ? NK : 1][S > 4 ? XSLOT : 16];
+  __attribute__((aligned(1024))) uint8_t xs5[S > 5 ? NK : 1][S > 5 ? XSLOT : 16];
+  f32x4 red[NK > 1 ? NK - 1 : 1][NC][RB][64];
+};
+
+// Workgroup `wg` of the product `args` (column block 16 NC wg ..).  Kernels:
+// gemm_small_kernel (one product) and gemm_grouped_small_kernel (several).
+template <int B, int RB, int NC, int NK>
+__device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLds<RB, NC, NK>& L) {
+  // X slices and packed weights of step j + D are issued together at step j
+  // (ring of S = D + 1 slots each).  Loads finish in issue order, so waiting
+  // for the X of step j never waits for a later step's packed weights.
+  constexpr int XSLOT = SmallLds<RB, NC, NK>::XSLOT;
+  constexpr int S = SmallLds<RB, NC, NK>::S;
   constexpr int D = S - 1;                    // steps in flight
   constexpr int DMA_SLOT = XSLOT / 1024;      // 1 KB DMA instructions per slice
   static_assert(DMA_SLOT % NC == 0, "slice DMA must split evenly over the column waves");
@@ -452,30 +471,20 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
   // issued after X(j) (at step j - D): W(j), then D - 1 steps of X + W
   constexpr int VM_AHEAD = NWL + (D - 1) * (ND + NWL);
   static_assert(VM_AHEAD < 64, "vmcnt field");
-  // One LDS array per ring slot: the compiler can then see that a DMA into
-  // one slot does not alias reads of another, and does not make the reads
-  // wait for it.
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[NK][XSLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs1[NK][XSLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[S > 2 ? NK : 1][S > 2 ? XSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs3[S > 3 ? NK : 1][S > 3 ? XSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs4[S > 4 ? NK : 1][S > 4 ? XSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs5[S > 5 ? NK : 1][S > 5 ? XSLOT : 16];
-  __shared__ f32x4 red[NK > 1 ? NK - 1 : 1][NC][RB][64];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = wave % NC, h = wave / NC;
   auto xslot = [&]<int SL>(std::integral_constant<int, SL>) -> uint8_t* {
-    if constexpr (SL == 0) return &xs0[h][0];
-    else if constexpr (SL == 1) return &xs1[h][0];
-    else if constexpr (SL == 2) return &xs2[h][0];
-    else if constexpr (SL == 3) return &xs3[h][0];
-    else if constexpr (SL == 4) return &xs4[h][0];
-    else return &xs5[h][0];
+    if constexpr (SL == 0) return &L.xs0[h][0];
+    else if constexpr (SL == 1) return &L.xs1[h][0];
+    else if constexpr (SL == 2) return &L.xs2[h][0];
+    else if constexpr (SL == 3) return &L.xs3[h][0];
+    else if constexpr (SL == 4) return &L.xs4[h][0];
+    else return &L.xs5[h][0];
   };
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NC;
+  const int n0 = wg * 16 * NC;
   const int K = args.k;
   const int G = K / kGroup;
   const int g_begin = h * G / NK, g_end = (h + 1) * G / NK;
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
   if constexpr (NK > 1) {
     if (h > 0) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) red[h - 1][c][rb][lane] = acc[rb];
+      for (int rb = 0; rb < RB; ++rb) L.red[h - 1][c][rb][lane] = acc[rb];
     }
     __syncthreads();
     if (h > 0) return;
@@ -614,7 +623,7 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
     for (int k = 0; k < NK - 1; ++k)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const f32x4 v = red[k][c][rb][lane];
+        const f32x4 v = L.red[k][c][rb][lane];
         acc[rb][0] += v[0]; acc[rb][1] += v[1]; acc[rb][2] += v[2]; acc[rb][3] += v[3];
       }
   }
@@ -644,6 +653,12 @@ __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args)
     else
       store_tile<false>(args.y, args.n, rb * 16 + 4 * lq, n0 + c * 16 + lr, args.m, args.n, acc[rb]);
   }
+}
+
+template <int B, int RB, int NC, int NK>
+__global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args) {
+  __shared__ SmallLds<RB, NC, NK> L;
+  small_body<B, RB, NC, NK>(args, blockIdx.x, L);
 }
 
 // ---------------------------------------------------------------------------

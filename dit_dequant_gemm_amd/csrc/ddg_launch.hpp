@@ -32,6 +32,9 @@ hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream);
 // up to kMaxGroup products with M > 64 in one launch of 256 x 256 tiles
 // (ga.tile_start is the prefix sum of the products' tile counts)
 hipError_t launch_gemm_grouped_large(const GroupLargeArgs& ga, hipStream_t stream);
+// up to kMaxGroup products with 16 < M <= 16 rb (rb = 2 or 4) in one launch
+// (ga.wg_start is the prefix sum of ceil(n / 32) over the products)
+hipError_t launch_gemm_grouped_small(const GroupArgs& ga, int rb, hipStream_t stream);
 
 // per-row and total quantization error at widths 3..7 (row_sse: n x 5)
 hipError_t launch_quant_sse(const void* w, bool f32_in, int64_t n, int64_t k, double* row_sse,

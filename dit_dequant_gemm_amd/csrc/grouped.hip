@@ -49,6 +49,39 @@ __global__ __launch_bounds__(512, 1) void gemm_grouped_large_kernel(GroupLargeAr
   }
 }
 
+// Several products with 16 < M <= 16 RB: workgroup i runs workgroup
+// i - wg_start[j] of product j (32 output columns: two column waves, a
+// two-way K split) with that product's bit width.
+template <int RB>
+__global__ __launch_bounds__(256) void gemm_grouped_small_kernel(GroupArgs ga) {
+  __shared__ SmallLds<RB, 2, 2> L;
+  const int bid = blockIdx.x;
+  int j = 0;
+  while (j + 1 < ga.count && bid >= ga.wg_start[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const int wg = bid - ga.wg_start[j];
+  switch (ga.bits[j]) {
+    case 3: small_body<3, RB, 2, 2>(ga.g[j], wg, L); break;
+    case 4: small_body<4, RB, 2, 2>(ga.g[j], wg, L); break;
+    case 5: small_body<5, RB, 2, 2>(ga.g[j], wg, L); break;
+    case 6: small_body<6, RB, 2, 2>(ga.g[j], wg, L); break;
+    case 7: small_body<7, RB, 2, 2>(ga.g[j], wg, L); break;
+  }
+}
+
+hipError_t launch_gemm_grouped_small(const GroupArgs& ga, int rb, hipStream_t stream) {
+  if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
+  const int wgs = ga.wg_start[ga.count];
+  if (wgs <= 0) return hipSuccess;
+  if (rb == 2)
+    gemm_grouped_small_kernel<2><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(ga);
+  else if (rb == 4)
+    gemm_grouped_small_kernel<4><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(ga);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_grouped_large(const GroupLargeArgs& ga, hipStream_t stream) {
   if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
   const int tiles = ga.tile_start[ga.count];

@@ -149,11 +149,10 @@ typedef struct ddg_gemm_desc {
  * the fly; §3.2: each tensor gets its own bit width, so e.g. the q, k and v
  * projections of a block cannot share one packed tensor).  Equivalent to
  * ddg_dequant_gemm on every descriptor, with every requirement of that call.
- * Products with M <= 16 go into one launch per 16 products (mixed bit widths
- * and shapes); so do products with M > 64 (the large-M kernel's 256 x 256
- * tiles of up to 16 products, deepest K first; their results equal those of
- * separate calls bit for bit).  Products with 16 < M <= 64 are launched one
- * by one on the same stream.
+ * Products go into one launch per 16 products (mixed bit widths and shapes)
+ * of the same class: M <= 16; 16 < M <= 32; 32 < M <= 64; M > 64 (the
+ * large-M kernel's 256 x 256 tiles, deepest K first; these results equal
+ * those of separate calls bit for bit).  All launches are on `stream`.
  *   descs   host array of `count` descriptors, read during the call only.
  *   count   0 .. DDG_MAX_GROUPED (0 is a no-op).
  * No y may overlap another product's inputs or output.  Results equal those

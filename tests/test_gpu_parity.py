@@ -220,6 +220,33 @@ _GROUP_LARGE_CASES = [
 ]
 
 
+# Products with 16 < M <= 32 and 32 < M <= 64 share launches of the small-M
+# kernel's body (two column waves, a two-way K split): mixed widths, ragged
+# N (a half-filled last workgroup), one group to 108 groups of K (ring tails).
+_GROUP_MID_CASES = [
+    (17, 5120, 1280, 4, torch.bfloat16),
+    (32, 272, 384, 6, torch.float32),        # N = 8.5 workgroups of 32 columns
+    (24, 1024, 13824, 3, torch.bfloat16),    # 108 groups
+    (33, 3072, 128, 7, torch.float32),       # one group: one K half idle
+    (64, 528, 2560, 5, torch.bfloat16),
+    (50, 4096, 512, 4, torch.float32),
+    (16, 272, 640, 6, torch.float32),        # a 16-token product in the same call
+    (80, 192, 384, 3, torch.float32),        # and a large-M one
+]
+
+
+def test_gemm_grouped_mid(gpu_lib):
+    _case("dequant_gemm_grouped products with 16 < M <= 64 (grouped small-M body)")
+    _run_group(gpu_lib, _GROUP_MID_CASES, 5)
+
+
+def test_gemm_grouped_mid_more_than_one_launch(gpu_lib):
+    _case("dequant_gemm_grouped 18 products with 16 < M <= 32 (two launches)")
+    cases = [(17 + (i % 16), 64 * (1 + i % 5), 128 * (1 + i % 7), 3 + i % 5,
+              torch.float32 if i % 2 else torch.bfloat16) for i in range(18)]
+    _run_group(gpu_lib, cases, 6)
+
+
 def test_gemm_grouped_large(gpu_lib):
     _case("dequant_gemm_grouped products with M > 64 (grouped large tiles)")
     _run_group(gpu_lib, _GROUP_LARGE_CASES, 3)

@@ -117,3 +117,44 @@ def test_small_kernel_load_order(asm_by_bits, bits):
             assert w in allowed, f"{where}: barrier after vmcnt({w}), allowed {sorted(allowed)}"
         # the steady-state count appears (main loop) unless the ring is one step deep
         assert nwl + (d - 1) * (nd + nwl) in waits, f"{where}: no steady-state wait"
+
+
+GROUPED_SMALL = re.compile(r"^(_ZN3ddg25gemm_grouped_small_kernelILi(\d)EEEvNS_9GroupArgsE):", re.M)
+
+
+@pytest.fixture(scope="module")
+def grouped_asm(tmp_path_factory):
+    if not (shutil.which(B.HIPCC) or os.path.exists(B.HIPCC)):
+        pytest.skip("hipcc not found")
+    tmp = str(tmp_path_factory.mktemp("asm_grouped"))
+    out = os.path.join(tmp, "grouped.s")
+    cmd = [B.HIPCC, *B.COMMON, "--cuda-device-only", "-S", os.path.join(B.CSRC, "grouped.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
+    assert r.returncode == 0, r.stderr[-2000:]
+    with open(out) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("rb", (2, 4))
+def test_grouped_small_kernel_load_order(grouped_asm, rb):
+    """The grouped kernel inlines the same body once per bit width, one after
+    the other: every barrier-to-barrier segment is a prologue (D groups), one
+    group or nothing, for a width of two (3, 4 bits) or three (5..7 bits)
+    weight loads, and every wait is one the schedule allows."""
+    text = grouped_asm
+    ms = [m for m in GROUPED_SMALL.finditer(text) if int(m.group(2)) == rb]
+    assert ms, f"no gemm_grouped_small_kernel<{rb}> found"
+    m = ms[0]
+    body = text[m.end(): text.index("s_endpgm", m.end())]
+    ev, waits = _events(body)
+    segs = ev.split("|")
+    allowed_segs, allowed_waits = {""}, {0}
+    for bits in (3, 5):
+        d, nd, nwl = _schedule(bits, rb, 2, 2)
+        group = "X" * nd + "W" * nwl
+        allowed_segs |= {group, group * d}
+        allowed_waits |= {nwl + u * (nd + nwl) for u in range(d)}
+    for sg in segs:
+        assert sg in allowed_segs, f"RB={rb}: segment {sg!r}"
+    for w in waits:
+        assert w in allowed_waits, f"RB={rb}: barrier after vmcnt({w}), allowed {sorted(allowed_waits)}"
