@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <system_error>
+#include <thread>
 #include <vector>
 
 #include "ddg.h"
@@ -253,12 +255,17 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
   const double step = 1.0 / (2.0 * kPenalty * span * span * wsq);
   const double budget = target_bpw * tot;
 
-  std::vector<double> t(n), u(n), b(n), g(n), sw(ncand), frac(n);
-  std::vector<int> idx(n), order(n), best_bits(n);
-  bool have = false;
-  int best_feasible = 0, best_restart = 0;
-  double best_e = 0.0, best_p = 0.0;
-  for (int r = 0; r < restarts; ++r) {
+  // One restart: descent from its own starting point, then the rounding and
+  // the exact score.  Restarts share nothing but the read-only tables.
+  struct Outcome {
+    int feasible = 0;
+    double e = 0.0, p = 0.0;
+    std::vector<int> bits;
+  };
+  std::vector<Outcome> out(restarts);
+  auto run_restart = [&](int r) {
+    std::vector<double> t(n), u(n), b(n), g(n), sw(ncand), frac(n);
+    std::vector<int> idx(n), order(n);
     for (int i = 0; i < n; ++i) t[i] = t_init[(int64_t)r * n + i];
     double lam = 0.5;
     for (int it = 0; it < iters; ++it) {
@@ -301,23 +308,47 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
       e += (double)nparams[i] * mse[(int64_t)i * ncand + idx[i]];
       p += (double)nparams[i] * (double)candidates[idx[i]];
     }
-    e /= tot;
-    p /= tot;
-    const int feasible = p <= target_bpw + 1e-9 ? 1 : 0;
-    bool better;
-    if (!have) better = true;
-    else if (feasible != best_feasible) better = feasible > best_feasible;
-    else if (feasible) better = e < best_e || (e == best_e && p < best_p);
-    else better = p < best_p || (p == best_p && e < best_e);
-    if (better) {
-      have = true;
-      best_feasible = feasible;
-      best_e = e;
-      best_p = p;
-      best_restart = r;
-      for (int i = 0; i < n; ++i) best_bits[i] = candidates[idx[i]];
+    Outcome& o = out[r];
+    o.e = e / tot;
+    o.p = p / tot;
+    o.feasible = o.p <= target_bpw + 1e-9 ? 1 : 0;
+    o.bits.resize(n);
+    for (int i = 0; i < n; ++i) o.bits[i] = candidates[idx[i]];
+  };
+  // Restarts on up to 16 host threads, restart r on thread r mod T.  Each
+  // restart's arithmetic is the same on any thread, so the result does not
+  // depend on T; a thread that cannot be started leaves its restarts to the
+  // calling thread.
+  const int hw = (int)std::thread::hardware_concurrency();
+  const int nthreads = std::max(1, std::min({restarts, hw > 0 ? hw : 1, 16}));
+  auto run_stride = [&](int first) {
+    for (int r = first; r < restarts; r += nthreads) run_restart(r);
+  };
+  std::vector<std::thread> pool;
+  std::vector<int> orphaned;
+  for (int w = 1; w < nthreads; ++w) {
+    try {
+      pool.emplace_back(run_stride, w);
+    } catch (const std::system_error&) {
+      orphaned.push_back(w);
     }
   }
+  run_stride(0);
+  for (int w : orphaned) run_stride(w);
+  for (auto& th : pool) th.join();
+  // the kept restart, compared in restart order
+  int best = 0;
+  for (int r = 1; r < restarts; ++r) {
+    const Outcome &c = out[r], &k = out[best];
+    bool better;
+    if (c.feasible != k.feasible) better = c.feasible > k.feasible;
+    else if (c.feasible) better = c.e < k.e || (c.e == k.e && c.p < k.p);
+    else better = c.p < k.p || (c.p == k.p && c.e < k.e);
+    if (better) best = r;
+  }
+  const std::vector<int>& best_bits = out[best].bits;
+  const double best_e = out[best].e, best_p = out[best].p;
+  const int best_restart = best;
   for (int i = 0; i < n; ++i) bits_out[i] = best_bits[i];
   if (info) { info[0] = best_e; info[1] = best_p; info[2] = best_restart; }
   return DDG_OK;

@@ -229,3 +229,22 @@ def test_quant_sse_rejects_bad_arguments():
     assert lib.ddg_quant_sse(None, 0, 4, 128, FAKE, FAKE, None) == -1
     assert lib.ddg_quant_sse(FAKE + 4, 0, 4, 128, FAKE, FAKE, None) == -3      # w alignment
     assert lib.ddg_quant_sse(FAKE, 0, 4, 128, FAKE + 4, FAKE, None) == -3
+
+
+def test_library_search_restarts_are_independent():
+    """Restarts run on several host threads: the kept widths must equal those
+    of the best single-restart call under the same rule (feasible first, then
+    the lower error, then the lower bpw, the earlier restart on ties)."""
+    mse, n = O.mse_table(_tensors(21, count=24))
+    n = n * np.random.default_rng(21).integers(1, 9, size=len(n))
+    t_init = 0.8 * np.random.default_rng(121).standard_normal((37, len(n)))
+    bits, info = api.pd_allocate(mse, n, 4.3, t_init, iters=120)
+    singles = [api.pd_allocate(mse, n, 4.3, t_init[r:r + 1], iters=120) for r in range(len(t_init))]
+    def key(r):
+        b, inf = singles[r]
+        feasible = inf["bpw"] <= 4.3 + 1e-9
+        return (0, inf["mse"], inf["bpw"], r) if feasible else (1, inf["bpw"], inf["mse"], r)
+    best = min(range(len(t_init)), key=key)
+    assert info["restart"] == best
+    assert np.array_equal(bits, singles[best][0])
+    assert info["mse"] == singles[best][1]["mse"] and info["bpw"] == singles[best][1]["bpw"]
