@@ -227,7 +227,9 @@ int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_
  * its width, then moves up one candidate, by decreasing fraction of the way
  * there (lower index first on ties), while the added bits fit in
  * target * sum n.  The kept restart has the lowest exact error within the
- * budget, else the lowest bpw; ties go to the earlier restart.
+ * budget, else the lowest bpw; ties go to the earlier restart.  Restarts run
+ * on up to 16 host threads started and joined inside the call (the inputs are
+ * only read meanwhile); the result does not depend on their number.
  *   mse        n x ncand per-weight errors (row i: tensor i, column c: width
  *              candidates[c]); finite, >= 0.
  *   nparams    n weight counts, > 0.
