@@ -1,0 +1,143 @@
+"""GPU parity at the limits of the C ABI: the largest K it accepts (2^20), and
+buffers past 4 GiB (an input, a packed weight and an output), so that every
+byte offset a kernel forms above 2^32 is exercised.
+
+Large inputs are built on the GPU by repeating a seeded block from the input
+generators; the rows that are checked are overwritten with rows of their own
+(another seeded draw), so an offset that wrapped at 32 bits would read other
+data and fail the comparison.  The oracle quantizes and multiplies only the
+checked rows.  Same bars as the other parity tests: packed bytes and scales
+bit for bit, products within a relative Frobenius error of 1e-3 and a per-row
+max error of 2e-2 * max |row|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dit_dequant_gemm_amd import synth
+from parity_util import check_product, dev_bf16, f32_bits, host
+
+pytestmark = pytest.mark.gpu
+
+K_MAX = 1 << 20          # the largest K the C ABI accepts
+GIB4 = 1 << 32
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _rows_to_host(t, rows):
+    idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    return t.index_select(0, idx).float().cpu().numpy()
+
+
+def _w16(w, bits):
+    q_u, s = O.quantize_groups(w, bits)
+    return O.dequant_bf16(q_u, s, bits)
+
+
+@pytest.mark.parametrize("bits", (3, 7))
+def test_quantize_and_gemm_at_k_max(gpu_lib, bits):
+    """K = 2^20 (8192 groups per row) through every product kernel: M = 4
+    (weight streaming), 20 (small-M, two row blocks), 80 (large tiles)."""
+    c = synth.random_case(31 + bits, 80, 32, K_MAX)
+    _case(f"quantize_pack 32 x 2^20 bits={bits}")
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+    p_ref, s_ref, q_ref = O.quantize_pack(c["w"], bits)
+    assert np.array_equal(host(qw.packed).reshape(-1), p_ref), "packed bytes differ"
+    assert np.array_equal(f32_bits(host(qw.scales).reshape(-1)), f32_bits(s_ref.reshape(-1))), "scales differ"
+    w16 = O.dequant_bf16(q_ref, s_ref, bits)
+    xd = dev_bf16(c["x"])
+    for m in (4, 20, 80):
+        _case(f"dequant_gemm M={m} N=32 K=2^20 bits={bits}")
+        y_ref = O.gemm_ref(c["x"][:m], w16)
+        check_product(host(gpu_lib.dequant_gemm(xd[:m], qw, torch.float32)), y_ref, False, f"M={m} f32")
+        check_product(host(gpu_lib.dequant_gemm(xd[:m], qw, torch.bfloat16)), y_ref, True, f"M={m} bf16")
+
+
+def test_gemm_input_past_4gib(gpu_lib):
+    """X of 2176 x 2^20 bf16 (4.56 GB, large tiles): rows from 2048 on start
+    past 4 GiB."""
+    api = gpu_lib
+    m, n, bits = 2176, 32, 5
+    assert m * K_MAX * 2 > GIB4
+    c = synth.random_case(41, 64, n, K_MAX)
+    rows = np.array([0, 1, 63, 1000, 2047, 2048, 2049, 2100, 2111, 2112, 2150, 2175])
+    own = synth.random_case(42, len(rows), 16, K_MAX)["x"]
+    _case(f"dequant_gemm X past 4 GiB: M={m} N={n} K=2^20 bits={bits}")
+    xd = dev_bf16(c["x"]).repeat(m // 64, 1)
+    xd[torch.as_tensor(rows, device="cuda")] = dev_bf16(own)
+    x_rows = _rows_to_host(xd, rows)
+    assert np.array_equal(x_rows, own)
+    qw = api.quantize_pack(dev_bf16(c["w"]), bits)
+    w16 = _w16(c["w"], bits)
+    y_ref = O.gemm_ref(x_rows, w16)
+    for dt, bf in ((torch.float32, False), (torch.bfloat16, True)):
+        y = api.dequant_gemm(xd, qw, dt)
+        check_product(_rows_to_host(y, rows), y_ref, bf, f"X past 4 GiB {dt}")
+        del y
+    del xd
+    torch.cuda.empty_cache()
+
+
+def test_quantize_and_gemm_weight_past_4gib(gpu_lib):
+    """W of 3,842,048 x 1280 at 7 bits: the packed weight is 4.30 GB and the
+    bf16 input 9.8 GB.  The checked rows include the last ones, whose packed
+    bytes start past 4 GiB; products at M = 4, 24 and 100 compare those
+    columns."""
+    api = gpu_lib
+    k, bits, block = 1280, 7, 4096
+    n = 938 * block
+    row_bytes = k * bits // 8
+    assert n * row_bytes > GIB4 and n % 16 == 0
+    base = synth.random_case(51, 100, block, k)
+    cols = np.unique(np.concatenate([[0, 1, 4095, 4096, 2_000_000],
+                                     np.arange(GIB4 // row_bytes - 2, GIB4 // row_bytes + 3),
+                                     np.arange(n - 40, n)]))
+    own = synth.random_case(52, 0, len(cols), k)["w"]
+    _case(f"quantize_pack W past 4 GiB: N={n} K={k} bits={bits}")
+    wd = dev_bf16(base["w"]).repeat(n // block, 1)
+    wd[torch.as_tensor(cols, device="cuda")] = dev_bf16(own)
+    assert np.array_equal(_rows_to_host(wd, cols), own)
+    qw = api.quantize_pack(wd, bits)
+    del wd
+    torch.cuda.empty_cache()
+    p_ref, s_ref, q_ref = O.quantize_pack(own, bits)
+    packed = qw.packed.view(n, row_bytes)
+    got = _rows_to_host(packed, cols).astype(np.uint8)
+    assert np.array_equal(got.reshape(-1), p_ref), "packed bytes differ"
+    sc = _rows_to_host(qw.scales.view(n, k // 128), cols)
+    assert np.array_equal(f32_bits(sc), f32_bits(s_ref.reshape(len(cols), -1))), "scales differ"
+    w16 = O.dequant_bf16(q_ref, s_ref, bits)
+    xd = dev_bf16(base["x"])
+    colt = torch.as_tensor(cols, device="cuda")
+    for m in (4, 24, 100):
+        _case(f"dequant_gemm W past 4 GiB: M={m} N={n} K={k} bits={bits}")
+        y_ref = O.gemm_ref(base["x"][:m], w16)
+        y = api.dequant_gemm(xd[:m], qw, torch.bfloat16)
+        check_product(y.index_select(1, colt).float().cpu().numpy(), y_ref, True, f"M={m}")
+        del y
+    del qw, packed
+    torch.cuda.empty_cache()
+
+
+def test_gemm_output_past_4gib(gpu_lib):
+    """Y of 32800 x 65536 (bf16 4.30 GB, float32 8.6 GB; large tiles): the
+    last rows are stored past 4 GiB."""
+    api = gpu_lib
+    m, n, k, bits = 32800, 65536, 128, 4
+    assert m * n * 2 > GIB4
+    c = synth.random_case(61, m, n, k)
+    rows = np.unique(np.concatenate([[0, 1, 16383, 16384, 32767, 32768], np.arange(m - 40, m)]))
+    _case(f"dequant_gemm Y past 4 GiB: M={m} N={n} K={k} bits={bits}")
+    qw = api.quantize_pack(dev_bf16(c["w"]), bits)
+    w16 = _w16(c["w"], bits)
+    y_ref = O.gemm_ref(c["x"][rows], w16)
+    xd = dev_bf16(c["x"])
+    for dt, bf in ((torch.bfloat16, True), (torch.float32, False)):
+        y = api.dequant_gemm(xd, qw, dt)
+        check_product(_rows_to_host(y, rows), y_ref, bf, f"Y past 4 GiB {dt}")
+        del y
+        torch.cuda.empty_cache()
