@@ -141,3 +141,66 @@ def test_gemm_output_past_4gib(gpu_lib):
         check_product(_rows_to_host(y, rows), y_ref, bf, f"Y past 4 GiB {dt}")
         del y
         torch.cuda.empty_cache()
+
+
+def _w4a8_check(y, xc, xs, wc, ws, out_bf16, what):
+    from oracle import fp4 as F
+    ref = F.w4a8_ref(xc, xs, wc, ws, "e2m1")
+    if not out_bf16:
+        absref = F.w4a8_ref(xc & 0x7F, xs, wc & 7, ws, "e2m1")     # the same sum over magnitudes
+        assert np.all(np.abs(y - ref) <= 2.0 ** -14 * absref + 1e-37), what
+    check_product(y, ref, out_bf16, what)
+
+
+def test_w4a8_chain_activation_codes_past_4gib(gpu_lib):
+    """E4M3 codes of X (1,048,832 x 4096, 4.30 GB; bf16 input 8.6 GB) from the
+    row quantizer, then the tiled FP4 product: the last rows' codes start past
+    4 GiB.  Codes and scales of the checked rows bit for bit, then the
+    product's rows."""
+    from oracle import fp4 as F
+    api = gpu_lib
+    k, n, block = 4096, 64, 256
+    m = 4097 * block
+    assert m * k > GIB4
+    base = synth.random_case(71, block, n, k)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 500_000], np.arange(GIB4 // k - 2, GIB4 // k + 3),
+                                     np.arange(m - 40, m)]))
+    own = synth.random_case(72, len(rows), 16, k)["x"]
+    _case(f"fp8_quantize_rows + w4a8_gemm X codes past 4 GiB: M={m} N={n} K={k}")
+    xd = dev_bf16(base["x"]).repeat(m // block, 1)
+    rt = torch.as_tensor(rows, device="cuda")
+    xd[rt] = dev_bf16(own)
+    xq, xs = api.fp8_quantize_rows(xd)
+    del xd
+    torch.cuda.empty_cache()
+    xc, xsc = F.quantize_rows_e4m3(own)
+    assert np.array_equal(_rows_to_host(xq, rows).astype(np.uint8), xc), "E4M3 codes differ"
+    assert np.array_equal(f32_bits(xs.index_select(0, rt).cpu().numpy()), f32_bits(xsc)), "row scales differ"
+    qw = api.fp4_quantize_pack(dev_bf16(base["w"]), "e2m1", tiled=True)
+    wc, ws = F.quantize_fp4_groups(base["w"], "e2m1")
+    for dt, bf in ((torch.float32, False), (torch.bfloat16, True)):
+        y = api.w4a8_gemm(xq, xs, qw, dt)
+        _w4a8_check(_rows_to_host(y, rows).astype(np.float64), xc, xsc, wc, ws, bf, f"w4a8 X past 4 GiB {dt}")
+        del y
+    del xq, xs
+    torch.cuda.empty_cache()
+
+
+def test_w4a8_output_past_4gib(gpu_lib):
+    """The tiled FP4 x E4M3 product into a 32800 x 65536 bf16 output
+    (4.30 GB): the last rows are stored past 4 GiB."""
+    from oracle import fp4 as F
+    api = gpu_lib
+    m, n, k = 32800, 65536, 128
+    assert m * n * 2 > GIB4
+    c = synth.random_case(81, m, n, k)
+    rows = np.unique(np.concatenate([[0, 1, 16383, 16384, 32767, 32768], np.arange(m - 40, m)]))
+    _case(f"w4a8_gemm Y past 4 GiB: M={m} N={n} K={k}")
+    qw = api.fp4_quantize_pack(dev_bf16(c["w"]), "e2m1", tiled=True)
+    xq, xs = api.fp8_quantize_rows(dev_bf16(c["x"]))
+    wc, ws = F.quantize_fp4_groups(c["w"], "e2m1")
+    xc, xsc = F.quantize_rows_e4m3(c["x"][rows])
+    y = api.w4a8_gemm(xq, xs, qw, torch.bfloat16)
+    _w4a8_check(_rows_to_host(y, rows).astype(np.float64), xc, xsc, wc, ws, True, "w4a8 Y past 4 GiB")
+    del y
+    torch.cuda.empty_cache()
