@@ -204,3 +204,23 @@ def test_w4a8_output_past_4gib(gpu_lib):
     _w4a8_check(_rows_to_host(y, rows).astype(np.float64), xc, xsc, wc, ws, True, "w4a8 Y past 4 GiB")
     del y
     torch.cuda.empty_cache()
+
+
+def test_lowrank_output_past_4gib(gpu_lib):
+    """The fused low-rank product (r = 32) into a 32800 x 65536 bf16 output
+    (4.30 GB): the last rows, with their T . L2 term, are stored past 4 GiB."""
+    api = gpu_lib
+    m, n, k, r, bits = 32800, 65536, 128, 32, 4
+    assert m * n * 2 > GIB4
+    c = synth.random_case(91, m, n, k, wstd=0.05)
+    rows = np.unique(np.concatenate([[0, 1, 16383, 16384, 32767, 32768], np.arange(m - 40, m)]))
+    _case(f"lowrank_fused_gemm Y past 4 GiB: M={m} N={n} K={k} r={r} bits={bits}")
+    l1, l2, res = O.svd_split(c["w"], r)
+    qr = api.quantize_pack(torch.from_numpy(np.ascontiguousarray(res, dtype=np.float32)).cuda(), bits)
+    y_ref, _ = O.lowrank_fused_ref(c["x"][rows], _w16(res, bits), l1, l2)
+    ld = dev_bf16(np.ascontiguousarray(l1.T))
+    lu = dev_bf16(np.ascontiguousarray(l2.T))
+    y = api.lowrank_fused_gemm(dev_bf16(c["x"]), qr, ld, lu, torch.bfloat16)
+    check_product(_rows_to_host(y, rows), y_ref, True, "lowrank Y past 4 GiB")
+    del y
+    torch.cuda.empty_cache()
