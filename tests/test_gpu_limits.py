@@ -224,3 +224,37 @@ def test_lowrank_output_past_4gib(gpu_lib):
     check_product(_rows_to_host(y, rows), y_ref, True, "lowrank Y past 4 GiB")
     del y
     torch.cuda.empty_cache()
+
+
+def test_grouped_past_4gib(gpu_lib):
+    """One grouped call: a 32800 x 65536 product (bf16 output past 4 GiB, large
+    tiles) beside a 16-token and a 40-token product on a packed weight of
+    3,842,048 x 1280 at 7 bits (4.30 GB).  Each is checked on its own rows or
+    columns."""
+    api = gpu_lib
+    big = synth.random_case(101, 32800, 65536, 128)
+    rows = np.unique(np.concatenate([[0, 16384, 32767, 32768], np.arange(32800 - 24, 32800)]))
+    k, bits, block = 1280, 7, 4096
+    n = 938 * block
+    row_bytes = k * bits // 8
+    base = synth.random_case(102, 40, block, k)
+    cols = np.unique(np.concatenate([[0, 4096], np.arange(GIB4 // row_bytes - 1, GIB4 // row_bytes + 2),
+                                     np.arange(n - 20, n)]))
+    own = synth.random_case(103, 0, len(cols), k)["w"]
+    _case(f"grouped: 32800 x 65536 x 128 (4 bits) + 16/40 x {n} x {k} (7 bits)")
+    qb = api.quantize_pack(dev_bf16(big["w"]), 4)
+    wd = dev_bf16(base["w"]).repeat(n // block, 1)
+    colt = torch.as_tensor(cols, device="cuda")
+    wd[colt] = dev_bf16(own)
+    qw = api.quantize_pack(wd, bits)
+    del wd
+    torch.cuda.empty_cache()
+    xb, xs = dev_bf16(big["x"]), dev_bf16(base["x"])
+    yb, y16, y40 = api.dequant_gemm_grouped([(xb, qb), (xs[:16], qw), (xs, qw)], torch.bfloat16)
+    check_product(_rows_to_host(yb, rows), O.gemm_ref(big["x"][rows], _w16(big["w"], 4)), True, "grouped big")
+    w16 = _w16(own, bits)
+    for y, m in ((y16, 16), (y40, 40)):
+        check_product(y.index_select(1, colt).float().cpu().numpy(), O.gemm_ref(base["x"][:m], w16), True,
+                      f"grouped M={m}")
+    del yb, y16, y40, qw
+    torch.cuda.empty_cache()
