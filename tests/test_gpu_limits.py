@@ -258,3 +258,42 @@ def test_grouped_past_4gib(gpu_lib):
                       f"grouped M={m}")
     del yb, y16, y40, qw
     torch.cuda.empty_cache()
+
+
+def test_w4a6_chain_activation_codes_past_4gib(gpu_lib):
+    """E2M3 codes of X (1,398,272 x 4096, 4.30 GB in the tiled 32-row records;
+    bf16 input 11.5 GB), then the W4A6 product.  Whole 32-row blocks are
+    checked (the first, the two around the 4 GiB byte, the last): their
+    records bit for bit, then the product's rows."""
+    from oracle import fp4 as F
+    api = gpu_lib
+    k, n, block = 4096, 64, 256
+    m = 5462 * block
+    blk_bytes = 32 * k * 3 // 4                      # one 32-row record block
+    assert m * k * 3 // 4 > GIB4 and blk_bytes == (k // 128) * 3072
+    blocks = np.array([0, GIB4 // blk_bytes, GIB4 // blk_bytes + 1, m // 32 - 1])
+    rows = (blocks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    base = synth.random_case(111, block, n, k)
+    own = synth.random_case(112, len(rows), 16, k)["x"]
+    _case(f"fp6_quantize_rows + w4a6_gemm X codes past 4 GiB: M={m} N={n} K={k}")
+    xd = dev_bf16(base["x"]).repeat(m // block, 1)
+    rt = torch.as_tensor(rows, device="cuda")
+    xd[rt] = dev_bf16(own)
+    xq, xs = api.fp6_quantize_rows(xd, "e2m3")
+    del xd
+    torch.cuda.empty_cache()
+    xc, xsc = F.quantize_rows_fp6(own, "e2m3")
+    for i, b in enumerate(blocks):
+        got = xq[int(b) * blk_bytes:(int(b) + 1) * blk_bytes].cpu().numpy()
+        assert np.array_equal(got, F.pack_fp6_tiled(xc[32 * i:32 * (i + 1)])), f"records of block {b} differ"
+    assert np.array_equal(f32_bits(xs.index_select(0, rt).cpu().numpy()), f32_bits(xsc)), "row scales differ"
+    qw = api.fp4_quantize_pack(dev_bf16(base["w"]), "e2m1", tiled=True)
+    wc, ws = F.quantize_fp4_groups(base["w"], "e2m1")
+    ref = F.w4a6_ref(xc, xsc, wc, ws, "e2m1", "e2m3")
+    y = api.w4a6_gemm(xq, xs, "e2m3", qw, torch.float32)
+    yr = _rows_to_host(y, rows).astype(np.float64)
+    absref = F.w4a6_ref(xc & 31, xsc, wc & 7, ws, "e2m1", "e2m3")
+    assert np.all(np.abs(yr - ref) <= 2.0 ** -14 * absref + 1e-37)
+    check_product(yr, ref, False, "w4a6 X past 4 GiB")
+    del y, xq, xs
+    torch.cuda.empty_cache()
