@@ -297,3 +297,34 @@ def test_w4a6_chain_activation_codes_past_4gib(gpu_lib):
     check_product(yr, ref, False, "w4a6 X past 4 GiB")
     del y, xq, xs
     torch.cuda.empty_cache()
+
+
+def test_rotate_past_4gib(gpu_lib):
+    """The rotation pre-pass on 699,136 x 3072 bf16 rows (4.30 GB in; float32
+    out, 8.6 GB): rows from 699,051 on start past 4 GiB in the input.  Checked
+    rows within the float32 butterfly bound of the float64 oracle."""
+    import math
+    api = gpu_lib
+    d, h, block = 3072, 128, 256
+    n = 2731 * block
+    assert n * d * 2 > GIB4
+    base = synth.random_case(121, block, 16, d)["x"]
+    rows = np.unique(np.concatenate([[0, 1, 255, 256], np.arange(GIB4 // (2 * d) - 2, GIB4 // (2 * d) + 3),
+                                     np.arange(n - 40, n)]))
+    own = synth.random_case(122, len(rows), 16, d)["x"]
+    perm, signs = synth.rpbh_draw(d, 12)
+    _case(f"rpbh_rotate past 4 GiB: n={n} d={d} h={h}")
+    xd = dev_bf16(base).repeat(n // block, 1)
+    rt = torch.as_tensor(rows, device="cuda")
+    xd[rt] = dev_bf16(own)
+    y = api.rpbh_rotate(xd, torch.from_numpy(perm).cuda(), torch.from_numpy(signs).cuda(), h, torch.float32)
+    got = _rows_to_host(y, rows).astype(np.float64)
+    del y, xd
+    torch.cuda.empty_cache()
+    import oracle.rpbh_oracle as R
+    ref = R.rpbh_rotate(own, perm, signs, h)
+    t = np.abs(np.asarray(own, dtype=np.float64)[:, perm])
+    blk = t.reshape(len(rows), d // h, h).sum(axis=2, keepdims=True)
+    bound = np.broadcast_to((math.log2(h) + 1) * 2.0 ** -24 * blk / math.sqrt(h),
+                            (len(rows), d // h, h)).reshape(len(rows), d) * 1.01 + 1e-37
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / bound))
