@@ -286,12 +286,13 @@ def alloc_suite(args):
         w = torch.where(mask, w * 10.0, w).to(torch.bfloat16)
         ws.append(w)
     nweights = sum(w.numel() for w in ws)
-    api.mse_table(ws[:2])                                  # warm-up
+    api.sse_table(ws[:2])                                  # warm-up
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    mse, nparams = api.mse_table(ws)
+    sse, nparams = api.sse_table(ws)
     torch.cuda.synchronize()
     t_tables = time.perf_counter() - t0
+    mse = sse / nparams[:, None].astype(np.float64)        # the oracle's per-weight tables
     # the dominant kernel alone: events around one tensor's table on the stream
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -318,7 +319,7 @@ def alloc_suite(args):
     }
     for target in (4.0, 5.0, 6.0):
         t0 = time.perf_counter()
-        bits, info = api.pd_allocate(mse, nparams, target, t_init, iters=500)
+        bits, info = api.pd_allocate(sse, nparams, target, t_init, iters=500)
         t_search = time.perf_counter() - t0
         # the oracle's search on the same tables (numpy on the host)
         t0 = time.perf_counter()
@@ -338,7 +339,7 @@ def alloc_suite(args):
         }
     # the allocation drives the block's widths: every tensor packed at its width
     # (5.0 bpw), then each block's ten products at 16 tokens in one grouped launch
-    bits5, _ = api.pd_allocate(mse, nparams, 5.0, t_init, iters=500)
+    bits5, _ = api.pd_allocate(sse, nparams, 5.0, t_init, iters=500)
     qws = [api.quantize_pack(w, int(b)) for w, b in zip(ws, bits5)]
     del ws
     xs = {k: torch.randn((16, k), generator=gen, device=dev).to(torch.bfloat16) for k in (5120, 13824)}

@@ -44,7 +44,7 @@ SIGNATURES = {
     "ddg_dequantize": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp]),
     "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
     "ddg_dequant_gemm_grouped": (_c_int, [ctypes.POINTER(GemmDesc), _c_int, _vp]),
-    "ddg_lowrank_workspace_bytes": (_c_int, [_c_i64, _c_int, ctypes.POINTER(_sz)]),
+    "ddg_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.POINTER(_sz)]),
     "ddg_quant_sse": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ddg_pd_allocate": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64), _c_int,
                                  ctypes.POINTER(_c_int), _c_int, ctypes.c_double,
@@ -357,10 +357,11 @@ def dequant_gemm_grouped(items, out_dtype=torch.bfloat16):
     return outs
 
 
-def lowrank_workspace_bytes(m: int, r: int) -> int:
+def workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    """Workspace bytes of lowrank_fused_gemm for an m x k input, an n x k
+    weight and rank r."""
     b = ctypes.c_size_t()
-    _check(load_library().ddg_lowrank_workspace_bytes(m, r, ctypes.byref(b)),
-           "ddg_lowrank_workspace_bytes")
+    _check(load_library().ddg_workspace_bytes(m, n, k, r, ctypes.byref(b)), "ddg_workspace_bytes")
     return b.value
 
 
@@ -383,7 +384,7 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
     if lora_up.shape != (qw.n, r):
         raise ValueError("lora_up must be (out x r)")
     y = _out(x, qw.n, out_dtype, out)
-    need = lowrank_workspace_bytes(x.shape[0], r)
+    need = workspace_bytes(x.shape[0], qw.n, qw.k, r)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _check(load_library().ddg_lowrank_fused_gemm(
@@ -417,39 +418,36 @@ def quant_sse(w: torch.Tensor):
     return rows[:n], total
 
 
-def mse_table(weights):
-    """(mse N x 5, nparams N) numpy arrays: per-weight quantization error of
-    every tensor at widths 3..7 (the tables the allocation searches over).
-    Weights padded along the input dimension count their real elements."""
+def sse_table(weights):
+    """(sse N x 5, nparams N) numpy arrays: the squared-error sums of every
+    tensor at widths 3..7 (the totals of ddg_quant_sse, the tables the
+    allocation searches over) and each tensor's element count (weights padded
+    along the input dimension count their real elements)."""
     import numpy as np
-    mse = np.empty((len(weights), 5), dtype=np.float64)
-    nparams = np.empty(len(weights), dtype=np.int64)
-    totals = []
-    for w in weights:
-        totals.append(quant_sse(w)[1])
-    for i, (w, t) in enumerate(zip(weights, totals)):
-        nparams[i] = w.numel()
-        mse[i] = t.cpu().numpy() / nparams[i]
-    return mse, nparams
+    totals = [quant_sse(w)[1] for w in weights]
+    sse = np.stack([t.cpu().numpy() for t in totals]) if totals else np.empty((0, 5))
+    nparams = np.array([w.numel() for w in weights], dtype=np.int64)
+    return sse, nparams
 
 
-def pd_allocate(mse, nparams, target_bpw: float, t_init, iters: int = 500,
+def pd_allocate(sse, nparams, target_bpw: float, t_init, iters: int = 500,
                 candidates=PD_CANDIDATES):
     """PD-guided widths for every tensor (host-side search in the library).
-    t_init: restarts x N starting parameters.  Returns (bits, info dict)."""
+    sse: N x len(candidates) squared-error sums (sse_table); t_init: restarts
+    x N starting parameters.  Returns (bits, info dict)."""
     import numpy as np
-    mse = np.ascontiguousarray(mse, dtype=np.float64)
+    sse = np.ascontiguousarray(sse, dtype=np.float64)
     nparams = np.ascontiguousarray(nparams, dtype=np.int64)
     t_init = np.ascontiguousarray(t_init, dtype=np.float64)
     cand = np.ascontiguousarray(candidates, dtype=np.int32)
     n = nparams.shape[0]
-    if mse.shape != (n, cand.shape[0]) or t_init.ndim != 2 or t_init.shape[1] != n:
-        raise ValueError("mse must be N x len(candidates) and t_init restarts x N")
+    if sse.shape != (n, cand.shape[0]) or t_init.ndim != 2 or t_init.shape[1] != n:
+        raise ValueError("sse must be N x len(candidates) and t_init restarts x N")
     bits = np.empty(n, dtype=np.int32)
     info = np.empty(3, dtype=np.float64)
     dp = ctypes.POINTER(ctypes.c_double)
     _check(load_library().ddg_pd_allocate(
-        mse.ctypes.data_as(dp), nparams.ctypes.data_as(ctypes.POINTER(_c_i64)), n,
+        sse.ctypes.data_as(dp), nparams.ctypes.data_as(ctypes.POINTER(_c_i64)), n,
         cand.ctypes.data_as(ctypes.POINTER(_c_int)), cand.shape[0], float(target_bpw),
         t_init.ctypes.data_as(dp), t_init.shape[0], iters, bits.ctypes.data_as(ctypes.POINTER(_c_int)),
         info.ctypes.data_as(dp)), "ddg_pd_allocate")

@@ -154,6 +154,29 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream) {
   return by_bits<LargeF>(bits, a, stream);
 }
 
+// Bytes of the low-rank intermediate T (M x r bf16), rounded up to 256.
+size_t lowrank_t_bytes(int64_t m, int r) { return (size_t)((m * r * 2 + 255) / 256 * 256); }
+
+// T = bf16(X L1) into t, then the product with the branch in its epilogue.
+hipError_t launch_lowrank(const void* x, int64_t m, int64_t k, const uint8_t* packed, const float* scales,
+                          int bits, int64_t n, const void* lora_down, const void* lora_up, int r, void* y,
+                          int y_dtype, __bf16* t, hipStream_t stream) {
+  if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
+                                           static_cast<const __bf16*>(lora_down), t, (int)m,
+                                           (int)k, r, stream))
+    return e;
+  ddg::GemmArgs a{};
+  a.x = static_cast<const __bf16*>(x);
+  a.packed = packed;
+  a.scales = scales;
+  a.y = y;
+  a.t = t;
+  a.lora_up = static_cast<const __bf16*>(lora_up);
+  a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = r;
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return launch_product(a, bits, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,11 +350,11 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
   return DDG_OK;
 }
 
-int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes) {
+int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
   if (!bytes) return DDG_ERR_ARG;
-  if (m < 0 || m > kMaxDim || r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
-  const int64_t raw = m * r * 2;
-  *bytes = (size_t)((raw + 255) / 256 * 256);
+  if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || k < 0 || r < 8 || r > 128 || r % 8)
+    return DDG_ERR_SHAPE;
+  *bytes = lowrank_t_bytes(m, r);
   return DDG_OK;
 }
 
@@ -345,26 +368,11 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
   if (!lora_down || !lora_up || !workspace) return DDG_ERR_ARG;
   if (!aligned(lora_down, 16) || !aligned(lora_up, 16) || !aligned(workspace, 16))
     return DDG_ERR_ALIGN;
-  size_t need = 0;
-  ddg_lowrank_workspace_bytes(m, r, &need);
-  if (workspace_bytes < need) return DDG_ERR_WORKSPACE;
+  if (workspace_bytes < lowrank_t_bytes(m, r)) return DDG_ERR_WORKSPACE;
   int cus = 0;
   if (int st = device_info(&cus)) return st;
-  __bf16* t = static_cast<__bf16*>(workspace);
-  if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
-                                           static_cast<const __bf16*>(lora_down), t, (int)m,
-                                           (int)k, r, stream))
-    return hip_status(e);
-  ddg::GemmArgs a{};
-  a.x = static_cast<const __bf16*>(x);
-  a.packed = packed;
-  a.scales = scales;
-  a.y = y;
-  a.t = t;
-  a.lora_up = static_cast<const __bf16*>(lora_up);
-  a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = r;
-  a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(launch_product(a, bits, stream));
+  return hip_status(launch_lowrank(x, m, k, packed, scales, bits, n, lora_down, lora_up, r, y, y_dtype,
+                                   static_cast<__bf16*>(workspace), stream));
 }
 
 int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,

@@ -219,10 +219,10 @@ extern "C" int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, d
              : DDG_ERR_HIP;
 }
 
-extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int* candidates,
+extern "C" int ddg_pd_allocate(const double* sse, const int64_t* nparams, int n, const int* candidates,
                                int ncand, double target_bpw, const double* t_init, int restarts,
                                int iters, int* bits_out, double* info) {
-  if (!mse || !nparams || !candidates || !t_init || !bits_out) return DDG_ERR_ARG;
+  if (!sse || !nparams || !candidates || !t_init || !bits_out) return DDG_ERR_ARG;
   if (n < 1 || ncand < 2 || ncand > 8 || restarts < 1 || iters < 1) return DDG_ERR_SHAPE;
   for (int c = 1; c < ncand; ++c)
     if (candidates[c] <= candidates[c - 1]) return DDG_ERR_ARG;
@@ -231,9 +231,15 @@ extern "C" int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n,
   for (int i = 0; i < n; ++i) {
     if (nparams[i] <= 0) return DDG_ERR_ARG;
     for (int c = 0; c < ncand; ++c)
-      if (!(mse[(int64_t)i * ncand + c] >= 0.0) || !std::isfinite(mse[(int64_t)i * ncand + c]))
+      if (!(sse[(int64_t)i * ncand + c] >= 0.0) || !std::isfinite(sse[(int64_t)i * ncand + c]))
         return DDG_ERR_ARG;
   }
+  // per-weight errors: the tensor's squared-error sum over its weight count
+  std::vector<double> mse_v((size_t)n * ncand);
+  for (int i = 0; i < n; ++i)
+    for (int c = 0; c < ncand; ++c)
+      mse_v[(size_t)i * ncand + c] = sse[(int64_t)i * ncand + c] / (double)nparams[i];
+  const double* mse = mse_v.data();
   // weights of the tensors, and the error table in percent of the uniform
   // allocation at the candidate nearest the target
   double tot = 0.0;

@@ -164,12 +164,13 @@ typedef struct ddg_gemm_desc {
 int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream);
 
 /*
- * Workspace bytes ddg_lowrank_fused_gemm needs for M rows and rank r
- * (the M x r bf16 intermediate T, rounded up to 256 bytes).  Host-only.
- * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m < 0, r outside 8..128 or not a
- * multiple of 8).
+ * Workspace bytes ddg_lowrank_fused_gemm needs for an M x K input, an N x K
+ * weight and rank r: the M x r bf16 intermediate T, rounded up to 256 bytes.
+ * Host-only.
+ * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m, n or k negative or m, n above
+ * 2^31 - 1, r outside 8..128 or not a multiple of 8).
  */
-int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes);
+int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
 
 /*
  * Y = X * w_hat^T + T * L2 with T = bf16(X * L1)  ([SVDQ] 技术原理详解: a
@@ -181,7 +182,7 @@ int ddg_lowrank_workspace_bytes(int64_t m, int r, size_t* bytes);
  * T is computed in float32 and rounded to bf16 once (the branch is a bf16
  * product); the branch term T * L2 is summed into the same float32
  * accumulator as the main product before y is written.
- *   workspace  device scratch of at least ddg_lowrank_workspace_bytes(M, r)
+ *   workspace  device scratch of at least ddg_workspace_bytes(M, N, K, r)
  *              bytes; its contents are scratch (no initial state needed).
  * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_WORKSPACE,
@@ -212,8 +213,10 @@ int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_
 
 /*
  * PD-guided mixed-precision bit allocation ([WDQ] §3.2).  Host only: every
- * pointer is a host pointer and nothing runs on the GPU.  Minimises the
- * parameter-weighted error sum_i n_i mse_i(b_i) / sum_i n_i subject to
+ * pointer is a host pointer and nothing runs on the GPU.  With the per-weight
+ * errors mse_i(c) = sse_i(c) / n_i (float64 division), minimises the
+ * parameter-weighted error sum_i n_i mse_i(b_i) / sum_i n_i (the section's
+ * sum of squared errors over the weight count) subject to
  * sum_i n_i b_i / sum_i n_i <= target_bpw by the section's relaxation: one
  * parameter per tensor, b = bmin + sigmoid(t) (bmax - bmin); a softmax over
  * the candidates of -|b - c| / temp, temp = max(2 (1 - it/iters), 0.05),
@@ -230,8 +233,8 @@ int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_
  * budget, else the lowest bpw; ties go to the earlier restart.  Restarts run
  * on up to 16 host threads started and joined inside the call (the inputs are
  * only read meanwhile); the result does not depend on their number.
- *   mse        n x ncand per-weight errors (row i: tensor i, column c: width
- *              candidates[c]); finite, >= 0.
+ *   sse        n x ncand squared-error sums (row i: tensor i, column c: width
+ *              candidates[c]; the totals of ddg_quant_sse); finite, >= 0.
  *   nparams    n weight counts, > 0.
  *   candidates ncand (2..8) increasing widths; target_bpw within their range.
  *   t_init     restarts x n starting parameters (the random draws).
@@ -241,7 +244,7 @@ int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_
  * increasing, target out of range), DDG_ERR_SHAPE (n < 1, ncand outside
  * 2..8, restarts or iters < 1).
  */
-int ddg_pd_allocate(const double* mse, const int64_t* nparams, int n, const int* candidates,
+int ddg_pd_allocate(const double* sse, const int64_t* nparams, int n, const int* candidates,
                     int ncand, double target_bpw, const double* t_init, int restarts,
                     int iters, int* bits_out, double* info);
 

@@ -53,7 +53,7 @@ import numpy as np
 
 from .ddg_oracle import dequant_f32, quantize_groups
 
-__all__ = ["PD_CANDIDATES", "quant_sse_rows", "mse_table", "pd_objective", "pd_loss_grad",
+__all__ = ["PD_CANDIDATES", "quant_sse_rows", "sse_table", "mse_table", "pd_objective", "pd_loss_grad",
            "pd_search", "pd_exhaustive", "round_to_budget", "pd_step"]
 
 PD_CANDIDATES = (3, 4, 5, 6, 7)
@@ -71,15 +71,23 @@ def quant_sse_rows(w, bits: int) -> np.ndarray:
     return np.sum(d * d, axis=1)
 
 
-def mse_table(weights, candidates=PD_CANDIDATES):
-    """(mse N x C, nparams N): per-weight MSE of every tensor at every width."""
-    mse = np.empty((len(weights), len(candidates)), dtype=np.float64)
+def sse_table(weights, candidates=PD_CANDIDATES):
+    """(sse N x C, nparams N): the §3.2 objective's ||W_i - Q_c(W_i)||_F^2 of
+    every tensor at every width, and each tensor's element count."""
+    sse = np.empty((len(weights), len(candidates)), dtype=np.float64)
     n = np.empty(len(weights), dtype=np.int64)
     for i, w in enumerate(weights):
         n[i] = np.asarray(w).size
         for j, b in enumerate(candidates):
-            mse[i, j] = quant_sse_rows(w, b).sum() / n[i]
-    return mse, n
+            sse[i, j] = quant_sse_rows(w, b).sum()
+    return sse, n
+
+
+def mse_table(weights, candidates=PD_CANDIDATES):
+    """(mse N x C, nparams N): per-weight MSE of every tensor at every width,
+    the squared-error sum over the element count."""
+    sse, n = sse_table(weights, candidates)
+    return sse / n[:, None].astype(np.float64), n
 
 
 def pd_objective(mse, nparams, bits, candidates=PD_CANDIDATES):
@@ -145,9 +153,11 @@ def pd_loss_grad(t, lam, m, wgt, cand, target_bpw: float, temp: float):
 
 
 def pd_search(mse, nparams, target_bpw: float, t_init, iters: int = 500,
-              candidates=PD_CANDIDATES):
+              candidates=PD_CANDIDATES, trace=None):
     """The §3.2 search (readings R7-R12).  t_init: restarts x N starting
-    parameters.  Returns dict(bits, mse, bpw, restart)."""
+    parameters.  Returns dict(bits, mse, bpw, restart).  When `trace` is a
+    list, one dict per (restart, iteration) is appended to it: the restart,
+    the iteration, the temperature it used, and t and lambda after its update."""
     mse = np.asarray(mse, dtype=np.float64)
     n = np.asarray(nparams, dtype=np.float64)
     cand = np.asarray(candidates, dtype=np.float64)
@@ -167,6 +177,8 @@ def pd_search(mse, nparams, target_bpw: float, t_init, iters: int = 500,
             _, g, bpw = pd_loss_grad(t, lam, m, wgt, cand, target_bpw, temp)
             t = t - step * g
             lam = lam + step * (bpw - target_bpw)
+            if trace is not None:
+                trace.append({"restart": r, "it": it, "temp": temp, "t": t.copy(), "lam": lam})
         u = 1.0 / (1.0 + np.exp(-t))
         bits = round_to_budget(bmin + u * (bmax - bmin), n, target_bpw, candidates)   # R11
         e_r, p_r = pd_objective(mse, n, bits, candidates)

@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("ddg_quantize_pack", "ddg_dequant_gemm", "ddg_lowrank_fused_gemm",
-              "ddg_dequantize", "ddg_packed_bytes", "ddg_lowrank_workspace_bytes",
+              "ddg_dequantize", "ddg_packed_bytes", "ddg_workspace_bytes",
               "ddg_status_string", "ddg_version"):
         assert n in names
 
@@ -73,12 +73,14 @@ def test_packed_bytes_bad_bits(lib):
 
 def test_workspace_bytes(lib):
     b = ctypes.c_size_t()
-    assert lib.ddg_lowrank_workspace_bytes(4096, 32, ctypes.byref(b)) == OK and b.value == 4096 * 64
-    assert lib.ddg_lowrank_workspace_bytes(3, 8, ctypes.byref(b)) == OK and b.value == 256
-    assert lib.ddg_lowrank_workspace_bytes(0, 32, ctypes.byref(b)) == OK and b.value == 0
+    assert lib.ddg_workspace_bytes(4096, 3072, 3072, 32, ctypes.byref(b)) == OK and b.value == 4096 * 64
+    assert lib.ddg_workspace_bytes(3, 16, 128, 8, ctypes.byref(b)) == OK and b.value == 256
+    assert lib.ddg_workspace_bytes(0, 16, 128, 32, ctypes.byref(b)) == OK and b.value == 0
+    assert lib.ddg_workspace_bytes(64, -1, 128, 32, ctypes.byref(b)) == E_SHAPE
+    assert lib.ddg_workspace_bytes(64, 16, -128, 32, ctypes.byref(b)) == E_SHAPE
     for r in (0, 4, 12, 136, -8):
-        assert lib.ddg_lowrank_workspace_bytes(64, r, ctypes.byref(b)) == E_SHAPE
-    assert lib.ddg_lowrank_workspace_bytes(64, 32, None) == E_ARG
+        assert lib.ddg_workspace_bytes(64, 16, 128, r, ctypes.byref(b)) == E_SHAPE
+    assert lib.ddg_workspace_bytes(64, 16, 128, 32, None) == E_ARG
 
 
 def test_quantize_pack_rejects_bad_arguments(lib):
@@ -272,3 +274,4 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     assert call(xq=MISALIGNED) == E_ALIGN and call(packed=FAKE + 8) == E_ALIGN
     assert call(ws=FAKE + 2) == E_ALIGN and call(y=FAKE + 1) == E_ALIGN
     assert call(m=0, xq=None, xs=None, packed=None, ws=None, y=None) == OK
+

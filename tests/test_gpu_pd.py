@@ -56,7 +56,7 @@ def test_quant_sse_empty(gpu_lib):
 
 
 def test_allocation_end_to_end(gpu_lib):
-    _case("mse_table on the GPU + library search against the oracle")
+    _case("sse_table on the GPU + library search against the oracle")
     rng = np.random.default_rng(11)
     ws = []
     for i in range(10):
@@ -65,13 +65,14 @@ def test_allocation_end_to_end(gpu_lib):
         else:
             w = rng.normal(0, 0.02 * (1 + i / 5), size=(64, 1024))
         ws.append(synth.to_bf16(w))
-    mse_gpu, n_gpu = gpu_lib.mse_table([dev_bf16(w) for w in ws])
-    mse_ref, n_ref = O.mse_table(ws)
+    sse_gpu, n_gpu = gpu_lib.sse_table([dev_bf16(w) for w in ws])
+    sse_ref, n_ref = O.sse_table(ws)
+    mse_ref = sse_ref / n_ref[:, None]
     assert np.array_equal(n_gpu, n_ref)
-    assert np.allclose(mse_gpu, mse_ref, rtol=1e-12, atol=0.0)
+    assert np.allclose(sse_gpu, sse_ref, rtol=1e-12, atol=0.0)
     t_init = 0.5 * np.random.default_rng(12).standard_normal((8, len(ws)))
     for target in (4.0, 4.7, 5.0):
-        bits, info = gpu_lib.pd_allocate(mse_gpu, n_gpu, target, t_init, iters=300)
+        bits, info = gpu_lib.pd_allocate(sse_gpu, n_gpu, target, t_init, iters=300)
         ro = O.pd_search(mse_ref, n_ref, target, t_init, iters=300)
         assert np.array_equal(bits, ro["bits"]), (target, bits, ro["bits"])
         assert info["bpw"] <= target + 1e-9
@@ -87,9 +88,9 @@ def test_allocation_drives_a_grouped_block(gpu_lib):
     shapes = [(256, 512), (256, 512), (256, 512), (256, 512), (704, 512), (512, 768)]
     ws = [synth.to_bf16(rng.normal(0, 0.01 * (1 + i), size=s)) for i, s in enumerate(shapes)]
     ws[3] = synth.to_bf16(rng.standard_t(3, size=shapes[3]) * 0.02)
-    mse, nparams = gpu_lib.mse_table([dev_bf16(w) for w in ws])
+    sse, nparams = gpu_lib.sse_table([dev_bf16(w) for w in ws])
     t_init = 0.5 * np.random.default_rng(32).standard_normal((6, len(ws)))
-    bits, info = gpu_lib.pd_allocate(mse, nparams, 5.0, t_init, iters=300)
+    bits, info = gpu_lib.pd_allocate(sse, nparams, 5.0, t_init, iters=300)
     assert info["bpw"] <= 5.0 + 1e-9 and len(set(bits.tolist())) > 1
     items, refs = [], []
     for i, (w, b) in enumerate(zip(ws, bits)):
