@@ -52,6 +52,8 @@ SIGNATURES = {
                                  ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_double)]),
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
+    "ddg_lowrank_fused_gemm_noalloc": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
+                                                _c_int, _vp, _c_int, _vp]),
     "ddg_rpbh_rotate": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp]),
     "ddg_fp4_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
     "ddg_fp8_quantize_rows": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
@@ -394,6 +396,31 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream_ptr(x.device)),
         "ddg_lowrank_fused_gemm")
     return y
+
+
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
+
+
+def lowrank_fused_gemm_noalloc(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
+                               lora_up: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """lowrank_fused_gemm without a workspace (for callers that cannot
+    allocate): T goes to the library's own device array, shared by every call
+    on the GPU.  Allocates nothing: x (m x k), lora_down (r x k), lora_up
+    (n x r) and out (m x n) must already have the shapes of the record."""
+    for t, name in ((x, "x"), (lora_down, "lora_down"), (lora_up, "lora_up"), (out, "out")):
+        _require_cuda(t, name)
+    r = lora_down.shape[0]
+    if (x.dtype != torch.bfloat16 or lora_down.dtype != torch.bfloat16 or lora_up.dtype != torch.bfloat16
+            or x.dim() != 2 or x.shape[1] != qw.k or lora_down.shape != (r, qw.k)
+            or lora_up.shape != (qw.n, r) or out.shape != (x.shape[0], qw.n)
+            or out.dtype not in (torch.bfloat16, torch.float32)):
+        raise ValueError("x, lora_down, lora_up (bf16) and out must have the record's shapes")
+    _check(load_library().ddg_lowrank_fused_gemm_noalloc(
+        x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
+        qw.n, lora_down.data_ptr(), lora_up.data_ptr(), r, out.data_ptr(),
+        DDG_F32 if out.dtype == torch.float32 else DDG_BF16, _stream_ptr(x.device)),
+        "ddg_lowrank_fused_gemm_noalloc")
+    return out
 
 
 # ------------------------------------------------------------------ bit allocation

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "ddg.h"
 #include "ddg_launch.hpp"
@@ -374,6 +375,61 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
   return hip_status(launch_lowrank(x, m, k, packed, scales, bits, n, lora_down, lora_up, r, y, y_dtype,
                                    static_cast<__bf16*>(workspace), stream));
 }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The fused low-rank product without a caller workspace: T lives in a
+// file-scope device array of DDG_NOALLOC_SCRATCH_BYTES bytes.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); its device address is looked up once per device, with that device
+// current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DDG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device).  DDG_ERR_HIP when the lookup fails.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DDG_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DDG_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DDG_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DDG_OK;
+}
+}  // namespace
+
+extern "C" int ddg_lowrank_fused_gemm_noalloc(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                                              const float* scales, int bits, int64_t n, const void* lora_down,
+                                              const void* lora_up, int r, void* y, int y_dtype,
+                                              hipStream_t stream) {
+  if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
+  if (r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!lora_down || !lora_up) return DDG_ERR_ARG;
+  if (!aligned(lora_down, 16) || !aligned(lora_up, 16)) return DDG_ERR_ALIGN;
+  if (lowrank_t_bytes(m, r) > (size_t)DDG_NOALLOC_SCRATCH_BYTES) return DDG_ERR_WORKSPACE;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  void* t = nullptr;
+  if (int st = scratch_ptr(&t)) return st;
+  return hip_status(launch_lowrank(x, m, k, packed, scales, bits, n, lora_down, lora_up, r, y, y_dtype,
+                                   static_cast<__bf16*>(t), stream));
+}
+
+extern "C" {
 
 int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int32_t* perm,
                     const int8_t* signs, int h, void* out, int out_dtype, hipStream_t stream) {

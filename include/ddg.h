@@ -195,6 +195,26 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ddg_lowrank_fused_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results without `workspace`.  T goes to
+ * a device array of DDG_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends (the
+ * first call on a GPU looks up its address; no call allocates).  Every call on
+ * a GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and give undefined results; calls on one stream are
+ * ordered and safe.  Requirements and errors as ddg_lowrank_fused_gemm, plus
+ * DDG_ERR_WORKSPACE when T needs more than the array (M * r * 2 bytes, rounded
+ * up to 256, above DDG_NOALLOC_SCRATCH_BYTES: M * r up to 4,194,304, e.g.
+ * 32768 tokens at rank 128).
+ */
+#define DDG_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+int ddg_lowrank_fused_gemm_noalloc(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                                   const float* scales, int bits, int64_t n,
+                                   const void* lora_down, const void* lora_up, int r,
+                                   void* y, int y_dtype, hipStream_t stream);
+
+/*
  * Quantization error of an N x K weight at every width 3..7 ([WDQ] §3.2:
  * the per-tensor error tables the bit allocation searches over; §3.1: the
  * quantizer of ddg_quantize_pack, float32 arithmetic bit for bit):

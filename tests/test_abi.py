@@ -275,3 +275,17 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     assert call(ws=FAKE + 2) == E_ALIGN and call(y=FAKE + 1) == E_ALIGN
     assert call(m=0, xq=None, xs=None, packed=None, ws=None, y=None) == OK
 
+
+def test_noalloc_lowrank_host_checks(lib):
+    """The workspace-free low-rank product refuses, on the host and before
+    any launch, a T larger than the library's device array (8 MiB: M * r up
+    to 4,194,304) and the shapes the workspace call refuses."""
+    FAKE = 1 << 20
+    def call(m=16, k=128, bits=4, n=16, r=32, ld=FAKE, y=FAKE):
+        return lib.ddg_lowrank_fused_gemm_noalloc(FAKE, m, k, FAKE, FAKE, bits, n, ld, FAKE, r, y, 0, None)
+    assert call(m=32769, r=128) == E_WS
+    assert call(m=4194305, r=8) == E_WS
+    assert call(r=4) == E_SHAPE and call(r=136) == E_SHAPE and call(r=12) == E_SHAPE
+    assert call(k=100) == E_SHAPE and call(n=20) == E_SHAPE and call(bits=8) == E_ARG
+    assert call(ld=0) == E_ARG and call(ld=FAKE + 8) == E_ALIGN
+    assert call(m=0) == OK
