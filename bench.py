@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' keys (workloads 3, 4 and 5)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the oracle's GEMM sample time")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
@@ -723,6 +725,151 @@ def cpu_baseline(w, x, budget_s):
     }
 
 
+def _median_burst_ms(torch, fn, count, repeats=REPEATS):
+    """Median over `repeats` bursts of the average duration of `count`
+    back-to-back calls fn(i), HIP events on the current stream."""
+    import statistics
+    stream = torch.cuda.current_stream()
+    out = []
+    for r in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(count):
+            fn(r * count + i)
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) / count)
+    return float(statistics.median(out))
+
+
+def _copies(q0, nbytes):
+    """Records of q0's weight totalling >= 1 GiB of packed bytes and scales."""
+    n = max(2, -(-ROTATE_BYTES // nbytes))
+    return [q0] + [dataclasses.replace(q0, packed=q0.packed.clone(), scales=q0.scales.clone())
+                   for _ in range(n - 1)]
+
+
+def workload_lines(api, synth, torch, steps, warmup):
+    """The other workloads the metric is quoted over, each timed as back-to-back
+    launches of its kernels (median of 5 bursts), weights rotated over >= 1 GiB
+    of packed copies, inputs drawn on the GPU with the workloads' shapes and
+    distributions (seeded; bf16):
+      workload3_m4096   the MLP pair (up 12288x3072, down 3072x12288, Student-t
+                        weights) at 3/5/6/7 bits, 4096 tokens: TFLOP/s;
+      workload4_lowrank the rank-32 branch + 4-bit residual of a 3072x3072
+                        weight at 4096 tokens: the fused call, and the residual's
+                        product alone beside it (their difference is the branch:
+                        the T pre-pass and the epilogue term);
+      workload5_m32760  the four Wan-14B block linears at their drawn widths,
+                        32760 tokens (one by one and grouped): TFLOP/s;
+      workload5_m16     the same at 16 tokens: packed-weight GB/s (one by one and
+                        grouped)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    out = {}
+
+    def randn(shape, std=1.0):
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+
+    def tflops(m, n, k, ms):
+        t = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 2), "TFLOPs": round(t, 1), "frac_of_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4)}
+
+    def gbps(nbytes, ms):
+        g = nbytes / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "packed_weight_GBps": round(g, 1),
+                "frac_of_hbm_peak": round(g / PEAK_HBM_GBPS, 4)}
+
+    def burst(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        return _median_burst_ms(torch, fn, steps)
+
+    # workload 3: Student-t(4) weights, std 0.02
+    t4 = torch.distributions.StudentT(torch.tensor(4.0, device=dev))
+    w3 = {}
+    lines3 = {}
+    for which, (n, k) in (("up", (12288, 3072)), ("down", (3072, 12288))):
+        torch.manual_seed(3 + (which == "down"))
+        w = (t4.sample((n, k)) * (0.02 / 2 ** 0.5)).to(torch.bfloat16)
+        x = randn((4096, k))
+        y = torch.empty((4096, n), dtype=torch.bfloat16, device=dev)
+        for bits in (3, 5, 6, 7):
+            q0 = api.quantize_pack(w, bits)
+            qs = _copies(q0, q0.packed.numel() + q0.scales.numel() * 4)
+            ms = burst(lambda i: api.dequant_gemm(x, qs[i % len(qs)], out=y))
+            lines3.setdefault(which, {})[str(bits)] = tflops(4096, n, k, ms)
+            del qs, q0
+        del w, x, y
+    out["workload3_m4096"] = lines3
+    torch.cuda.empty_cache()
+
+    # workload 4: outlier weight, rank-32 branch, 4-bit residual
+    c4 = synth.config4(m=4096)
+    w4 = torch.from_numpy(c4["w"]).to(dev)
+    u, s_, v = torch.svd_lowrank(w4, q=40, niter=3)
+    root = s_[:32].sqrt()
+    lora_up = (u[:, :32] * root).to(torch.bfloat16).contiguous()             # N x r = L2^T
+    lora_down = (v[:, :32] * root).t().contiguous().to(torch.bfloat16)        # r x K = L1^T
+    resid = (w4 - lora_up.float() @ lora_down.float()).contiguous()
+    q0 = api.quantize_pack(resid, 4)
+    qs = _copies(q0, q0.packed.numel() + q0.scales.numel() * 4)
+    x4 = torch.from_numpy(c4["x"]).to(dev, torch.bfloat16)
+    y4 = torch.empty((4096, 3072), dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(api.workspace_bytes(4096, 3072, 3072, 32), dtype=torch.uint8, device=dev)
+    ms_f = burst(lambda i: api.lowrank_fused_gemm(x4, qs[i % len(qs)], lora_down, lora_up,
+                                                  out=y4, workspace=wsp))
+    ms_m = burst(lambda i: api.dequant_gemm(x4, qs[i % len(qs)], out=y4))
+    fl_lr = 2.0 * 4096 * 32 * (3072 + 3072)
+    out["workload4_lowrank_m4096"] = {
+        "fused": dict(tflops(4096, 3072, 3072, ms_f),
+                      TFLOPs_with_branch=round((2.0 * 4096 * 3072 * 3072 + fl_lr) / (ms_f * 1e-3) / 1e12, 1)),
+        "residual_product_alone": tflops(4096, 3072, 3072, ms_m),
+        "branch_us": round((ms_f - ms_m) * 1e3, 2), "rank": 32}
+    del qs, q0, w4, resid, x4, y4, wsp
+    torch.cuda.empty_cache()
+
+    # workload 5: the block's linears at their drawn widths
+    bits_of = synth.config5_bits()
+    recs = {}
+    for name, (n, k) in synth.C5_SHAPES.items():
+        q0 = api.quantize_pack(randn((n, k), 0.02), bits_of[name])
+        recs[name] = (q0, _copies(q0, q0.packed.numel() + q0.scales.numel() * 4))
+    big, grouped_big = {}, []
+    for name, (n, k) in synth.C5_SHAPES.items():
+        x = randn((32760, k))
+        y = torch.empty((32760, n), dtype=torch.bfloat16, device=dev)
+        q = recs[name][1][:2]
+        ms = burst(lambda i: api.dequant_gemm(x, q[i % 2], out=y))
+        big[name] = dict(tflops(32760, n, k, ms), bits=bits_of[name])
+        grouped_big.append((x, q[0], y))
+    ms = burst(lambda i: api.dequant_gemm_grouped(grouped_big))
+    flops = sum(2.0 * 32760 * n * k for n, k in synth.C5_SHAPES.values())
+    big["grouped"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                      "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    out["workload5_m32760"] = big
+    del grouped_big, x, y
+    torch.cuda.empty_cache()
+    small, lins = {}, []
+    for name, (n, k) in synth.C5_SHAPES.items():
+        x = randn((16, k))
+        y = torch.empty((16, n), dtype=torch.bfloat16, device=dev)
+        q0, qs = recs[name]
+        nbytes = q0.packed.numel() + q0.scales.numel() * 4
+        ms = burst(lambda i: api.dequant_gemm(x, qs[i % len(qs)], out=y))
+        small[name] = dict(gbps(nbytes, ms), bits=bits_of[name], copies_rotated=len(qs))
+        lins.append((x, qs, y, nbytes))
+    ms = burst(lambda i: api.dequant_gemm_grouped([(x, qs[i % len(qs)], y) for x, qs, y, _ in lins]))
+    small["grouped"] = gbps(sum(L[3] for L in lins), ms)
+    out["workload5_m16"] = small
+    del recs, lins
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -764,19 +911,23 @@ def main():
     w_bytes = N * K * 2
     p_bytes = N * K * BITS // 8
     s_bytes = N * K // 128 * 4
-    n_copies = max(2, -(-ROTATE_BYTES // (w_bytes + p_bytes + s_bytes)))
+    # bf16 weight copies for the quantizer (>= 1 GiB with its outputs) and
+    # packed records for the products (>= 1 GiB of packed bytes and scales
+    # alone: the M=16 product reads nothing else)
+    n_w = max(2, -(-ROTATE_BYTES // (w_bytes + p_bytes + s_bytes)))
+    n_copies = max(n_w, -(-ROTATE_BYTES // (p_bytes + s_bytes)))
     w0 = torch.from_numpy(w_np).to(dev, torch.bfloat16)
-    ws = [w0.clone() for _ in range(n_copies)]
-    qws = [api.quantize_pack(wc, BITS) for wc in ws]
+    ws = [w0.clone() for _ in range(n_w)]
+    qws = [api.quantize_pack(ws[i % n_w], BITS) for i in range(n_copies)]
     x_big = torch.from_numpy(x_np).to(dev, torch.bfloat16)
     x_small = x_big[:M_SMALL].contiguous()
     y_big = torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev)
     y_small = torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev)
 
     def quantize_into(i):
-        q = qws[i]
+        q = qws[i % n_copies]
         st = api.load_library().ddg_quantize_pack(
-            ws[i].data_ptr(), api.DDG_BF16, N, K, BITS, q.packed.data_ptr(),
+            ws[i % n_w].data_ptr(), api.DDG_BF16, N, K, BITS, q.packed.data_ptr(),
             q.scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
         if st:
             raise api.DDGError(st, "ddg_quantize_pack")
@@ -792,7 +943,7 @@ def main():
         api.dequant_gemm(x_small, qws[(i + n_copies // 2) % n_copies], out=y_small)
 
     def step(i):
-        quantize_into(i % n_copies)
+        quantize_into(i)
         gemm_big(i)
         gemm_small(i)
 
@@ -826,7 +977,7 @@ def main():
     reps = {"q": [], "g": [], "s": []}
     for r in range(REPEATS):
         off = base + r * args.steps
-        reps["q"].append(burst_ms(lambda i: quantize_into(i % n_copies), args.steps, off))
+        reps["q"].append(burst_ms(quantize_into, args.steps, off))
         reps["g"].append(burst_ms(gemm_big, args.steps, off))
         reps["s"].append(burst_ms(gemm_small, args.steps, off))
     t_q, t_g, t_s = (float(np.median(reps[k])) for k in ("q", "g", "s"))
@@ -870,6 +1021,7 @@ def main():
                         "fp32 scales, X 4096x3072 bf16 ~N(0,1) (+ its first 16 rows)",
             "m": M_BIG, "m_small": M_SMALL, "n": N, "k": K, "bits": BITS, "y_dtype": "bf16",
             "weight_copies_rotated": n_copies,
+            "packed_bytes_rotated": n_copies * (p_bytes + s_bytes),
         },
         "kernels_ms": {"quantize_pack": round(t_q, 5), "dequant_gemm_m4096": round(t_g, 5),
                        "dequant_gemm_m16": round(t_s, 5)},
@@ -892,6 +1044,10 @@ def main():
             "traffic": traffic,
         },
     }
+    del ws, qws
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        out.update(workload_lines(api, synth, torch, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np, x_np, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -42,7 +42,7 @@ SIGNATURES = {
     "ddg_packed_bytes": (_c_int, [_c_i64, _c_i64, _c_int, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64)]),
     "ddg_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
     "ddg_dequantize": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _vp, _vp]),
-    "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
+    "ddg_dequant_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _sz, _vp]),
     "ddg_dequant_gemm_grouped": (_c_int, [ctypes.POINTER(GemmDesc), _c_int, _vp]),
     "ddg_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.POINTER(_sz)]),
     "ddg_quant_sse": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp]),
@@ -160,12 +160,33 @@ class QWeight:
     @classmethod
     def from_state_dict(cls, sd: dict, prefix: str, orig_in: Optional[int] = None,
                         device="cuda") -> "QWeight":
+        """The record's four fields, checked against one another on the host
+        (the kernels size their reads from n, k and bits): ValueError for a
+        width outside 3..7, a padded input dimension that is not a positive
+        multiple of 128, scales that are not whole rows of k/128, packed bytes
+        other than n*k*bits/8, or orig_in outside (k - 128, k]."""
         bits = int(sd[f"{prefix}_bw"])
         k = int(sd[f"{prefix}_nin"])
-        scales = sd[f"{prefix}_scales"].to(device=device, dtype=torch.float32).contiguous()
+        if bits < 3 or bits > 7:
+            raise ValueError(f"{prefix}_bw = {bits}: widths are 3..7")
+        if k <= 0 or k % GROUP:
+            raise ValueError(f"{prefix}_nin = {k}: not a positive multiple of {GROUP}")
+        scales = sd[f"{prefix}_scales"]
+        packed = sd[f"{prefix}_packed"]
+        if scales.dtype != torch.float32 or packed.dtype != torch.uint8:
+            raise ValueError(f"{prefix}: scales must be float32 and packed uint8")
+        if scales.numel() == 0 or scales.numel() % (k // GROUP):
+            raise ValueError(f"{prefix}_scales: {scales.numel()} values are not whole rows of {k // GROUP}")
         n = scales.numel() // (k // GROUP)
-        packed = sd[f"{prefix}_packed"].to(device=device, dtype=torch.uint8).contiguous()
-        return cls(packed, scales.view(n, k // GROUP), bits, n, k, orig_in or k)
+        pb, ns = packed_sizes(n, k, bits)
+        if packed.numel() != pb or scales.numel() != ns:
+            raise ValueError(f"{prefix}_packed: {packed.numel()} bytes, {pb} expected for {n} x {k} at {bits} bits")
+        orig = orig_in or k
+        if not k - GROUP < orig <= k:
+            raise ValueError(f"orig_in = {orig} does not pad to {k}")
+        scales = scales.to(device=device).contiguous().view(n, k // GROUP)
+        packed = packed.to(device=device).contiguous().view(-1)
+        return cls(packed, scales, bits, n, k, orig)
 
 
 def quantize_pack(w: torch.Tensor, bits: int) -> QWeight:
@@ -323,15 +344,39 @@ def _out(x: torch.Tensor, n: int, out_dtype, out):
     return out
 
 
+# Workspaces kept per (device, stream): calls on one stream are ordered, so
+# they may share one; calls on different streams get their own.
+_WORKSPACES: dict = {}
+
+
+def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def dequant_gemm(x: torch.Tensor, qw: QWeight, out_dtype=torch.bfloat16,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X @ w_hat^T with on-the-fly dequantization."""
+                 out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X @ w_hat^T with on-the-fly dequantization.  workspace: optional
+    scratch (uint8, at least workspace_bytes(m, n, k, 0) bytes) for the
+    stream-K form of products with few output tiles; by default one kept per
+    device and stream is used."""
     x = _prep_x(x, qw)
     y = _out(x, qw.n, out_dtype, out)
+    sp = _stream_ptr(x.device)
+    if workspace is None:
+        workspace = _cached_workspace(x.device, sp, workspace_bytes(x.shape[0], qw.n, qw.k, 0))
+    wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _check(load_library().ddg_dequant_gemm(
         x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
-        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
-        _stream_ptr(x.device)), "ddg_dequant_gemm")
+        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16, wp or None, wb,
+        sp), "ddg_dequant_gemm")
     return y
 
 
@@ -388,7 +433,7 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
     y = _out(x, qw.n, out_dtype, out)
     need = workspace_bytes(x.shape[0], qw.n, qw.k, r)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        workspace = _cached_workspace(x.device, _stream_ptr(x.device), max(need, 256))
     _check(load_library().ddg_lowrank_fused_gemm(
         x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
         qw.n, lora_down.data_ptr(), lora_up.data_ptr(), r, y.data_ptr(),

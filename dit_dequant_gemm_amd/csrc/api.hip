@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <random>
 
 #include "ddg.h"
 #include "ddg_launch.hpp"
@@ -113,8 +114,78 @@ int skinny_chunk(int g) {
   return kc;
 }
 
+template <int B>
+struct StreamKF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_streamk<B>(a...); }
+};
+
+// Stream-K for the large-M product: one workgroup per compute unit, at most
+// kSkMaxGrid (the workspace is sized for that many partial slots).
+constexpr int kSkMaxGrid = 256;
+constexpr size_t kSkSlotBytes = (size_t)ddg::kSkSlotFloats * sizeof(float);
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+int streamk_grid(int cus) { return std::min(cus, kSkMaxGrid) / ddg::kSkXcds * ddg::kSkXcds; }
+
+// K split across workgroups, from timings of 512- to 8192-token products of
+// the DiT shapes (whole tiles against each form):
+//   * split-K with `split` aligned K chunks when at most half the compute
+//     units would hold a tile: split x tiles workgroups, each chunk at least
+//     6 groups (so the exchange of partial sums stays small next to the work),
+//     at most 8 chunks;
+//   * stream-K for more tiles than workgroup slots (up to four per slot)
+//     when its even spread saves at least 30% of the iterations on the
+//     busiest compute unit (e.g. 320 tiles on 256 units: 241 us whole, 213
+//     stream-K); with fewer tiles than slots, the exchange and the staggered
+//     K positions (which defeat L2 sharing) cost more than the spread gains
+//     (192 tiles of K = 3072: 90 us whole, 105 stream-K; 160 tiles of K =
+//     5120: 112 us whole, 133 stream-K);
+//   * else whole tiles (0).
+// Returns the K chunks per tile (> 1: split-K), -1 for stream-K, 0 for tiles.
+int k_split_form(int64_t tiles, int groups, int grid) {
+  if (grid < ddg::kSkXcds || tiles < 1) return 0;
+  if (2 * tiles <= grid) {
+    const int split = (int)std::min<int64_t>({grid / tiles, groups / 6, ddg::kSkMaxSplit});
+    return split >= 2 ? split : 0;
+  }
+  if (tiles <= grid || tiles >= 4 * (int64_t)grid) return 0;
+  const double whole = (double)((tiles + grid - 1) / grid) * groups;
+  const double spread = (double)tiles * groups / grid;
+  return spread <= 0.7 * whole ? -1 : 0;
+}
+
+// Workspace bytes of stream-K for an m x n output (0 where it is never used).
+size_t streamk_bytes(int64_t m, int64_t n) {
+  if (m <= 64) return 0;
+  const int64_t tiles = ((m + ddg::kBM - 1) / ddg::kBM) * ((n + ddg::kBN - 1) / ddg::kBN);
+  if (tiles >= 4 * (int64_t)kSkMaxGrid) return 0;
+  return align256(kSkMaxGrid * kSkSlotBytes + kSkMaxGrid * sizeof(unsigned long long));
+}
+
+// Launch epochs: unique per launch, never zero, from a random start (so a
+// fresh workspace's contents are not mistaken for a published flag).
+std::atomic<unsigned long long> g_epoch{0};
+std::once_flag g_epoch_once;
+unsigned long long next_epoch() {
+  std::call_once(g_epoch_once, [] {
+    std::random_device rd;
+    const unsigned long long seed = ((unsigned long long)rd() << 32) ^ rd();
+    g_epoch.store(seed | 1ull);
+  });
+  unsigned long long e = g_epoch.fetch_add(1);
+  return e ? e : g_epoch.fetch_add(1);
+}
+
+// Scratch a product may use beyond its inputs and outputs (null: none).
+struct Scratch {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
 // Kernel choice for the product; fills a.tiles_* for the large kernel.
-hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream) {
+hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratch sk = {}, int cus = 0) {
   if (a.m <= 16) {
     // Wide outputs (at least 200 workgroups of 64 columns): the
     // weight-streaming kernel with an 8-way K split and X in registers.  Below
@@ -151,7 +222,20 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream) {
   // large kernel: 256 x 256 tiles
   a.tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
   a.tiles_n = (a.n + ddg::kBN - 1) / ddg::kBN;
-  if ((int64_t)a.tiles_m * a.tiles_n > kMaxDim) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  if (tiles > kMaxDim) return hipErrorInvalidValue;
+  const int grid_max = streamk_grid(cus);
+  const int form = sk.p != nullptr ? k_split_form(tiles, a.k / DDG_GROUP, grid_max) : 0;
+  if (form != 0 && sk.bytes >= (size_t)grid_max * kSkSlotBytes + (size_t)grid_max * sizeof(unsigned long long)) {
+    ddg::StreamK k{};
+    k.partials = static_cast<float*>(sk.p);
+    k.flags = reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(sk.p) + (size_t)grid_max * kSkSlotBytes);
+    k.epoch = next_epoch();
+    k.wpx = grid_max / ddg::kSkXcds;
+    k.split = form > 0 ? form : 0;
+    const int grid = form > 0 ? form * (int)tiles : grid_max;
+    return by_bits<StreamKF>(bits, a, k, grid, stream);
+  }
   return by_bits<LargeF>(bits, a, stream);
 }
 
@@ -161,7 +245,7 @@ size_t lowrank_t_bytes(int64_t m, int r) { return (size_t)((m * r * 2 + 255) / 2
 // T = bf16(X L1) into t, then the product with the branch in its epilogue.
 hipError_t launch_lowrank(const void* x, int64_t m, int64_t k, const uint8_t* packed, const float* scales,
                           int bits, int64_t n, const void* lora_down, const void* lora_up, int r, void* y,
-                          int y_dtype, __bf16* t, hipStream_t stream) {
+                          int y_dtype, __bf16* t, hipStream_t stream, Scratch sk = {}, int cus = 0) {
   if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
                                            static_cast<const __bf16*>(lora_down), t, (int)m,
                                            (int)k, r, stream))
@@ -175,7 +259,7 @@ hipError_t launch_lowrank(const void* x, int64_t m, int64_t k, const uint8_t* pa
   a.lora_up = static_cast<const __bf16*>(lora_up);
   a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = r;
   a.out_bf16 = y_dtype == DDG_BF16;
-  return launch_product(a, bits, stream);
+  return launch_product(a, bits, stream, sk, cus);
 }
 
 }  // namespace
@@ -233,9 +317,10 @@ int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t
 
 int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                      const float* scales, int bits, int64_t n, void* y, int y_dtype,
-                     hipStream_t stream) {
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
   if (m == 0) return DDG_OK;
+  if (workspace && !aligned(workspace, 16)) return DDG_ERR_ALIGN;
   int cus = 0;
   if (int st = device_info(&cus)) return st;
   ddg::GemmArgs a{};
@@ -247,7 +332,9 @@ int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
   a.lora_up = nullptr;
   a.m = (int)m; a.n = (int)n; a.k = (int)k; a.r = 0;
   a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(launch_product(a, bits, stream));
+  Scratch sk;
+  if (workspace) { sk.p = workspace; sk.bytes = workspace_bytes; }
+  return hip_status(launch_product(a, bits, stream, sk, cus));
 }
 
 int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream) {
@@ -353,9 +440,9 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
 
 int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
   if (!bytes) return DDG_ERR_ARG;
-  if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || k < 0 || r < 8 || r > 128 || r % 8)
+  if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || k < 0 || (r != 0 && (r < 8 || r > 128 || r % 8)))
     return DDG_ERR_SHAPE;
-  *bytes = lowrank_t_bytes(m, r);
+  *bytes = (r ? lowrank_t_bytes(m, r) : 0) + streamk_bytes(m, n);
   return DDG_OK;
 }
 
@@ -369,11 +456,17 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
   if (!lora_down || !lora_up || !workspace) return DDG_ERR_ARG;
   if (!aligned(lora_down, 16) || !aligned(lora_up, 16) || !aligned(workspace, 16))
     return DDG_ERR_ALIGN;
-  if (workspace_bytes < lowrank_t_bytes(m, r)) return DDG_ERR_WORKSPACE;
+  const size_t t_bytes = lowrank_t_bytes(m, r);
+  if (workspace_bytes < t_bytes) return DDG_ERR_WORKSPACE;
   int cus = 0;
   if (int st = device_info(&cus)) return st;
+  Scratch sk;
+  if (workspace_bytes > t_bytes) {
+    sk.p = static_cast<uint8_t*>(workspace) + t_bytes;
+    sk.bytes = workspace_bytes - t_bytes;
+  }
   return hip_status(launch_lowrank(x, m, k, packed, scales, bits, n, lora_down, lora_up, r, y, y_dtype,
-                                   static_cast<__bf16*>(workspace), stream));
+                                   static_cast<__bf16*>(workspace), stream, sk, cus));
 }
 
 }  // extern "C"
@@ -479,7 +572,7 @@ int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
 
 int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, float* xscales,
                           hipStream_t stream) {
-  if (m < 0 || m > kMaxDim || !k_ok(k) || !mul_ok(m, k) || !mul_ok(m * k, 2)) return DDG_ERR_SHAPE;
+  if (m < 0 || m > DDG_FP8_ROWS_MAX || !k_ok(k) || !mul_ok(m, k) || !mul_ok(m * k, 2)) return DDG_ERR_SHAPE;
   if (m == 0) return DDG_OK;
   if (!x || !xq || !xscales) return DDG_ERR_ARG;
   if (!aligned(x, 16) || !aligned(xq, 8) || !aligned(xscales, 4)) return DDG_ERR_ALIGN;
@@ -492,7 +585,8 @@ int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, floa
 int ddg_fp6_quantize_rows(const void* x, int64_t m, int64_t k, int fmt6, uint8_t* xq, float* xscales,
                           hipStream_t stream) {
   if (fmt6 != DDG_FP6_E2M3 && fmt6 != DDG_FP6_E3M2) return DDG_ERR_ARG;
-  if (m < 0 || m > kMaxDim || !k_ok(k) || !mul_ok(m + 31, k) || !mul_ok((m + 31) * k, 2)) return DDG_ERR_SHAPE;
+  if (m < 0 || m > DDG_FP6_ROWS_MAX || !k_ok(k) || !mul_ok(m + 31, k) || !mul_ok((m + 31) * k, 2))
+    return DDG_ERR_SHAPE;
   if (m == 0) return DDG_OK;
   if (!x || !xq || !xscales) return DDG_ERR_ARG;
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xscales, 4)) return DDG_ERR_ALIGN;

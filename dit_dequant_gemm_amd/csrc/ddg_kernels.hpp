@@ -203,15 +203,33 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gm;
 }
 
+// Tile t of the stream-K order: tiles in groups of 4 tile rows per column
+// strip (the ranges of an XCD then cover few X row strips and few weight
+// column strips).
+__device__ __forceinline__ void tile_coords_range(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 4;
+  const int group_size = GM * tiles_n;
+  const int gid = t / group_size;
+  const int first_m = gid * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_group = t - gid * group_size;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One 256 x 256 output tile (tile index `tile` of the product `args`); `lds`
-// is the workgroup's 128 KB LDS block.  Kernels: gemm_large_kernel (one
-// product) and gemm_grouped_large_kernel (several products in one launch).
+// Groups [g0, g1) of the 256 x 256 output tile (tm, tn) of the product
+// `args`, added into acc (8 row blocks of the 32x32 accumulator layout; wave w
+// holds columns 32w..32w+31).  With `lowrank` set, the branch term
+// T * lora_up^T of the tile is added first.  `lds` is the workgroup's 128 KB
+// LDS block; on return the last group's LDS reads may still be pending in
+// other waves (a barrier must precede any reuse of LDS).
 template <int B>
-__device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8_t* lds) {
+__device__ __forceinline__ void large_accumulate(const GemmArgs& args, int tm, int tn, int g0, int g1,
+                                                 bool lowrank, f32x16 (&acc)[kBM / 32], uint8_t* lds) {
   constexpr int RB = kBM / 32;          // 8 row blocks of 32
   constexpr int LA = 4;                 // A-operand look-ahead, in MFMA steps
   constexpr int RING = 8;               // A-operand ring (64 steps per group = 8 laps)
@@ -221,8 +239,6 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
-  int tm, tn;
-  tile_coords(tile, args.tiles_m, args.tiles_n, tm, tn);
   const int m0 = tm * kBM;
   const int nw0 = tn * kBN;
   const int K = args.k;
@@ -272,13 +288,7 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
                                             aoff[u >> 3]);
   };
 
-  f32x16 acc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
-
-  if (args.t != nullptr) {
+  if (lowrank && args.t != nullptr) {
     // acc = T * lora_up^T over the rank dimension, 16 at a time (zero-padded).
     const int R = args.r;
     const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -322,12 +332,13 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
     bnx[p] = dequant_pair<B>(be, nib, ks, p, sc, ns64);
   };
 
-  // Group g uses LDS stage (g + G) % 2, so that after an optional lone first
-  // group (odd G) the loop runs in (stage 0, stage 1) pairs.
-  const int st0 = G & 1;
+  // Group g0 + j uses LDS stage (j + count) % 2, so that after an optional
+  // lone first group (odd count) the loop runs in (stage 0, stage 1) pairs.
+  const int count = g1 - g0;
+  const int st0 = count & 1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue_x_one(0, st0, i);
-  load_w(0, wn, sn);
+  for (int i = 0; i < 8; ++i) issue_x_one(g0, st0, i);
+  load_w(g0, wn, sn);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   take_next_weights();
@@ -350,7 +361,7 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
   // (clamped), fetched into the idle stage and never used.
   auto group = [&](int g, auto stage_tag) {
     constexpr int ST = decltype(stage_tag)::value;
-    const int gn = min(g + 1, G - 1);
+    const int gn = min(g + 1, g1 - 1);
     auto step = [&]<int T>(std::integral_constant<int, T>) {
       constexpr int ks = T >> 3, rb = T & 7;
       if constexpr (T < 8) issue_x_one(gn, ST ^ 1, T);
@@ -383,21 +394,25 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int g = 0;
+  int g = g0;
   if (st0 == 1) group(g++, I1{});
-  for (; g < G; g += 2) {
+  for (; g < g1; g += 2) {
     group(g, I0{});
     group(g + 1, I1{});
   }
+}
 
-  // Epilogue: every wave is done with LDS (the last group's reads run past
-  // its barrier); each 32 x 32 block leaves through a 5 KB scratch per wave
-  // as 16-byte pieces of rows.
-  __syncthreads();
+// Epilogue of tile (tm, tn): each 32 x 32 block leaves through a 5 KB
+// scratch per wave in LDS as 16-byte pieces of rows.  Every wave must be done
+// with LDS before it is called (a barrier after large_accumulate).
+__device__ __forceinline__ void large_store(const GemmArgs& args, int tm, int tn,
+                                            const f32x16 (&acc)[kBM / 32], uint8_t* lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* scratch = reinterpret_cast<float*>(lds + wave * kEpiScratch);
   const bool vec = epi_vec_ok(args.y, args.n, args.out_bf16 != 0);
+  const int m0 = tm * kBM, nw0 = tn * kBN;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < kBM / 32; ++rb) {
     if (args.out_bf16)
       store_block32<true>(acc[rb], scratch, args.y, args.m, args.n, m0 + rb * 32, nw0 + wave * 32, vec);
     else
@@ -405,10 +420,266 @@ __device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8
   }
 }
 
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kBM / 32]) {
+#pragma unroll
+  for (int rb = 0; rb < kBM / 32; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+}
+
+// One whole 256 x 256 output tile (tile index `tile`).  Kernels:
+// gemm_large_kernel (one product) and gemm_grouped_large_kernel (several
+// products in one launch).
+template <int B>
+__device__ __forceinline__ void large_tile(const GemmArgs& args, int tile, uint8_t* lds) {
+  int tm, tn;
+  tile_coords(tile, args.tiles_m, args.tiles_n, tm, tn);
+  f32x16 acc[kBM / 32];
+  zero_acc(acc);
+  large_accumulate<B>(args, tm, tn, 0, args.k / kGroup, true, acc, lds);
+  __syncthreads();
+  large_store(args, tm, tn, acc, lds);
+}
+
 template <int B>
 __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
   large_tile<B>(args, blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------------------
+// K2sk: the large-M product with K split across workgroups, for outputs whose
+// 256 x 256 tiles would fill the compute units unevenly.  At most one
+// workgroup per compute unit, all resident at once.  Two assignments:
+//   * split-K (split > 1, few tiles): workgroup u takes K chunk u / tiles
+//     (of `split` equal chunks) of tile u % tiles, so the workgroups of one
+//     moment read the same K range of the operands (they share L2 the way
+//     whole tiles do);
+//   * stream-K (split == 0): workgroup w runs on XCD w % 8 (the dispatcher's
+//     round robin); the tiles are split into 8 contiguous sets, one per XCD,
+//     and each XCD's (tile, 128-group) iterations into equal contiguous
+//     ranges, one per workgroup of that XCD in order of w / 8.  A range holds
+//     at most one tile's tail (it starts inside a tile), whole tiles, and at
+//     most one tile's head (it ends inside a tile).
+// Split-K: every chunk writes its partial tile to its workgroup's slot of the
+// workspace and sets its flag to this launch's epoch; then the chunks of a
+// tile wait for one another's flags and each adds up, in chunk order, and
+// stores a share of the tile's 32 x 32 blocks (the reduction is spread over
+// the tile's workgroups).  The grid is at most one workgroup per compute unit
+// (128 KB of LDS each), so all of them are resident once dispatched, and each
+// publishes before it waits.
+// Stream-K: a piece that ends before the tile's last group publishes its
+// partial sums the same way; the piece holding the tile's last group waits
+// for the flags of the workgroups holding the tile's other groups, adds their
+// partial sums in workgroup order and stores the tile.  Those workgroups have
+// smaller ids (the dispatcher starts them first) and publish before they wait
+// for anything.
+// Either way the sums are added in a fixed order, so results do not depend on
+// timing.  Each wait is also bounded (a flag that never comes, which a correct
+// caller never causes, ends it after about a second with a wrong tile instead
+// of a hang).  Flags hold a per-launch epoch (never zero, drawn by the host
+// from a random start), so the workspace needs no clearing.
+// ---------------------------------------------------------------------------
+struct StreamK {
+  float* partials;                 // grid x 65536 floats, accumulator layout
+  unsigned long long* flags;       // grid flags
+  unsigned long long epoch;
+  int wpx;                         // stream-K: workgroups per XCD (grid = 8 wpx)
+  int split;                       // split-K: K chunks per tile (grid = split x tiles); 0: stream-K
+};
+constexpr int kSkXcds = 8;
+constexpr int kSkSlotFloats = kBM * kBN;
+constexpr unsigned kSkSpinLimit = 1u << 20;
+// The exchange bypasses the cache maintenance of fences (an agent-scope
+// acquire invalidates the whole XCD L2, which the other workgroups of that XCD
+// are streaming X and weights through): the partial sums are written and read
+// with device-scope coherent buffer accesses (cache policy SC1) and the flags
+// are relaxed agent-scope atomics.  A writer's partial stores have completed
+// (s_waitcnt, then the workgroup barrier) before its flag is stored; a reader
+// issues its partial loads only after it has seen the flag.
+constexpr int kSkCoherent = 16;   // SC1
+constexpr int kSkMaxSplit = 8;    // K chunks per tile in split-K
+
+template <int B>
+__global__ __launch_bounds__(512, 1) void gemm_streamk_kernel(GemmArgs args, StreamK sk) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
+  const int w = blockIdx.x;
+  const int G = args.k / kGroup;
+  const int tiles = args.tiles_m * args.tiles_n;
+  const bool split_k = sk.split > 0;
+  // stream-K: this XCD's tiles and this workgroup's iteration range
+  const int xcd = w % kSkXcds, l = w / kSkXcds;
+  const int t_lo = split_k ? 0 : (int)((int64_t)xcd * tiles / kSkXcds);
+  const int t_hi = split_k ? 0 : (int)((int64_t)(xcd + 1) * tiles / kSkXcds);
+  const int64_t I = (int64_t)(t_hi - t_lo) * G;
+  auto start = [&](int ll) { return (int64_t)(I * ll / sk.wpx); };
+  int nseg, tf = 0, tl = 0, a_f = 0, b_l = G;
+  bool head_last = false;
+  if (split_k) {
+    nseg = 1;
+  } else {
+    const int64_t i0 = start(l), i1 = start(l + 1);
+    if (i0 >= i1) return;
+    tf = (int)(i0 / G); tl = (int)((i1 - 1) / G);                  // first, last tile (XCD-relative)
+    a_f = (int)(i0 % G); b_l = (int)((i1 - 1) % G) + 1;
+    head_last = b_l < G && tl != tf;                                // ends inside another tile
+    nseg = tl - tf + 1;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // a slot holds the 256 x 256 partial tile in the accumulator layout: wave
+  // w's 32 KB, then (row block, quarter) pieces of 1 KB, 16 bytes per lane
+  const uint32_t slot_voff = (uint32_t)wave * 32768u + (uint32_t)lane * 16u;
+  auto slot_rsrc = [&](int wi) {
+    return make_rsrc(sk.partials + (int64_t)wi * kSkSlotFloats, (uint32_t)(kSkSlotFloats * 4));
+  };
+
+  for (int s = 0; s < nseg; ++s) {
+    int tm, tn, a, b, n_contrib, c_first;
+    if (split_k) {
+      const int c = w / tiles, t = w % tiles;
+      tile_coords(t, args.tiles_m, args.tiles_n, tm, tn);
+      a = (int)((int64_t)c * G / sk.split);
+      b = (int)((int64_t)(c + 1) * G / sk.split);
+      n_contrib = c;                    // chunks 0 .. c-1 of this tile: workgroups c' tiles + t
+      c_first = t;
+    } else {
+      // order: the head of the last tile, the whole tiles, the first tile
+      int t;
+      if (head_last) t = s == 0 ? tl : (s == nseg - 1 ? tf : tf + s);
+      else t = s == nseg - 1 ? tf : tf + 1 + s;
+      t = __builtin_amdgcn_readfirstlane(t);
+      a = t == tf ? a_f : 0;
+      b = t == tl ? b_l : G;
+      tile_coords_range(t_lo + t, args.tiles_m, args.tiles_n, tm, tn);
+      // earlier workgroups of this XCD holding groups of this tile: c_first .. l-1
+      const int64_t it0 = (int64_t)t * G;
+      int c0 = l - 1;
+      while (c0 > 0 && start(c0) > it0) --c0;
+      c_first = c0;
+      n_contrib = l - c0;
+    }
+    f32x16 acc[kBM / 32];
+    zero_acc(acc);
+    large_accumulate<B>(args, tm, tn, a, b, a == 0, acc, lds);
+    __syncthreads();
+    if (split_k) {
+      // every chunk publishes its partial tile, then reduces and stores the
+      // 32 x 32 blocks (wave, row block) numbered chunk, chunk + split, ...
+      // of the tile from all `split` slots in chunk order
+      const rsrc_t ro = slot_rsrc(w);
+#pragma unroll
+      for (int rb = 0; rb < kBM / 32; ++rb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef float f4 __attribute__((ext_vector_type(4)));
+          typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+          const f4 v = {acc[rb][4 * q], acc[rb][4 * q + 1], acc[rb][4 * q + 2], acc[rb][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ro, slot_voff,
+                                                 (uint32_t)((rb * 4 + q) * 1024), kSkCoherent);
+        }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(&sk.flags[w], sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int chunk = w / tiles;
+      for (int c = 0; c < sk.split; ++c) {
+        if (c == chunk) continue;
+        unsigned spins = 0;
+        while (__hip_atomic_load(&sk.flags[c * tiles + c_first], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                   sk.epoch && ++spins < kSkSpinLimit)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      float* scratch = reinterpret_cast<float*>(lds + wave * kEpiScratch);
+      const bool vec = epi_vec_ok(args.y, args.n, args.out_bf16 != 0);
+      const uint32_t lane_off = (uint32_t)lane * 16u;
+      for (int piece = chunk + sk.split * wave; piece < 8 * (kBM / 32); piece += sk.split * 8) {
+        const int pw = piece / (kBM / 32), prb = piece % (kBM / 32);   // block of wave pw, row block prb
+        // every chunk's block in flight at once (chunks past `split` read
+        // nothing: their offset lies past the resource and returns zeros),
+        // then added in chunk order
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        u4 r[kSkMaxSplit][4];
+#pragma unroll
+        for (int c = 0; c < kSkMaxSplit; ++c) {
+          const bool live = c < sk.split;
+          const rsrc_t ri = slot_rsrc((live ? c : 0) * tiles + c_first);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            r[c][q] = __builtin_amdgcn_raw_buffer_load_b128(ri, live ? lane_off : 0x80000000u,
+                                                             (uint32_t)(pw * 32768 + (prb * 4 + q) * 1024),
+                                                             kSkCoherent);
+        }
+        f32x16 v16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v16[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < kSkMaxSplit; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 f = __builtin_bit_cast(f32x4, r[c][q]);
+            v16[4 * q] += f[0]; v16[4 * q + 1] += f[1]; v16[4 * q + 2] += f[2]; v16[4 * q + 3] += f[3];
+          }
+        if (args.out_bf16)
+          store_block32<true>(v16, scratch, args.y, args.m, args.n, tm * kBM + prb * 32, tn * kBN + pw * 32, vec);
+        else
+          store_block32<false>(v16, scratch, args.y, args.m, args.n, tm * kBM + prb * 32, tn * kBN + pw * 32, vec);
+      }
+      continue;
+    }
+    if (b < G) {
+      // partial: publish this workgroup's sums of the tile
+      const rsrc_t ro = slot_rsrc(w);
+#pragma unroll
+      for (int rb = 0; rb < kBM / 32; ++rb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef float f4 __attribute__((ext_vector_type(4)));
+          typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+          const f4 v = {acc[rb][4 * q], acc[rb][4 * q + 1], acc[rb][4 * q + 2], acc[rb][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ro, slot_voff,
+                                                 (uint32_t)((rb * 4 + q) * 1024), kSkCoherent);
+        }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(&sk.flags[w], sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    if (a > 0) {
+      // the tile's last piece: add the partial sums of its other pieces
+      for (int j = 0; j < n_contrib; ++j) {
+        int wc;
+        if (split_k) {
+          wc = j * tiles + c_first;
+        } else {
+          const int c = c_first + j;
+          if (start(c) >= start(c + 1)) continue;                  // an empty range publishes nothing
+          wc = c * kSkXcds + xcd;
+        }
+        unsigned spins = 0;
+        while (__hip_atomic_load(&sk.flags[wc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != sk.epoch &&
+               ++spins < kSkSpinLimit)
+          __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_waitcnt(0);
+        const rsrc_t ri = slot_rsrc(wc);
+#pragma unroll
+        for (int rb = 0; rb < kBM / 32; ++rb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+            const u4 r = __builtin_amdgcn_raw_buffer_load_b128(ri, slot_voff, (uint32_t)((rb * 4 + q) * 1024),
+                                                                kSkCoherent);
+            const f32x4 v = __builtin_bit_cast(f32x4, r);
+            acc[rb][4 * q] += v[0]; acc[rb][4 * q + 1] += v[1];
+            acc[rb][4 * q + 2] += v[2]; acc[rb][4 * q + 3] += v[3];
+          }
+      }
+    }
+    large_store(args, tm, tn, acc, lds);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -958,7 +1229,30 @@ __global__ __launch_bounds__(256) void lowrank_t_kernel(const __bf16* __restrict
   f32x4 acc[RBLK];
 #pragma unroll
   for (int j = 0; j < RBLK; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = wave * 32; k0 < k; k0 += 128) {
+  // U steps of this wave's K range per trip, their loads issued before the
+  // first MFMA (the loop is bound by load latency otherwise)
+  constexpr int U = RBLK <= 2 ? 8 : (RBLK <= 4 ? 4 : 2);
+  const int steps = (k - wave * 32 + 127) / 128;
+  int st = 0;
+  for (; st + U <= steps; st += U) {
+    bf16x8 bv[U], av[U][RBLK];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = wave * 32 + 128 * (st + u);
+      bv[u] = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+      for (int j = 0; j < RBLK; ++j) {
+        const int rr = j * 16 + lr;
+        av[u][j] = load_bf16x8_or_zero(lora_down + (int64_t)min(rr, r - 1) * k + k0 + 8 * lq, rr < r);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < RBLK; ++j) acc[j] = mfma16x16x32(av[u][j], bv[u], acc[j]);
+  }
+  for (; st < steps; ++st) {
+    const int k0 = wave * 32 + 128 * st;
     const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow + k0);
 #pragma unroll
     for (int j = 0; j < RBLK; ++j) {

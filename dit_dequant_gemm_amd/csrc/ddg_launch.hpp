@@ -22,6 +22,11 @@ hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t stream);
 // workgroup: (2,2) (1,4) (1,8) (2,4) (4,2) for rb = 1, (1,4) (2,2) otherwise
 template <int B>
 hipError_t launch_gemm_small(const GemmArgs& a, int rb, int nc, int nk, hipStream_t stream);
+// split-K or stream-K over a.tiles_m x a.tiles_n tiles of 256 x 256 with
+// `grid` workgroups (sk.split x tiles, or 8 sk.wpx); sk.partials / sk.flags:
+// workspace of `grid` slots
+template <int B>
+hipError_t launch_gemm_streamk(const GemmArgs& a, const StreamK& sk, int grid, hipStream_t stream);
 
 template <int B>
 hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t stream);

@@ -40,6 +40,12 @@ hipError_t launch_gemm_large<DDG_BITS>(const GemmArgs& a, hipStream_t stream) {
 }
 
 template <>
+hipError_t launch_gemm_streamk<DDG_BITS>(const GemmArgs& a, const StreamK& sk, int grid, hipStream_t stream) {
+  gemm_streamk_kernel<DDG_BITS><<<dim3((unsigned)grid), dim3(512), 0, stream>>>(a, sk);
+  return hipGetLastError();
+}
+
+template <>
 hipError_t launch_gemm_small<DDG_BITS>(const GemmArgs& a, int rb, int nc, int nk,
                                        hipStream_t stream) {
   const dim3 grid((unsigned)((a.n + 16 * nc - 1) / (16 * nc)));

@@ -200,7 +200,7 @@ void round_to_budget(const double* b, const int64_t* nparams, int n, const int* 
 extern "C" int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_sse,
                              double* total_sse, hipStream_t stream) {
   if (w_dtype != DDG_BF16 && w_dtype != DDG_F32) return DDG_ERR_ARG;
-  if (n < 0 || n > 2147483647 || k <= 0 || k % DDG_GROUP || k > (INT64_C(1) << 31))
+  if (n < 0 || n > DDG_SSE_ROWS_MAX || k <= 0 || k % DDG_GROUP || k > (INT64_C(1) << 31))
     return DDG_ERR_SHAPE;
   if (!total_sse) return DDG_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(total_sse) & 7) return DDG_ERR_ALIGN;

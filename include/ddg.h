@@ -121,13 +121,22 @@ int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t
  * Y = X * w_hat^T ([WDQ] §3.4 + §5.4, dequantizing inside the GEMM).
  *   x       M x K bf16.       packed/scales: the record of an N x K weight.
  *   y       M x N, y_dtype (DDG_BF16 or DDG_F32), fully overwritten.
+ *   workspace, workspace_bytes
+ *           optional device scratch (NULL, 0: none; 16-byte aligned).  With
+ *           at least ddg_workspace_bytes(M, N, K, 0) bytes, products whose
+ *           256 x 256 output tiles would fill the compute units unevenly run
+ *           as stream-K: K ranges of tiles split across workgroups, partial
+ *           sums exchanged through the workspace.  Its contents need no
+ *           initialisation and are scratch afterwards; calls that share a
+ *           workspace must be ordered (one stream).  Results then differ
+ *           from the call without workspace only in float32 summation order.
  * Requirements: M >= 0 (M == 0 is a no-op), N a positive multiple of 16,
  * K a positive multiple of 128 and at most 2^20, M, N <= 2^31 - 1.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP.
  */
 int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                      const float* scales, int bits, int64_t n, void* y, int y_dtype,
-                     hipStream_t stream);
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One product of a grouped call: y = x * w_hat^T, arguments as in
  * ddg_dequant_gemm. */
@@ -164,11 +173,14 @@ typedef struct ddg_gemm_desc {
 int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream);
 
 /*
- * Workspace bytes ddg_lowrank_fused_gemm needs for an M x K input, an N x K
- * weight and rank r: the M x r bf16 intermediate T, rounded up to 256 bytes.
+ * Workspace bytes for an M x K input and an N x K weight: with r = 0, what
+ * ddg_dequant_gemm can use (the stream-K partial sums: 64 MiB and a flag per
+ * workgroup where the output has fewer than 1024 tiles of 256 x 256, else 0);
+ * with rank r, what ddg_lowrank_fused_gemm needs: the M x r bf16
+ * intermediate T, rounded up to 256 bytes, followed by that stream-K area.
  * Host-only.
  * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m, n or k negative or m, n above
- * 2^31 - 1, r outside 8..128 or not a multiple of 8).
+ * 2^31 - 1, r not 0 and outside 8..128 or not a multiple of 8).
  */
 int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
 
@@ -182,8 +194,10 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
  * T is computed in float32 and rounded to bf16 once (the branch is a bf16
  * product); the branch term T * L2 is summed into the same float32
  * accumulator as the main product before y is written.
- *   workspace  device scratch of at least ddg_workspace_bytes(M, N, K, r)
- *              bytes; its contents are scratch (no initial state needed).
+ *   workspace  device scratch: T first (M * r * 2 bytes rounded up to 256,
+ *              required), then optionally the stream-K area of
+ *              ddg_dequant_gemm; ddg_workspace_bytes(M, N, K, r) bytes hold
+ *              both.  Its contents are scratch (no initial state needed).
  * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_WORKSPACE,
  * DDG_ERR_HIP.
@@ -224,10 +238,13 @@ int ddg_lowrank_fused_gemm_noalloc(const void* x, int64_t m, int64_t k, const ui
  *   w          N x K bf16 or float32 (w_dtype), finite.
  *   row_sse    device, N x 5 doubles (also the scratch of the total).
  *   total_sse  device, 5 doubles.
- * n == 0 writes zero totals.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (n < 0, k
- * not a positive multiple of 128 or above 2^31), DDG_ERR_ALIGN (w 16-byte,
- * the outputs 8-byte), DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ * n == 0 writes zero totals.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (n < 0 or
+ * above DDG_SSE_ROWS_MAX (one workgroup of up to 256 lanes per row: the launch
+ * stays below 2^32 work-items), k not a positive multiple of 128 or above
+ * 2^31), DDG_ERR_ALIGN (w 16-byte, the outputs 8-byte), DDG_ERR_HIP,
+ * DDG_ERR_UNSUPPORTED.
  */
+#define DDG_SSE_ROWS_MAX ((INT64_C(1) << 24) - 1)
 int ddg_quant_sse(const void* w, int w_dtype, int64_t n, int64_t k, double* row_sse,
                   double* total_sse, hipStream_t stream);
 
@@ -353,9 +370,11 @@ int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
  * bias 7, subnormals, largest 448); an all-zero row gets s_x = 0 and zeros.
  *   x   device, 16-byte aligned.  xq  device m x k bytes, 8-byte aligned.
  *   xscales  device, m floats.
- * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (k not a positive multiple of 128),
- * DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (m above DDG_FP8_ROWS_MAX: one workgroup
+ * of 256 lanes per row keeps the launch below 2^32 work-items; k not a
+ * positive multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
  */
+#define DDG_FP8_ROWS_MAX ((INT64_C(1) << 24) - 1)
 int ddg_fp8_quantize_rows(const void* x, int64_t m, int64_t k, uint8_t* xq, float* xscales,
                           hipStream_t stream);
 
@@ -396,9 +415,12 @@ int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
  * (b, g) order.  Size: ceil(m/32) * (k/128) * 3072 bytes.
  *   x   device, 16-byte aligned.  xq  device, 16-byte aligned.
  *   xscales  device, m floats.
- * m == 0 is a no-op.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (k not a positive
- * multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ * m == 0 is a no-op.  Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (m above
+ * DDG_FP6_ROWS_MAX: 1024 lanes per 16 rows keep the launch below 2^32
+ * work-items; k not a positive multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP,
+ * DDG_ERR_UNSUPPORTED.
  */
+#define DDG_FP6_ROWS_MAX ((INT64_C(1) << 26) - 32)
 int ddg_fp6_quantize_rows(const void* x, int64_t m, int64_t k, int fmt6, uint8_t* xq, float* xscales,
                           hipStream_t stream);
 

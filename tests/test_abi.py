@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from dit_dequant_gemm_amd import api
 
@@ -73,12 +74,18 @@ def test_packed_bytes_bad_bits(lib):
 
 def test_workspace_bytes(lib):
     b = ctypes.c_size_t()
-    assert lib.ddg_workspace_bytes(4096, 3072, 3072, 32, ctypes.byref(b)) == OK and b.value == 4096 * 64
+    sk = 256 * 256 * 256 * 4 + 256 * 8          # stream-K slots and flags (fewer than 1024 tiles)
+    assert lib.ddg_workspace_bytes(4096, 3072, 3072, 32, ctypes.byref(b)) == OK and b.value == 4096 * 64 + sk
     assert lib.ddg_workspace_bytes(3, 16, 128, 8, ctypes.byref(b)) == OK and b.value == 256
     assert lib.ddg_workspace_bytes(0, 16, 128, 32, ctypes.byref(b)) == OK and b.value == 0
+    # r = 0: the stream-K area of the plain product, where its tiles are few
+    assert lib.ddg_workspace_bytes(4096, 3072, 3072, 0, ctypes.byref(b)) == OK and b.value == sk
+    assert lib.ddg_workspace_bytes(64, 3072, 3072, 0, ctypes.byref(b)) == OK and b.value == 0
+    assert lib.ddg_workspace_bytes(32760, 5120, 5120, 0, ctypes.byref(b)) == OK and b.value == 0
+    assert lib.ddg_workspace_bytes(1024, 5120, 5120, 32, ctypes.byref(b)) == OK and b.value == 1024 * 64 + sk
     assert lib.ddg_workspace_bytes(64, -1, 128, 32, ctypes.byref(b)) == E_SHAPE
     assert lib.ddg_workspace_bytes(64, 16, -128, 32, ctypes.byref(b)) == E_SHAPE
-    for r in (0, 4, 12, 136, -8):
+    for r in (4, 12, 136, -8):
         assert lib.ddg_workspace_bytes(64, 16, 128, r, ctypes.byref(b)) == E_SHAPE
     assert lib.ddg_workspace_bytes(64, 16, 128, 32, None) == E_ARG
 
@@ -108,7 +115,11 @@ def test_dequantize_rejects_bad_arguments(lib):
 
 
 def test_dequant_gemm_rejects_bad_arguments(lib):
-    g = lib.ddg_dequant_gemm
+    gl = lib.ddg_dequant_gemm
+
+    def g(*a, ws=None, wsb=0):
+        return gl(*a[:-1], ws, wsb, a[-1])
+
     assert g(FAKE, 4, 128, FAKE, FAKE, 8, 32, FAKE, 0, None) == E_ARG      # bits
     assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE, 5, None) == E_ARG      # y dtype
     assert g(FAKE, 4, 130, FAKE, FAKE, 4, 32, FAKE, 0, None) == E_SHAPE    # k
@@ -126,6 +137,7 @@ def test_dequant_gemm_rejects_bad_arguments(lib):
     assert g(FAKE, 4, 128, FAKE, FAKE + 1, 4, 32, FAKE, 0, None) == E_ALIGN
     assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE + 8, 1, None) == E_ALIGN
     assert g(None, 0, 128, None, None, 4, 32, None, 0, None) == OK          # M == 0
+    assert g(FAKE, 4, 128, FAKE, FAKE, 4, 32, FAKE, 0, None, ws=FAKE + 8, wsb=1 << 20) == E_ALIGN
 
 
 def test_grouped_gemm_rejects_bad_arguments(lib):
@@ -289,3 +301,47 @@ def test_noalloc_lowrank_host_checks(lib):
     assert call(k=100) == E_SHAPE and call(n=20) == E_SHAPE and call(bits=8) == E_ARG
     assert call(ld=0) == E_ARG and call(ld=FAKE + 8) == E_ALIGN
     assert call(m=0) == OK
+
+
+def test_row_quantizers_and_error_tables_bound_their_rows(lib):
+    """One workgroup per row (or per 16 rows): row counts whose launch would
+    pass 2^32 work-items are refused on the host before anything is launched."""
+    FAKE = 1 << 20
+    assert lib.ddg_fp8_quantize_rows(FAKE, (1 << 24) - 1, 128, FAKE, FAKE, None) != E_SHAPE
+    assert lib.ddg_fp8_quantize_rows(FAKE, 1 << 24, 128, FAKE, FAKE, None) == E_SHAPE
+    assert lib.ddg_fp6_quantize_rows(FAKE, (1 << 26) - 32, 128, 0, FAKE, FAKE, None) != E_SHAPE
+    assert lib.ddg_fp6_quantize_rows(FAKE, (1 << 26) - 31, 128, 0, FAKE, FAKE, None) == E_SHAPE
+    assert lib.ddg_quant_sse(FAKE, 0, (1 << 24) - 1, 128, FAKE, FAKE, None) != E_SHAPE
+    assert lib.ddg_quant_sse(FAKE, 0, 1 << 24, 128, FAKE, FAKE, None) == E_SHAPE
+
+
+def test_record_round_trip_and_rejections():
+    """The stored record's four fields ([WDQ] §3.3): state_dict -> from_state_dict
+    keeps them, and records whose fields disagree are refused on the host."""
+    n, k, bits = 48, 384, 5
+    pb = n * k * bits // 8
+    qw = api.QWeight(torch.arange(pb, dtype=torch.int64).to(torch.uint8), torch.ones((n, k // 128)),
+                     bits, n, k, 300)
+    sd = qw.state_dict("blocks.0.attn.q")
+    assert set(sd) == {f"blocks.0.attn.q_{f}" for f in ("packed", "scales", "bw", "nin")}
+    assert sd["blocks.0.attn.q_bw"].dtype == torch.int8 and sd["blocks.0.attn.q_nin"].dtype == torch.int32
+    back = api.QWeight.from_state_dict(sd, "blocks.0.attn.q", orig_in=300, device="cpu")
+    assert (back.n, back.k, back.bits, back.orig_in) == (n, k, bits, 300)
+    assert torch.equal(back.packed, qw.packed) and torch.equal(back.scales, qw.scales)
+
+    def bad(**change):
+        d = dict(sd)
+        for key, v in change.items():
+            d[f"blocks.0.attn.q_{key}"] = v
+        with pytest.raises(ValueError):
+            api.QWeight.from_state_dict(d, "blocks.0.attn.q", device="cpu")
+    bad(bw=torch.tensor(8, dtype=torch.int8))
+    bad(bw=torch.tensor(2, dtype=torch.int8))
+    bad(bw=torch.tensor(4, dtype=torch.int8))                 # bytes of a 5-bit record
+    bad(nin=torch.tensor(400, dtype=torch.int32))
+    bad(nin=torch.tensor(1280, dtype=torch.int32))            # scales no longer whole rows
+    bad(packed=sd["blocks.0.attn.q_packed"][:-1])             # truncated
+    bad(scales=sd["blocks.0.attn.q_scales"].reshape(-1)[:-3])
+    bad(scales=sd["blocks.0.attn.q_scales"].double())
+    with pytest.raises(ValueError):
+        api.QWeight.from_state_dict(sd, "blocks.0.attn.q", orig_in=200, device="cpu")

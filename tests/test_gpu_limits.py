@@ -16,7 +16,7 @@ import torch
 
 import oracle as O
 from dit_dequant_gemm_amd import synth
-from parity_util import check_product, dev_bf16, f32_bits, host
+from parity_util import check_product, dev_bf16, dev_f32, f32_bits, host
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +40,10 @@ def _w16(w, bits):
 
 @pytest.mark.parametrize("bits", (3, 7))
 def test_quantize_and_gemm_at_k_max(gpu_lib, bits):
-    """K = 2^20 (8192 groups per row) through every product kernel: M = 4
-    (weight streaming), 20 (small-M, two row blocks), 80 (large tiles)."""
+    """K = 2^20 (8192 groups per row) with N = 32: M = 4 (the small-M kernel
+    with one row block), 20 (two row blocks), 80 (large tiles).  The
+    weight-streaming kernel (M <= 16 with N >= 12800), the grouped kernels,
+    the low-rank pre-pass and the W4A8 product at this K follow."""
     c = synth.random_case(31 + bits, 80, 32, K_MAX)
     _case(f"quantize_pack 32 x 2^20 bits={bits}")
     qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
@@ -328,3 +330,88 @@ def test_rotate_past_4gib(gpu_lib):
     bound = np.broadcast_to((math.log2(h) + 1) * 2.0 ** -24 * blk / math.sqrt(h),
                             (len(rows), d // h, h)).reshape(len(rows), d) * 1.01 + 1e-37
     assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / bound))
+
+
+def _wide_k_max_weight(n, bits, cols):
+    """An n x 2^20 weight on the GPU: a seeded 32-row block repeated, with
+    seeded rows of their own at `cols`.  Returns (device bf16, own rows)."""
+    base = synth.random_case(61 + bits, 0, 32, K_MAX)["w"]
+    own = synth.random_case(62 + bits, 0, len(cols), K_MAX)["w"]
+    wd = dev_bf16(base).repeat(n // 32, 1)
+    wd[torch.as_tensor(cols, device="cuda")] = dev_bf16(own)
+    return wd, own
+
+
+@pytest.mark.parametrize("bits", (3, 6))
+def test_weight_streaming_and_grouped_at_k_max(gpu_lib, bits):
+    """K = 2^20 through the weight-streaming kernel (M = 16 and 5 with
+    N = 12800: 200 workgroups of 64 columns) and through one grouped call that
+    holds that product beside a 20-token and an 80-token one on a 32-column
+    weight (the grouped kernels of each class)."""
+    api = gpu_lib
+    n = 12800
+    cols = np.array([0, 1, 63, 64, 6399, 6400, 12735, 12736, 12798, 12799])
+    _case(f"quantize_pack {n} x 2^20 bits={bits} (repeated block, own rows at the checked columns)")
+    wd, own = _wide_k_max_weight(n, bits, cols)
+    qw = api.quantize_pack(wd, bits)
+    del wd
+    torch.cuda.empty_cache()
+    p_ref, s_ref, q_ref = O.quantize_pack(own, bits)
+    colt = torch.as_tensor(cols, device="cuda")
+    got = qw.packed.view(n, -1).index_select(0, colt).cpu().numpy()
+    assert np.array_equal(got.reshape(-1), p_ref), "packed bytes differ"
+    w16 = O.dequant_bf16(q_ref, s_ref, bits)
+    xs = synth.random_case(63 + bits, 80, 32, K_MAX)
+    xd = dev_bf16(xs["x"])
+    for m in (16, 5):
+        _case(f"dequant_gemm weight streaming M={m} N={n} K=2^20 bits={bits}")
+        y = api.dequant_gemm(xd[:m], qw, torch.float32)
+        check_product(y.index_select(1, colt).cpu().numpy(), O.gemm_ref(xs["x"][:m], w16), False, f"M={m}")
+        del y
+    _case(f"dequant_gemm_grouped at K=2^20 bits={bits}: M=16 x N={n}, M=20 and M=80 x N=32")
+    qs = api.quantize_pack(dev_bf16(xs["w"]), bits)
+    ws16 = _w16(xs["w"], bits)
+    outs = api.dequant_gemm_grouped([(xd[:16], qw), (xd[:20], qs), (xd[:80], qs)], out_dtype=torch.float32)
+    check_product(outs[0].index_select(1, colt).cpu().numpy(), O.gemm_ref(xs["x"][:16], w16), False, "grouped M=16")
+    check_product(outs[1].cpu().numpy(), O.gemm_ref(xs["x"][:20], ws16), False, "grouped M=20")
+    check_product(outs[2].cpu().numpy(), O.gemm_ref(xs["x"][:80], ws16), False, "grouped M=80")
+    del outs, qw
+    torch.cuda.empty_cache()
+
+
+def test_lowrank_at_k_max(gpu_lib):
+    """The low-rank pre-pass and the fused product at K = 2^20, r = 32, for
+    M = 16 (small-M kernel) and 80 (large tiles)."""
+    api = gpu_lib
+    c = synth.random_case(71, 80, 64, K_MAX, wstd=0.05)
+    _case("lowrank_fused_gemm K=2^20 r=32 (SVD split of a 64 x 2^20 weight)")
+    l1, l2, res = O.svd_split(c["w"], 32)
+    qr = api.quantize_pack(dev_f32(res), 4)
+    ld = dev_bf16(np.ascontiguousarray(l1.T))
+    lu = dev_bf16(np.ascontiguousarray(l2.T))
+    w16 = _w16(res, 4)
+    xd = dev_bf16(c["x"])
+    for m in (16, 80):
+        _case(f"lowrank_fused_gemm M={m} N=64 K=2^20 r=32")
+        y_ref, _ = O.lowrank_fused_ref(c["x"][:m], w16, l1, l2)
+        check_product(host(api.lowrank_fused_gemm(xd[:m], qr, ld, lu, torch.float32)), y_ref, False, f"M={m}")
+
+
+def test_w4a8_tiled_at_k_max(gpu_lib):
+    """The E4M3 row quantizer, the tiled E2M1 quantizer and their product at
+    K = 2^20 (M = 20, N = 48)."""
+    from oracle import fp4 as F
+    api = gpu_lib
+    rng = np.random.default_rng(81)
+    w = synth.to_bf16(rng.standard_t(4, size=(48, K_MAX)) * 0.02)
+    x = synth.to_bf16(rng.normal(0, 1, size=(20, K_MAX)))
+    _case("fp8_quantize_rows + fp4_quantize_pack (tiled) + w4a8_gemm at K=2^20")
+    xq, xs = api.fp8_quantize_rows(dev_bf16(x))
+    cq, cs = F.quantize_rows_e4m3(x)
+    assert np.array_equal(host(xq), cq) and np.array_equal(f32_bits(host(xs)), f32_bits(cs))
+    qw = api.fp4_quantize_pack(dev_bf16(w), "e2m1", tiled=True)
+    wc, wsc = F.quantize_fp4_groups(w, "e2m1")
+    tp, ts = F.tile_fp4(F.pack_fp4(wc), wsc)
+    assert np.array_equal(host(qw.packed), tp)
+    y = host(api.w4a8_gemm(xq, xs, qw, torch.float32))
+    check_product(y, F.w4a8_ref(cq, cs, wc, wsc, "e2m1"), False, "w4a8 K=2^20")

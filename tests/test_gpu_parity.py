@@ -335,7 +335,6 @@ def test_gemm_config3(gpu_lib, which):
 @pytest.mark.parametrize("name", ["qkv", "o", "up", "down"])
 def test_gemm_config5(gpu_lib, name):
     w = synth.config5_weights(name)
-    drawn = synth.config5_bits()[name]
     x16 = synth.config5_x(name, 16)
     xd16 = dev_bf16(x16)
     wd = dev_bf16(w)
@@ -344,13 +343,59 @@ def test_gemm_config5(gpu_lib, name):
         qw = gpu_lib.quantize_pack(wd, bits)
         w16 = _oracle_w16(w, bits)
         check_product(host(gpu_lib.dequant_gemm(xd16, qw, torch.bfloat16)), O.gemm_ref(x16, w16), True)
-        if bits == drawn:                  # the drawn width at M = 32760 (ragged last tile)
-            _case(f"dequant_gemm workload 5 {name} M=32760 bits={bits}")
-            x = synth.config5_x(name, 32760)
-            rows = sample_rows(32760, 5, count=48, tail=248)
-            y = host(gpu_lib.dequant_gemm(dev_bf16(x), qw, torch.bfloat16))
-            check_product(y[rows], O.gemm_ref(x[rows], w16), True)
-            del x, y
+
+
+@functools.lru_cache(maxsize=1)
+def _c5_large(name):
+    """Workload 5 weight and its 32760-token X (one tensor held at a time)."""
+    return synth.config5_weights(name), synth.config5_x(name, 32760)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("name", ["qkv", "o", "up", "down"])
+def test_gemm_config5_m32760(gpu_lib, name, bits):
+    """Every width at 32760 tokens (127 full 256-row tiles and a 248-row
+    tail): the first rows, random rows and the whole ragged tail."""
+    _case(f"dequant_gemm workload 5 {name} M=32760 bits={bits}")
+    w, x = _c5_large(name)
+    qw = gpu_lib.quantize_pack(dev_bf16(w), bits)
+    rows = sample_rows(32760, 5 + bits, count=48, tail=248)
+    y = gpu_lib.dequant_gemm(dev_bf16(x), qw, torch.bfloat16)
+    ys = y.index_select(0, torch.as_tensor(rows, device="cuda")).float().cpu().numpy()
+    del y
+    check_product(ys, O.gemm_ref(x[rows], _oracle_w16(w, bits)), True)
+
+
+# ------------------------------------------------------------------ stream-K (large M, few tiles)
+@pytest.mark.parametrize("m,n,k,bits", [
+    (1041, 528, 1536, 3), (2065, 272, 6144, 5), (300, 4096, 3072, 7), (1024, 5120, 5120, 4),   # split-K 2, 8, 4, 3
+    (4096, 5120, 5120, 4), (4160, 5136, 1280, 6),                                               # stream-K
+    (4096, 3072, 3072, 4), (2065, 272, 384, 5)])                                                # whole tiles
+def test_gemm_streamk(gpu_lib, m, n, k, bits):
+    """Products whose 256 x 256 tiles fill the compute units unevenly split K
+    across workgroups when given a workspace (split-K for few tiles, stream-K
+    for some more): against the oracle, equal to themselves on a second call
+    (the partial sums are added in a fixed order), and against the same
+    product without a workspace (whole tiles) within float32 summation
+    order."""
+    _case(f"dequant_gemm stream-K m={m} n={n} k={k} bits={bits}")
+    c = synth.random_case(m + n + k, m, n, k)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+    need = gpu_lib.workspace_bytes(m, n, k, 0)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    xd = dev_bf16(c["x"])
+    rows = sample_rows(m, 7, count=96) if m > 512 else np.arange(m)
+    y_ref = O.gemm_ref(c["x"][rows], _oracle_w16(c["w"], bits))
+    y1 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=ws))
+    y2 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "stream-K results differ between calls"
+    check_product(y1[rows], y_ref, False, "stream-K f32")
+    yb = host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16, workspace=ws))
+    check_product(yb[rows], y_ref, True, "stream-K bf16")
+    y_plain = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=torch.empty(16, dtype=torch.uint8, device="cuda")))
+    check_product(y_plain[rows], y_ref, False, "whole tiles")
+    assert np.max(np.abs(y1 - y_plain)) <= 1e-5 * np.max(np.abs(y_plain)) + 1e-6
 
 
 # ------------------------------------------------------------------ low-rank branch
