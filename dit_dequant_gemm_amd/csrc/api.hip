@@ -208,14 +208,16 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
     const int rb = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
     // Column waves x K-split waves per workgroup, from timings of the 16-,
     // 32- and 64-token products: four column waves where that still leaves
-    // about 200+ workgroups (wide outputs; 16 tokens), two where 128+ remain,
-    // else one column wave and an 8-way (16 tokens) or 4-way K split.
+    // about 200+ workgroups (wide outputs; 16 tokens), two where 128+ remain
+    // (with a four-way K split at 16 tokens: 16 x 5120 x 5120 10.7 us against
+    // 11.8 with two), else one column wave and an 8-way (16 tokens) or 4-way
+    // K split.
     const int64_t nb = ((int64_t)a.n + 15) / 16;
     int nc = 1, nk = rb == 1 ? 8 : 4;
     if (rb == 1 && nb / 4 >= 200) {
       nc = 4; nk = 2;
     } else if (nb / 2 >= 128) {
-      nc = 2; nk = 2;
+      nc = 2; nk = rb == 1 ? 4 : 2;
     }
     return by_bits<SmallF>(bits, a, rb, nc, nk, stream);
   }

@@ -687,12 +687,12 @@ __global__ __launch_bounds__(512, 1) void gemm_streamk_kernel(GemmArgs args, Str
 // does not apply): a bandwidth kernel.
 // Workgroup = NC x NK waves.  Wave (c, h) owns column block c (16 columns of
 // the workgroup's 16*NC) and K split h (a contiguous range of 128-groups).
-//   * X: for each group, the 16*RB x 128 bf16 slice of a K split is staged
-//     into an LDS ring with coalesced buffer_load ... lds (1 KB per
-//     instruction, shared out among the NC waves of that split) and read back
+//   * X: for each group, the 16*RB x 128 bf16 slice of a K split is loaded
+//     into registers (16 bytes per lane per 1 KB piece, the pieces shared out
+//     among the NC waves of that split), written to an LDS ring and read back
 //     as MFMA A operands by all NC waves.  Rows past M read as zeros.
 //   * packed weights: each lane's chunk (B dwords) and scale in a register
-//     ring; the X slice and the weights of step j + D are issued together at
+//     ring; the X slice and the weights of step j + D are loaded together at
 //     step j.
 //   * the NK partial tiles of a column block are summed through LDS.
 // Ring slots are static (the step loop is unrolled by the ring size).  In the
@@ -729,19 +729,17 @@ struct SmallLds {
 // gemm_small_kernel (one product) and gemm_grouped_small_kernel (several).
 template <int B, int RB, int NC, int NK>
 __device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLds<RB, NC, NK>& L) {
-  // X slices and packed weights of step j + D are issued together at step j
-  // (ring of S = D + 1 slots each).  Loads finish in issue order, so waiting
-  // for the X of step j never waits for a later step's packed weights.
+  // X slices and packed weights of step j + D are loaded into registers at
+  // step j (rings of S = D + 1 slots); at step j each wave writes its share of
+  // X(j) to the LDS slot, and one LDS barrier hands the slot to the other
+  // column waves.  Every wait is the compiler's own (register dependences), so
+  // no wait depends on the order in which the loads were issued.
   constexpr int XSLOT = SmallLds<RB, NC, NK>::XSLOT;
   constexpr int S = SmallLds<RB, NC, NK>::S;
   constexpr int D = S - 1;                    // steps in flight
-  constexpr int DMA_SLOT = XSLOT / 1024;      // 1 KB DMA instructions per slice
-  static_assert(DMA_SLOT % NC == 0, "slice DMA must split evenly over the column waves");
-  constexpr int ND = DMA_SLOT / NC;           // DMA instructions per wave per group
-  constexpr int NWL = (B == 3 || B == 4) ? 2 : 3;   // buffer loads per group: chunk + scale
-  // issued after X(j) (at step j - D): W(j), then D - 1 steps of X + W
-  constexpr int VM_AHEAD = NWL + (D - 1) * (ND + NWL);
-  static_assert(VM_AHEAD < 64, "vmcnt field");
+  constexpr int PIECES = XSLOT / 1024;        // 1 KB pieces per slice (64 lanes x 16 bytes)
+  static_assert(PIECES % NC == 0, "the slice must split evenly over the column waves");
+  constexpr int ND = PIECES / NC;             // pieces per wave per group
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = wave % NC, h = wave / NC;
@@ -772,19 +770,26 @@ __device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLd
   const uint32_t woff = (uint32_t)(c * 16 + lr) * row_bytes + (uint32_t)lq * 4 * B;
   const uint32_t soffs = (uint32_t)(c * 16 + lr) * (uint32_t)G * 4;
 
-  // X DMA: instruction d of this wave fills 1 KB block c*ND + d of the slice:
-  // rows 4*(c*ND+d) + lane/16, slot lane%16 = logical chunk ^ (row & 15).
+  // X piece d of this wave: 1 KB block c*ND + d of the slice, rows
+  // 4*(c*ND+d) + lane/16; the lane's 16 bytes go to LDS position lane % 16 of
+  // its row and hold logical chunk (lane % 16) ^ (row & 15) (conflict-free
+  // operand reads).  Rows past M read zeros.
   const rsrc_t rx = make_rsrc(args.x, (uint32_t)args.m * (uint32_t)K * 2);
-  auto issue_x = [&](uint8_t* slot_base, int j) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 xr[S][ND];
+  auto load_x = [&](int slot, int j) {
     const int g = min(g_begin + j, g_last);
-    uint8_t* base = slot_base + (c * ND) * 1024;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       const int row = 4 * (c * ND + d) + (lane >> 4);
       const uint32_t voff = (uint32_t)row * (uint32_t)K * 2 + (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + d * 1024), 16, voff,
-                                               (uint32_t)g * kGroup * 2, 0, 0);
+      xr[slot][d] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, (uint32_t)g * kGroup * 2, 0);
     }
+  };
+  auto write_x = [&](uint8_t* slot_base, int slot) {
+    uint8_t* base = slot_base + (c * ND) * 1024 + lane * 16;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) *reinterpret_cast<u4*>(base + d * 1024) = xr[slot][d];
   };
   uint32_t aoff[4];
 #pragma unroll
@@ -824,46 +829,28 @@ __device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLd
     }
   };
 
-  // Step j (ring slot j % S for both rings): wait for X(j), barrier, issue
-  // X(j+D) and W(j+D) into slot (j-1) % S, compute step j.
-  //
-  // The wait leaves in flight exactly the loads issued after X(j): W(j), then
-  // X and W of every later step issued so far.  In the main loop that is D - 1
-  // steps; at tail step U (which issues nothing: its loads would be for steps
-  // past the end) it is D - 1 - U.  The count must be exact, not an upper
-  // bound: with fewer loads in flight than it allows, the wait would pass with
-  // this wave's share of X(j) still landing, and the barrier would hand the
-  // slot to the other column waves too early.  (A tail that issued loads would
-  // break it: their registers are never read, so the compiler drops the weight
-  // loads and keeps only the DMAs.)
+  // Step j (ring slot j % S of the three rings): write this wave's share of
+  // X(j) into LDS slot j % S, LDS barrier (every wave's share is there, and
+  // every wave is done with step j - 1, so slot (j - 1) % S is free), load
+  // X(j+D) and W(j+D) into register slot (j - 1) % S, compute step j.  Slot
+  // j % S last held X(j - S), read at step j - S <= j - 2, which every wave
+  // finished before the barrier of step j - 1.  The last steps (the tail)
+  // load nothing: their loads would be for steps past the end.
   using std::integral_constant;
-  constexpr auto vm_imm = [](int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); };
   auto step = [&]<int U, bool TAIL>(integral_constant<int, U>, std::bool_constant<TAIL>, int j) {
-    // own X DMA of step j landed; then every wave's has, and every wave is
-    // done with slot (j-1) % S.  A bare s_barrier: a fenced barrier would
-    // also wait for the loads of later steps still in flight.
-    constexpr int AHEAD = TAIL ? NWL + (D - 1 - U) * (ND + NWL) : VM_AHEAD;
-    static_assert(AHEAD >= NWL && AHEAD < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(vm_imm(AHEAD));
-    asm volatile("s_barrier" ::: "memory");
+    write_x(xslot(integral_constant<int, U % S>{}), U % S);
+    lds_barrier();
     if constexpr (!TAIL) {
-      issue_x(xslot(integral_constant<int, (U + D) % S>{}), j + D);
-      __builtin_amdgcn_sched_barrier(0);
+      load_x((U + D) % S, j + D);
       load_w((U + D) % S, j + D);
-      __builtin_amdgcn_sched_barrier(0);
     }
     if (j < cnt) compute(xslot(integral_constant<int, U % S>{}), U % S);
   };
-  // prologue: steps 0..D-1, X then W per step (the order of the steady state)
+  // prologue: steps 0..D-1
   [&]<int... J>(std::integer_sequence<int, J...>) {
-    // (sched_barrier on both sides of the weight loads: the scheduler would
-    // otherwise move them among or ahead of the X DMAs, or sink the scale
-    // loads to the end, and the counted waits above assume this order)
-    ((issue_x(xslot(integral_constant<int, J>{}), J), __builtin_amdgcn_sched_barrier(0),
-      load_w(J, J), __builtin_amdgcn_sched_barrier(0)), ...);
+    ((load_x(J, J), load_w(J, J)), ...);
   }(std::make_integer_sequence<int, D>{});
-  // main loop: whole blocks of S steps, every load unconditional (so the
-  // compiler's wait counts stay exact across the loop, and no load is dead)
+  // main loop: whole blocks of S steps (every ring index a constant)
   const int full = steps / S * S;
   for (int j0 = 0; j0 < full; j0 += S) {
     [&]<int... U>(std::integer_sequence<int, U...>) {

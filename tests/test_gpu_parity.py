@@ -398,6 +398,28 @@ def test_gemm_streamk(gpu_lib, m, n, k, bits):
     assert np.max(np.abs(y1 - y_plain)) <= 1e-5 * np.max(np.abs(y_plain)) + 1e-6
 
 
+# ------------------------------------------------------------------ M <= 16: repeatability
+@pytest.mark.parametrize("m,n,k,bits", [
+    (16, 3072, 3072, 4), (1, 16, 128, 3), (5, 272, 384, 5), (16, 5120, 5120, 4), (11, 5120, 13824, 5),
+    (16, 15360, 5120, 6), (3, 1040, 1024, 7), (16, 48, 40960, 6), (2, 12816, 640, 3)])
+def test_gemm_small_m_repeatable(gpu_lib, m, n, k, bits):
+    """The M <= 16 kernels (K split inside a workgroup, partial tiles added in
+    wave order) against the oracle, equal to themselves bit for bit on a
+    second call, with and without a workspace (they use none)."""
+    _case(f"dequant_gemm M<=16 repeatability m={m} n={n} k={k} bits={bits}")
+    c = synth.random_case(m * 31 + n + k, m, n, k)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+    assert gpu_lib.workspace_bytes(m, n, k, 0) == 0
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    xd = dev_bf16(c["x"])
+    y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], bits))
+    y1 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=ws))
+    y2 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "results differ between calls"
+    check_product(y1, y_ref, False, "f32")
+    check_product(host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16)), y_ref, True, "bf16")
+
+
 # ------------------------------------------------------------------ low-rank branch
 def _lowrank_case(api, x, w, bits, r, rows=None, out=torch.float32):
     l1, l2, res = O.svd_split(w, r)

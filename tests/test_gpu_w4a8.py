@@ -216,6 +216,10 @@ def test_fp4_quantize_tiled_bit_exact(gpu_lib, fmt, n, k, f32, pow2):
     assert qw.tiled and qw.packed.shape == t.shape and qw.scales.shape == ts.shape
     assert np.array_equal(host(qw.packed), t)                  # padding columns included: zero codes
     assert np.array_equal(host(qw.scales).view(np.uint32), ts.view(np.uint32))
+    # layout-free: back in row order, the codes and scales are the oracle's
+    back, bs = F.untile_fp4(host(qw.packed), host(qw.scales), n, k)
+    assert np.array_equal(F.unpack_fp4(back), codes)
+    assert np.array_equal(np.asarray(bs, dtype=np.float32).view(np.uint32), s.view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt", list(F.FP4_FORMATS))
@@ -264,6 +268,7 @@ def test_fp6_rows_bit_exact(gpu_lib, fmt, m, k):
     xq, xs = gpu_lib.fp6_quantize_rows(dev_bf16(x), fmt)
     cq, cs = F.quantize_rows_fp6(x, fmt)
     assert np.array_equal(host(xq), F.pack_fp6_tiled(cq))  # padding rows included: zero codes
+    assert np.array_equal(F.unpack_fp6_tiled(host(xq), m, k), cq)   # layout-free: row order
     assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
 
 
