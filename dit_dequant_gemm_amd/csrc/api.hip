@@ -77,6 +77,11 @@ struct LargeF {
   static hipError_t run(A... a) { return ddg::launch_gemm_large<B>(a...); }
 };
 template <int B>
+struct N192F {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_n192<B>(a...); }
+};
+template <int B>
 struct SkinnyF {
   template <typename... A>
   static hipError_t run(A... a) { return ddg::launch_gemm_skinny<B>(a...); }
@@ -156,6 +161,22 @@ int k_split_form(int64_t tiles, int groups, int grid) {
   return spread <= 0.7 * whole ? -1 : 0;
 }
 
+// 256 x 192 tiles (K2n) instead of 256 x 256 (whole tiles, or stream-K when
+// form is -1), from interleaved timings: a round of 256 x 192 tiles over the
+// compute units takes about 0.79 of a round of 256 x 256 tiles, and stream-K
+// costs about 1.45 rounds per (tiles / units) (4096 x 5120 x 5120: 320 tiles,
+// 214 us against 236 us for two whole rounds).  K2n is taken when its rounds
+// come to at most 0.95 of the 256 x 256 plan's: 4096 x 3072 x 3072 (192
+// tiles of 256 x 256, 256 of 256 x 192: 69 against 72 us), 4096 x 3072 x
+// 12288 (278 against 292 us), 4096 x 5120 x 5120; not 4096 x 12288 x 3072
+// (3 rounds against 4: 256 against 269 us) nor 32760 x 5120 x 5120.
+bool prefer_n192(int64_t tiles256, int64_t tiles192, int form, int cus) {
+  if (cus <= 0) return false;
+  const double t256 = form < 0 ? 1.45 * (double)tiles256 / cus : (double)((tiles256 + cus - 1) / cus);
+  const double t192 = 0.79 * (double)((tiles192 + cus - 1) / cus);
+  return t192 <= 0.95 * t256;
+}
+
 // Workspace bytes of stream-K for an m x n output (0 where it is never used).
 size_t streamk_bytes(int64_t m, int64_t n) {
   if (m <= 64) return 0;
@@ -228,6 +249,13 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
   if (tiles > kMaxDim) return hipErrorInvalidValue;
   const int grid_max = streamk_grid(cus);
   const int form = sk.p != nullptr ? k_split_form(tiles, a.k / DDG_GROUP, grid_max) : 0;
+  if (form <= 0) {
+    const int tn192 = (int)((a.n + ddg::kBN192 - 1) / ddg::kBN192);
+    if (prefer_n192(tiles, (int64_t)a.tiles_m * tn192, form, cus)) {
+      a.tiles_n = tn192;
+      return by_bits<N192F>(bits, a, stream);
+    }
+  }
   if (form != 0 && sk.bytes >= (size_t)grid_max * kSkSlotBytes + (size_t)grid_max * sizeof(unsigned long long)) {
     ddg::StreamK k{};
     k.partials = static_cast<float*>(sk.p);
@@ -521,7 +549,7 @@ extern "C" int ddg_lowrank_fused_gemm_noalloc(const void* x, int64_t m, int64_t 
   void* t = nullptr;
   if (int st = scratch_ptr(&t)) return st;
   return hip_status(launch_lowrank(x, m, k, packed, scales, bits, n, lora_down, lora_up, r, y, y_dtype,
-                                   static_cast<__bf16*>(t), stream));
+                                   static_cast<__bf16*>(t), stream, Scratch{}, cus));
 }
 
 extern "C" {

@@ -41,6 +41,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Bytes 2H, 2H+1 of w as floats, for bytes below 16 (codes plus one): an E4M3
+// byte whose top nibble is zero has exponent field 0 (value m 2^-9) or 1
+// (value (8 + m) 2^-9), i.e. the byte's integer value times 2^-9, so the
+// scaled FP8 conversion with scale 2^9 returns the integer exactly, two
+// bytes per instruction (v_cvt_scalef32_pk_f32_fp8).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int H>
+__device__ __forceinline__ f32x2 small_bytes_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, H != 0);
+}
+
 // fl32(q * s) given v = q + 64 as a float and ns64 = -64 * s.
 __device__ __forceinline__ float scale_code(float v, float s, float ns64) {
   return __builtin_fmaf(v, s, ns64);
@@ -87,20 +98,22 @@ __device__ __forceinline__ bf16x8 dequant8(const uint32_t* raw, const uint32_t* 
 }
 
 // Pair P (codes 8*S+2P, 8*S+2P+1) of a chunk as one packed bf16 pair.  For
-// B == 4, `nib` holds the two nibble-spread words of dword S (see
-// spread_nibbles); otherwise `be` holds the byte-swapped dwords.  S and P must
-// fold to constants after inlining.
+// B == 4, `nib` holds the two words of spread_nibbles for dword S (codes plus
+// one, as bytes) and nb = -8 s; otherwise `be` holds the byte-swapped dwords
+// and nb = -64 s (codes plus 64).  S and P must fold to constants after
+// inlining.
 template <int B>
 __device__ __forceinline__ uint32_t dequant_pair(const uint32_t* be, const uint32_t* nib, int S,
-                                                 int P, float s, float ns64) {
+                                                 int P, float s, float nb) {
   if constexpr (B == 4) {
-    const float a = (float)((nib[0] >> (8 * P)) & 0xFFu);
-    const float b = (float)((nib[1] >> (8 * P)) & 0xFFu);
-    return pack_bf16x2(scale_code(a, s, ns64), scale_code(b, s, ns64));
+    const f32x2 e = (P >> 1) ? small_bytes_f32<1>(nib[0]) : small_bytes_f32<0>(nib[0]);
+    const f32x2 o = (P >> 1) ? small_bytes_f32<1>(nib[1]) : small_bytes_f32<0>(nib[1]);
+    return pack_bf16x2(__builtin_fmaf((P & 1) ? e.y : e.x, s, nb),
+                       __builtin_fmaf((P & 1) ? o.y : o.x, s, nb));
   } else {
     const uint32_t c0 = chunk_code<B>(be, 8 * S + 2 * P) + Bits<B>::bias64;
     const uint32_t c1 = chunk_code<B>(be, 8 * S + 2 * P + 1) + Bits<B>::bias64;
-    return pack_bf16x2(scale_code((float)c0, s, ns64), scale_code((float)c1, s, ns64));
+    return pack_bf16x2(scale_code((float)c0, s, nb), scale_code((float)c1, s, nb));
   }
 }
 
@@ -153,16 +166,14 @@ __device__ __forceinline__ bf16x8 dequant8_p1(const uint32_t* be1, uint32_t x1, 
   if constexpr (B == 4) {
     uint32_t ev = (x1 >> 4) & 0x0F0F0F0Fu;
     uint32_t od = x1 & 0x0F0F0F0Fu;
-    // keep the two masked words: each byte then converts with one
-    // v_cvt_f32_ubyteN (the compiler would otherwise extract every nibble
-    // with its own bit-field extract)
+    // keep the two masked words: two bytes then convert per instruction
     asm("" : "+v"(ev), "+v"(od));
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float a = (float)((ev >> (8 * p)) & 0xFFu);
-      const float b = (float)((od >> (8 * p)) & 0xFFu);
-      out[p] = pack_bf16x2(__builtin_fmaf(a, s, nsh), __builtin_fmaf(b, s, nsh));
-    }
+    const f32x2 e0 = small_bytes_f32<0>(ev), e1 = small_bytes_f32<1>(ev);
+    const f32x2 o0 = small_bytes_f32<0>(od), o1 = small_bytes_f32<1>(od);
+    out[0] = pack_bf16x2(__builtin_fmaf(e0.x, s, nsh), __builtin_fmaf(o0.x, s, nsh));
+    out[1] = pack_bf16x2(__builtin_fmaf(e0.y, s, nsh), __builtin_fmaf(o0.y, s, nsh));
+    out[2] = pack_bf16x2(__builtin_fmaf(e1.x, s, nsh), __builtin_fmaf(o1.x, s, nsh));
+    out[3] = pack_bf16x2(__builtin_fmaf(e1.y, s, nsh), __builtin_fmaf(o1.y, s, nsh));
   } else {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -174,10 +185,12 @@ __device__ __forceinline__ bf16x8 dequant8_p1(const uint32_t* be1, uint32_t x1, 
   return __builtin_bit_cast(bf16x8, out);
 }
 
-// 4-bit only: dword x -> {even codes, odd codes} as bytes q + 64.
+// 4-bit only: dword x -> {even codes, odd codes} plus one, as bytes (every
+// code is at most 14, so adding 1 to each nibble carries into no other).
 __device__ __forceinline__ void spread_nibbles(uint32_t x, uint32_t* nib) {
-  nib[0] = ((x >> 4) & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
-  nib[1] = (x & 0x0F0F0F0Fu) + 0x01010101u * Bits<4>::bias64;
+  const uint32_t x1 = x + 0x11111111u;
+  nib[0] = (x1 >> 4) & 0x0F0F0F0Fu;
+  nib[1] = x1 & 0x0F0F0F0Fu;
 }
 
 template <int B>

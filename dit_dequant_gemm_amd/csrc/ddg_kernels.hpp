@@ -6,6 +6,10 @@
 //   gemm_large_kernel     Y = X w_hat^T for many tokens: bf16 MFMA, X tiles
 //                         staged HBM->LDS, packed weights streamed to
 //                         registers and dequantized there (§3.4 + §5.4)
+//   gemm_n192_kernel      the same with 256 x 192 tiles, for outputs that
+//                         256 x 256 tiles cover with compute units left idle
+//   gemm_streamk_kernel   the same with K split across workgroups (split-K,
+//                         stream-K) for products with few tiles
 //   gemm_small_kernel     the same product for M <= 64 tokens: a bandwidth
 //                         kernel that streams the packed weights once
 //   lowrank_t_kernel      T = bf16(X L1) for the low-rank branch (SVDQuant
@@ -322,7 +326,7 @@ __device__ __forceinline__ void large_accumulate(const GemmArgs& args, int tm, i
 #pragma unroll
       for (int j = 0; j < CW; ++j) be[j] = __builtin_bswap32(wc[j]);
     }
-    ns64 = -64.0f * sc;
+    ns64 = (B == 4 ? -8.0f : -64.0f) * sc;   // dequant_pair's offset
   };
   // dequantization job p (bf16 pair p, 0..3) of k-step ks
   auto dq_job = [&](int p, int ks) {
@@ -445,6 +449,292 @@ template <int B>
 __global__ __launch_bounds__(512, 1) void gemm_large_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
   large_tile<B>(args, blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------------------
+// K2n: large-M GEMM with 256 x 192 tiles, for outputs that 256 x 256 tiles
+// cover with compute units left idle (4096 x 3072: 192 tiles of 256 x 256 for
+// 256 units, 256 tiles of 256 x 192).  Workgroup = 4 waves, one per SIMD;
+// wave w owns columns [48w, 48w + 48) for all 256 rows as three column blocks
+// of 16, so every packed weight is still dequantized once per workgroup and
+// each A fragment feeds three MFMAs.  MFMA v_mfma_f32_16x16x32_bf16: A = X
+// rows (LDS), B = dequantized weights (registers), 192 accumulators per lane.
+// K index inside a group: k-step j (0..3), lane quarter q = lane / 16,
+// element e uses input 32q + 8j + e, for both operands.  X goes HBM -> LDS
+// as in K2 (64 KB stages, double-buffered; row r holds 16 chunks of 16 bytes,
+// logical chunk c in slot c ^ (r & 15)); the A fragment of lane (row r,
+// quarter q) at k-step j is chunk 4q + j.  Lane (column lr = lane % 16,
+// quarter q) of column block c streams the chunk of codes 32q .. 32q + 31 of
+// column 48w + 16c + lr, one group ahead, and dequantizes it in the plus-one
+// form (as dequant8_p1).
+// ---------------------------------------------------------------------------
+constexpr int kBN192 = 192;
+constexpr int kEpi48Stride = 52;     // floats per scratch row (48 + 4: conflict-free writes)
+
+template <int B>
+__device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, uint8_t* lds) {
+  constexpr int RB = kBM / 16;          // 16 row blocks of 16
+  constexpr int CB = 3;                 // column blocks of 16 per wave
+  constexpr int KS = 4;                 // k-steps of 32 per group
+  constexpr int STEPS = KS * RB;        // 64 steps of three MFMAs
+  constexpr int LA = 3;                 // A-operand look-ahead, in steps
+  constexpr int RING = 4;
+  constexpr int HAND = STEPS - LA;      // step of the group hand-over (barrier)
+  constexpr int JOBS = CB * 4;          // dequantization jobs (bf16 pairs) per k-step
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = tm * kBM;
+  const int nw0 = tn * kBN192;
+  const int K = args.k;
+  const int G = K / kGroup;
+  const uint32_t row_bytes = (uint32_t)K * B / 8;
+  const uint32_t xrow_bytes = (uint32_t)K * 2;
+  const int m_valid = min(kBM, args.m - m0);
+  const int n_valid = min(kBN192, args.n - nw0);
+  // Rows past M / columns past N read as zeros (their results are not stored).
+  const rsrc_t rx = make_rsrc(args.x + (int64_t)m0 * K, (uint32_t)m_valid * xrow_bytes);
+  const rsrc_t rw = make_rsrc(args.packed + (int64_t)nw0 * row_bytes, (uint32_t)n_valid * row_bytes);
+  const rsrc_t rs = make_rsrc(args.scales + (int64_t)nw0 * G, (uint32_t)n_valid * G * 4);
+
+  // X -> LDS.  DMA instruction i (0..15) of wave w fills 1 KB block 16w + i:
+  // rows 64w + 4i + lane/16, slot lane%16, holding logical chunk slot ^ (row & 15).
+  uint32_t xoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 64 + 4 * j + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    xoff[j] = (uint32_t)r * xrow_bytes + (uint32_t)c * 16;
+  }
+  auto issue_x_one = [&](int g, int stage, int i) {
+    uint8_t* base = lds + stage * kLdsStage + wave * 16 * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + i * 1024), 16,
+                                             xoff[i & 3] + (uint32_t)(i >> 2) * 16 * xrow_bytes,
+                                             (uint32_t)g * kGroup * 2, 0, 0);
+  };
+
+  // Packed chunks and scales of the lane's three columns.
+  const uint32_t ncol = (uint32_t)(wave * 48 + lr);
+  const uint32_t woff = ncol * row_bytes + (uint32_t)lq * 4 * B;
+  const uint32_t soffs = ncol * (uint32_t)G * 4;
+  auto load_w = [&](int g, uint32_t (&w)[CB][B], float (&s)[CB]) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      load_chunk_buf<B>(rw, woff + (uint32_t)c * 16 * row_bytes, (uint32_t)g * 16 * B, w[c]);
+      s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, soffs + (uint32_t)c * 16 * G * 4, (uint32_t)g * 4, 0));
+    }
+  };
+
+  // A operand of step u (k-step u/16, row block u%16) from an LDS stage.
+  uint32_t aoff[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) aoff[j] = (uint32_t)(lr * 256 + (((4 * lq + j) ^ lr) * 16));
+  auto read_a = [&](int stage, int u) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(lds + stage * kLdsStage + (u & 15) * 4096 + aoff[u >> 4]);
+  };
+
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (args.t != nullptr) {
+    // acc = T * lora_up^T over the rank dimension, 32 at a time (zero-padded).
+    const int R = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int j0 = 0; j0 < R; j0 += 32) {
+      const int kk = j0 + 8 * lq;
+      const bool kok = kk < R;
+      const int kc = min(kk, R - 8);
+      bf16x8 bl[CB];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int n = min(nw0 + (int)ncol + 16 * c, args.n - 1);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
+        bl[c] = kok ? v : zero;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int m = min(m0 + rb * 16 + lr, args.m - 1);
+        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
+        const bf16x8 a = kok ? tv : zero;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[rb][c] = mfma16x16x32(a, bl[c], acc[rb][c]);
+      }
+    }
+  }
+
+  uint32_t wc[CB][B], wn[CB][B], be1[CB][B];
+  float sc[CB], sn[CB], nsh[CB];
+  uint32_t ev[CB], od[CB];              // 4-bit: the chunk dword's codes plus one, as bytes
+  bf16x8 ring[RING];
+  u32x4 bc[CB], bnx[CB];
+
+  auto take_next_weights = [&]() {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) wc[c][j] = wn[c][j];
+      sc[c] = sn[c];
+      if constexpr (B != 4) plus_one_words<B>(wc[c], be1[c]);
+      nsh[c] = -(float)(1 << (B - 1)) * sc[c];
+    }
+  };
+  // dequantization job (chunk c, bf16 pair p) of k-step ks: codes 8ks + 2p, 8ks + 2p + 1
+  auto dq_job = [&](int c, int p, int ks) {
+    float a, b;
+    if constexpr (B == 4) {
+      if (p == 0) {
+        const uint32_t x1 = wc[c][ks] + 0x11111111u;
+        ev[c] = (x1 >> 4) & 0x0F0F0F0Fu;
+        od[c] = x1 & 0x0F0F0F0Fu;
+        // keep the masked words (two bytes per conversion below)
+        asm("" : "+v"(ev[c]), "+v"(od[c]));
+      }
+      const f32x2 fa = (p >> 1) ? small_bytes_f32<1>(ev[c]) : small_bytes_f32<0>(ev[c]);
+      const f32x2 fb = (p >> 1) ? small_bytes_f32<1>(od[c]) : small_bytes_f32<0>(od[c]);
+      a = (p & 1) ? fa.y : fa.x;
+      b = (p & 1) ? fb.y : fb.x;
+    } else {
+      a = (float)chunk_code_p1<B>(be1[c], 8 * ks + 2 * p);
+      b = (float)chunk_code_p1<B>(be1[c], 8 * ks + 2 * p + 1);
+    }
+    bnx[c][p] = pack_bf16x2(__builtin_fmaf(a, sc[c], nsh[c]), __builtin_fmaf(b, sc[c], nsh[c]));
+  };
+
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_x_one(0, 0, i);
+  load_w(0, wn, sn);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  take_next_weights();
+#pragma unroll
+  for (int u = 0; u < LA; ++u) ring[u % RING] = read_a(0, u);
+#pragma unroll
+  for (int j = 0; j < JOBS; ++j) dq_job(j >> 2, j & 3, 0);
+#pragma unroll
+  for (int c = 0; c < CB; ++c) bc[c] = bnx[c];
+
+  // One 128-group: 64 steps (4 k-steps x 16 row blocks), three MFMAs each.
+  // Every step index is a compile-time constant, so the operand ring and the
+  // dequantization schedule are static:
+  //   steps 0..15   one X DMA instruction each (next group -> idle stage)
+  //   step 16       packed chunks + scales of the next group
+  //   every step    one LDS read LA steps ahead; on row blocks 0..11 one
+  //                 dequantization job for the next k-step; 3 MFMAs
+  //   end of ks = 2 switch to the next group's weights (their loads landed)
+  //   step HAND     barrier: the next group's X is in LDS, this stage is free
+  // The last group's "next group" is itself (clamped), fetched into the idle
+  // stage and never used.
+  auto group = [&](int g, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const int gn = min(g + 1, G - 1);
+    auto step = [&]<int T>(std::integral_constant<int, T>) {
+      constexpr int ks = T >> 4, rb = T & 15;
+      if constexpr (T < 16) issue_x_one(gn, ST ^ 1, T);
+      if constexpr (T == 16) load_w(gn, wn, sn);
+      if constexpr (T == HAND) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      constexpr int u = T + LA;
+      if constexpr (u < STEPS) {
+        ring[u % RING] = read_a(ST, u);
+      } else {
+        ring[u % RING] = read_a(ST ^ 1, u - STEPS);
+      }
+      if constexpr (rb < JOBS) dq_job(rb >> 2, rb & 3, (ks + 1) & 3);
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+        acc[rb][c] = mfma16x16x32(ring[T % RING], __builtin_bit_cast(bf16x8, bc[c]), acc[rb][c]);
+      if constexpr (rb == RB - 1) {
+#pragma unroll
+        for (int c = 0; c < CB; ++c) bc[c] = bnx[c];
+        if constexpr (ks == KS - 2) take_next_weights();
+      }
+      // the VALU work rides in the shadow of the three MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... T>(std::integer_sequence<int, T...>) {
+      (step(std::integral_constant<int, T>{}), ...);
+    }(std::make_integer_sequence<int, STEPS>{});
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    group(g, I0{});
+    group(g + 1, I1{});
+  }
+  if (g < G) group(g, I0{});
+  __syncthreads();
+
+  // Epilogue: two row blocks (32 x 48) at a time through a per-wave scratch
+  // in LDS, leaving as 16-byte pieces of rows.
+  float* scratch = reinterpret_cast<float*>(lds + wave * 32 * kEpi48Stride * 4);
+  const bool bf = args.out_bf16 != 0;
+  const bool vec = epi_vec_ok(args.y, args.n, bf);
+  const int col0 = nw0 + wave * 48;
+#pragma unroll
+  for (int rp = 0; rp < RB / 2; ++rp) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          scratch[(16 * h + 4 * lq + i) * kEpi48Stride + 16 * c + lr] = acc[2 * rp + h][c][i];
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int W = bf ? 8 : 4;                              // values per 16-byte piece
+    const int per_row = 48 / W;
+    const int pieces = 32 * per_row;
+    for (int q = lane; q < pieces; q += 64) {
+      const int row = q / per_row, cc = (q - row * per_row) * W;
+      const int gr = m0 + 32 * rp + row, gc = col0 + cc;
+      if (gr >= args.m || gc >= args.n) continue;
+      const float* src = scratch + row * kEpi48Stride + cc;
+      const int64_t base = (int64_t)gr * args.n + gc;
+      if (bf) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+        __bf16 v[8] = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                       (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+        __bf16* dst = static_cast<__bf16*>(args.y) + base;
+        if (vec && gc + 8 <= args.n) {
+          *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
+        } else {
+          for (int e = 0; e < 8 && gc + e < args.n; ++e) dst[e] = v[e];
+        }
+      } else {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(src);
+        float* dst = static_cast<float*>(args.y) + base;
+        if (vec && gc + 4 <= args.n) {
+          *reinterpret_cast<f32x4*>(dst) = t;
+        } else {
+          for (int e = 0; e < 4 && gc + e < args.n; ++e) dst[e] = t[e];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(256, 1) void gemm_n192_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kLdsStage];
+  int tm, tn;
+  tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+  n192_tile<B>(args, tm, tn, lds);
 }
 
 // ---------------------------------------------------------------------------

@@ -18,6 +18,9 @@ hipError_t launch_dequantize(const uint8_t* packed, const float* scales, int64_t
 // a.tiles_m / a.tiles_n: 256 x 256 tiles
 template <int B>
 hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t stream);
+// a.tiles_m / a.tiles_n: 256 x 192 tiles
+template <int B>
+hipError_t launch_gemm_n192(const GemmArgs& a, hipStream_t stream);
 // rb: row blocks (of 16) in 1, 2, 4; nc column waves x nk K-split waves per
 // workgroup: (2,2) (1,4) (1,8) (2,4) (4,2) for rb = 1, (1,4) (2,2) otherwise
 template <int B>

@@ -40,6 +40,12 @@ hipError_t launch_gemm_large<DDG_BITS>(const GemmArgs& a, hipStream_t stream) {
 }
 
 template <>
+hipError_t launch_gemm_n192<DDG_BITS>(const GemmArgs& a, hipStream_t stream) {
+  gemm_n192_kernel<DDG_BITS><<<dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <>
 hipError_t launch_gemm_streamk<DDG_BITS>(const GemmArgs& a, const StreamK& sk, int grid, hipStream_t stream) {
   gemm_streamk_kernel<DDG_BITS><<<dim3((unsigned)grid), dim3(512), 0, stream>>>(a, sk);
   return hipGetLastError();

@@ -211,7 +211,10 @@ int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* p
 /*
  * ddg_lowrank_fused_gemm for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
- * allocation): the same arguments and results without `workspace`.  T goes to
+ * allocation): the same arguments without `workspace`, and the results of
+ * ddg_lowrank_fused_gemm given a workspace of T's bytes alone (whole output
+ * tiles, K never split across workgroups; with a larger workspace that call
+ * may split K, which sums in another order).  T goes to
  * a device array of DDG_NOALLOC_SCRATCH_BYTES bytes inside the library, one
  * per GPU, held from the first call on that GPU until the process ends (the
  * first call on a GPU looks up its address; no call allocates).  Every call on

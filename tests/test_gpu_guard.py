@@ -83,7 +83,9 @@ def test_quantize_pack_and_dequantize(gpu_lib, bits):
 PRODUCTS = [(257, 272, 384), (65, 48, 256), (15, 272, 384), (17, 272, 384), (33, 80, 512),
             (64, 272, 256), (16, 12816, 384), (5, 12816, 256), (1, 16, 128),
             (1041, 2320, 1536), (2100, 528, 6144),          # split-K: 50 tiles x 2, 27 x 8
-            (4160, 5136, 1280)]                             # stream-K: 357 tiles
+            (4160, 4080, 1280),                             # stream-K: 272 tiles
+            (4160, 5136, 1280),                             # 459 tiles of 256 x 192
+            (3800, 4112, 256)]                              # 255 tiles of 256 x 256
 
 
 @pytest.mark.parametrize("m,n,k", PRODUCTS)
@@ -122,7 +124,8 @@ def test_dequant_gemm_grouped(gpu_lib):
         check_product(host(g.t), ref, bf, f"grouped product {i}")
 
 
-@pytest.mark.parametrize("m,n,k", [(257, 272, 384), (17, 272, 384), (15, 272, 256), (5, 12816, 256)])
+@pytest.mark.parametrize("m,n,k", [(257, 272, 384), (17, 272, 384), (15, 272, 256), (5, 12816, 256),
+                                   (3800, 4112, 256)])
 def test_lowrank_fused_gemm(gpu_lib, m, n, k):
     r = 24
     _case(f"guards: lowrank_fused_gemm (workspace and no-allocation) m={m} n={n} k={k} r={r}")
