@@ -82,6 +82,11 @@ struct N192F {
   static hipError_t run(A... a) { return ddg::launch_gemm_n192<B>(a...); }
 };
 template <int B>
+struct SmallSplitF {
+  template <typename... A>
+  static hipError_t run(A... a) { return ddg::launch_gemm_small_split<B>(a...); }
+};
+template <int B>
 struct SkinnyF {
   template <typename... A>
   static hipError_t run(A... a) { return ddg::launch_gemm_skinny<B>(a...); }
@@ -185,6 +190,27 @@ size_t streamk_bytes(int64_t m, int64_t n) {
   return align256(kSkMaxGrid * kSkSlotBytes + kSkMaxGrid * sizeof(unsigned long long));
 }
 
+// The 16-token products that the skinny kernel does not take (fewer than
+// 200 workgroups of 64 columns) split K across workgroups when K is long (at
+// least 64 groups) and a workspace is given: 8 parts, column blocks in pairs
+// (two waves per workgroup).  Interleaved timings at 16 tokens, bf16 Y:
+// 5120 x 13824 (b = 5) 30.5 -> 24.5 us and 2048 x 8192 10.3 -> 9.2 us; with
+// shorter K the exchange costs what the spread saves (5120 x 5120: 10.8 us
+// whole, 11.1-11.8 split; 3072 x 3072 7.8 against 7.7-8.9; 1024 x 5120 7.51
+// against 7.54), and 4 column blocks per workgroup or 2, 4 or 16 parts were
+// no better.
+constexpr int kSplitNc = 2;
+int small_parts(int groups) { return groups >= 64 ? ddg::kSmallMaxParts : 1; }
+bool skinny_takes(int64_t m, int64_t n) { return m <= 16 && ((n + 15) / 16) / 4 >= 200; }
+
+// Workspace bytes of the split 16-token product (kSmallMaxParts parts of
+// every column block, padded to 4 blocks; 0 where it is never used).
+size_t small_split_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m > 16 || skinny_takes(m, n) || small_parts((int)(k / DDG_GROUP)) < 2) return 0;
+  const int64_t nb4 = ((n + 15) / 16 + 3) / 4 * 4;
+  return align256((size_t)nb4 * ddg::kSmallMaxParts * 1024) + align256((size_t)nb4 * ddg::kSmallMaxParts * 8);
+}
+
 // Launch epochs: unique per launch, never zero, from a random start (so a
 // fresh workspace's contents are not mistaken for a published flag).
 std::atomic<unsigned long long> g_epoch{0};
@@ -214,7 +240,7 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
     // into too many workgroups; the LDS-ring kernel below is faster there.
     const int64_t nb = ((int64_t)a.n + 15) / 16;
     const int g = a.k / DDG_GROUP;
-    if (nb / 4 >= 200) {
+    if (skinny_takes(a.m, a.n)) {
       int ncb = 4;
       int kc = skinny_chunk(g);
       // shrink until the weight buffers and the scale areas fit in LDS
@@ -223,6 +249,21 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
         if (ncb > 1) ncb /= 2; else --kc;
       }
       if (lds() <= ddg::kLdsLimit) return by_bits<SkinnyF>(bits, a, kc, ncb, stream);
+    }
+  }
+  if (a.m <= 16 && sk.p != nullptr && cus > 0) {
+    const int64_t nb = ((int64_t)a.n + 15) / 16;
+    const int parts = small_parts(a.k / DDG_GROUP);
+    const size_t need = small_split_bytes(a.m, a.n, a.k);
+    if (parts > 1 && need > 0 && sk.bytes >= need) {
+      const int64_t nb4 = (nb + 3) / 4 * 4;
+      ddg::SmallSplit sp{};
+      sp.partials = static_cast<float*>(sk.p);
+      sp.flags = reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(sk.p) +
+                                                       align256((size_t)nb4 * ddg::kSmallMaxParts * 1024));
+      sp.epoch = next_epoch();
+      sp.parts = parts;
+      return by_bits<SmallSplitF>(bits, a, kSplitNc, sp, stream);
     }
   }
   if (a.m <= 64) {
@@ -472,7 +513,7 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
   if (!bytes) return DDG_ERR_ARG;
   if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || k < 0 || (r != 0 && (r < 8 || r > 128 || r % 8)))
     return DDG_ERR_SHAPE;
-  *bytes = (r ? lowrank_t_bytes(m, r) : 0) + streamk_bytes(m, n);
+  *bytes = (r ? lowrank_t_bytes(m, r) : 0) + std::max(streamk_bytes(m, n), small_split_bytes(m, n, k));
   return DDG_OK;
 }
 

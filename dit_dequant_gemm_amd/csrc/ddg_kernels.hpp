@@ -1017,8 +1017,26 @@ struct SmallLds {
 
 // Workgroup `wg` of the product `args` (column block 16 NC wg ..).  Kernels:
 // gemm_small_kernel (one product) and gemm_grouped_small_kernel (several).
+// K split across workgroups for M <= 16 (one row block): workgroup (wg,
+// part) runs groups [part G / parts, (part + 1) G / parts) of its column
+// blocks.  Every part but the last publishes each column block's 16 x 16
+// partial sum (1 KB, the accumulator layout) to its slot and sets its flag;
+// the last part waits for the flags of the earlier parts (smaller workgroup
+// ids, dispatched before it), adds the partial sums in part order and its
+// own last (the same order on every call), and stores the result.  The
+// exchange uses the device-coherent accesses and epoch flags of StreamK.
+struct SmallSplit {
+  float* partials;                 // column blocks x parts x 256 floats
+  unsigned long long* flags;       // column blocks x parts
+  unsigned long long epoch;
+  int parts;                       // 1: K is not split
+};
+constexpr int kSmallMaxParts = 8;
+
 template <int B, int RB, int NC, int NK>
-__device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLds<RB, NC, NK>& L) {
+__device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLds<RB, NC, NK>& L,
+                                           const SmallSplit& sp = SmallSplit{nullptr, nullptr, 0, 1},
+                                           int part = 0) {
   // X slices and packed weights of step j + D are loaded into registers at
   // step j (rings of S = D + 1 slots); at step j each wave writes its share of
   // X(j) to the LDS slot, and one LDS barrier hands the slot to the other
@@ -1046,9 +1064,12 @@ __device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLd
   const int n0 = wg * 16 * NC;
   const int K = args.k;
   const int G = K / kGroup;
-  const int g_begin = h * G / NK, g_end = (h + 1) * G / NK;
+  // this workgroup's part of K, and this wave's share of it
+  const int ga = (int)((int64_t)part * G / sp.parts), gb = (int)((int64_t)(part + 1) * G / sp.parts);
+  const int gp = gb - ga;
+  const int g_begin = ga + h * gp / NK, g_end = ga + (h + 1) * gp / NK;
   const int cnt = g_end - g_begin;
-  const int steps = (G + NK - 1) / NK;        // the same for every wave (barriers)
+  const int steps = (gp + NK - 1) / NK;       // the same for every wave (barriers)
   const int g_last = cnt > 0 ? g_end - 1 : G - 1;
   const uint32_t row_bytes = (uint32_t)K * B / 8;
 
@@ -1176,6 +1197,48 @@ __device__ __forceinline__ void small_body(const GemmArgs& args, int wg, SmallLd
       }
   }
 
+  if constexpr (RB == 1) {
+    if (sp.parts > 1) {
+      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+      const int cb = wg * NC + c;                           // column block of 16
+      const rsrc_t rp = make_rsrc(sp.partials + (int64_t)cb * sp.parts * 256, (uint32_t)sp.parts * 1024u);
+      if (part < sp.parts - 1) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, acc[0]), rp, (uint32_t)lane * 16u,
+                                               (uint32_t)part * 1024u, kSkCoherent);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0)
+          __hip_atomic_store(&sp.flags[(int64_t)cb * sp.parts + part], sp.epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      for (int q = 0; q < sp.parts - 1; ++q) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(&sp.flags[(int64_t)cb * sp.parts + q], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) != sp.epoch &&
+               ++spins < kSkSpinLimit)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      // every earlier part's sums in flight at once (parts past the count read
+      // nothing: their offset lies past the resource), then added in order
+      u4 r[kSmallMaxParts - 1];
+#pragma unroll
+      for (int q = 0; q < kSmallMaxParts - 1; ++q)
+        r[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, q < sp.parts - 1 ? (uint32_t)lane * 16u : 0x80000000u,
+                                                     (uint32_t)q * 1024u, kSkCoherent);
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < kSmallMaxParts - 1; ++q) {
+        if (q < sp.parts - 1) {
+          const f32x4 v = __builtin_bit_cast(f32x4, r[q]);
+          sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+        }
+      }
+      sum[0] += acc[0][0]; sum[1] += acc[0][1]; sum[2] += acc[0][2]; sum[3] += acc[0][3];
+      acc[0] = sum;
+    }
+  }
+
   if (args.t != nullptr) {
     const int R_ = args.r;
     const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -1207,6 +1270,14 @@ template <int B, int RB, int NC, int NK>
 __global__ __launch_bounds__(64 * NC * NK) void gemm_small_kernel(GemmArgs args) {
   __shared__ SmallLds<RB, NC, NK> L;
   small_body<B, RB, NC, NK>(args, blockIdx.x, L);
+}
+
+// M <= 16 with K split across workgroups: workgroup id = wg * parts + part.
+template <int B, int NC>
+__global__ __launch_bounds__(64 * NC) void gemm_small_split_kernel(GemmArgs args, SmallSplit sp) {
+  __shared__ SmallLds<1, NC, 1> L;
+  const int wg = blockIdx.x / sp.parts, part = blockIdx.x - wg * sp.parts;
+  small_body<B, 1, NC, 1>(args, wg, L, sp, part);
 }
 
 // ---------------------------------------------------------------------------

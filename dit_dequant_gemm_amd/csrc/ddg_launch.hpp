@@ -31,6 +31,11 @@ hipError_t launch_gemm_small(const GemmArgs& a, int rb, int nc, int nk, hipStrea
 template <int B>
 hipError_t launch_gemm_streamk(const GemmArgs& a, const StreamK& sk, int grid, hipStream_t stream);
 
+// M <= 16 with K split across workgroups: nc (2) column blocks of 16 per
+// workgroup, sp.parts parts of K (grid ceil(n / 16 nc) x parts)
+template <int B>
+hipError_t launch_gemm_small_split(const GemmArgs& a, int nc, const SmallSplit& sp, hipStream_t stream);
+
 template <int B>
 hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t stream);
 

@@ -68,6 +68,15 @@ hipError_t launch_gemm_small<DDG_BITS>(const GemmArgs& a, int rb, int nc, int nk
 }
 
 template <>
+hipError_t launch_gemm_small_split<DDG_BITS>(const GemmArgs& a, int nc, const SmallSplit& sp,
+                                             hipStream_t stream) {
+  if (sp.parts < 2 || sp.parts > kSmallMaxParts || nc != 2) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n + 16 * nc - 1) / (16 * nc) * sp.parts));
+  gemm_small_split_kernel<DDG_BITS, 2><<<grid, dim3(128), 0, stream>>>(a, sp);
+  return hipGetLastError();
+}
+
+template <>
 hipError_t launch_gemm_skinny<DDG_BITS>(const GemmArgs& a, int kc, int ncb, hipStream_t stream) {
   const dim3 grid((unsigned)((a.n + 16 * ncb - 1) / (16 * ncb)));
   if (skinny_static_lds(DDG_BITS, kc, ncb) + skinny_scale_lds(kc) > kLdsLimit) return hipErrorInvalidValue;

@@ -123,13 +123,15 @@ int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t
  *   y       M x N, y_dtype (DDG_BF16 or DDG_F32), fully overwritten.
  *   workspace, workspace_bytes
  *           optional device scratch (NULL, 0: none; 16-byte aligned).  With
- *           at least ddg_workspace_bytes(M, N, K, 0) bytes, products whose
- *           256 x 256 output tiles would fill the compute units unevenly run
- *           as stream-K: K ranges of tiles split across workgroups, partial
- *           sums exchanged through the workspace.  Its contents need no
- *           initialisation and are scratch afterwards; calls that share a
- *           workspace must be ordered (one stream).  Results then differ
- *           from the call without workspace only in float32 summation order.
+ *           at least ddg_workspace_bytes(M, N, K, 0) bytes, K may be split
+ *           across workgroups, partial sums exchanged through the workspace:
+ *           products with M > 64 whose output tiles would fill the compute
+ *           units unevenly (split-K, stream-K), and products with M <= 16 and
+ *           K >= 8192 whose outputs are narrow (fewer than 12800 columns).
+ *           Its contents need no initialisation and are scratch afterwards;
+ *           calls that share a workspace must be ordered (one stream).
+ *           Results then differ from the call without workspace only in
+ *           float32 summation order (the same on every call).
  * Requirements: M >= 0 (M == 0 is a no-op), N a positive multiple of 16,
  * K a positive multiple of 128 and at most 2^20, M, N <= 2^31 - 1.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP.
@@ -174,10 +176,12 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
 
 /*
  * Workspace bytes for an M x K input and an N x K weight: with r = 0, what
- * ddg_dequant_gemm can use (the stream-K partial sums: 64 MiB and a flag per
- * workgroup where the output has fewer than 1024 tiles of 256 x 256, else 0);
- * with rank r, what ddg_lowrank_fused_gemm needs: the M x r bf16
- * intermediate T, rounded up to 256 bytes, followed by that stream-K area.
+ * ddg_dequant_gemm can use for split K (M > 64: 64 MiB of partial sums and
+ * a flag per workgroup where the output has fewer than 1024 tiles of
+ * 256 x 256; M <= 16, K >= 8192, N < 12800: 8 KiB of partial sums and 64
+ * bytes of flags per 16 output columns, padded to 64 columns; else 0); with
+ * rank r, what ddg_lowrank_fused_gemm needs: the M x r bf16 intermediate T,
+ * rounded up to 256 bytes, followed by that split-K area.
  * Host-only.
  * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m, n or k negative or m, n above
  * 2^31 - 1, r not 0 and outside 8..128 or not a multiple of 8).
@@ -195,7 +199,7 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
  * product); the branch term T * L2 is summed into the same float32
  * accumulator as the main product before y is written.
  *   workspace  device scratch: T first (M * r * 2 bytes rounded up to 256,
- *              required), then optionally the stream-K area of
+ *              required), then optionally the split-K area of
  *              ddg_dequant_gemm; ddg_workspace_bytes(M, N, K, r) bytes hold
  *              both.  Its contents are scratch (no initial state needed).
  * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0.

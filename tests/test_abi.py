@@ -83,6 +83,15 @@ def test_workspace_bytes(lib):
     assert lib.ddg_workspace_bytes(64, 3072, 3072, 0, ctypes.byref(b)) == OK and b.value == 0
     assert lib.ddg_workspace_bytes(32760, 5120, 5120, 0, ctypes.byref(b)) == OK and b.value == 0
     assert lib.ddg_workspace_bytes(1024, 5120, 5120, 32, ctypes.byref(b)) == OK and b.value == 1024 * 64 + sk
+    # 16 tokens, K >= 8192, fewer than 12800 columns: 8 parts x (1 KiB + 8 bytes)
+    # per block of 16 columns, blocks padded to a multiple of 4
+    split16 = lambda n: 8 * 1024 * ((n // 16 + 3) // 4 * 4) + -(-8 * 8 * ((n // 16 + 3) // 4 * 4) // 256) * 256
+    assert lib.ddg_workspace_bytes(16, 5120, 13824, 0, ctypes.byref(b)) == OK and b.value == split16(5120) == 2641920
+    assert lib.ddg_workspace_bytes(1, 1040, 8192, 0, ctypes.byref(b)) == OK and b.value == split16(1040)
+    assert lib.ddg_workspace_bytes(16, 5120, 13824, 32, ctypes.byref(b)) == OK and b.value == 1024 + split16(5120)
+    assert lib.ddg_workspace_bytes(16, 5120, 5120, 0, ctypes.byref(b)) == OK and b.value == 0       # K < 8192
+    assert lib.ddg_workspace_bytes(16, 12800, 8192, 0, ctypes.byref(b)) == OK and b.value == 0      # skinny kernel
+    assert lib.ddg_workspace_bytes(17, 5120, 13824, 0, ctypes.byref(b)) == OK and b.value == 0      # M > 16
     assert lib.ddg_workspace_bytes(64, -1, 128, 32, ctypes.byref(b)) == E_SHAPE
     assert lib.ddg_workspace_bytes(64, 16, -128, 32, ctypes.byref(b)) == E_SHAPE
     for r in (4, 12, 136, -8):

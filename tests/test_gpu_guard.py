@@ -85,7 +85,8 @@ PRODUCTS = [(257, 272, 384), (65, 48, 256), (15, 272, 384), (17, 272, 384), (33,
             (1041, 2320, 1536), (2100, 528, 6144),          # split-K: 50 tiles x 2, 27 x 8
             (4160, 4080, 1280),                             # stream-K: 272 tiles
             (4160, 5136, 1280),                             # 459 tiles of 256 x 192
-            (3800, 4112, 256)]                              # 255 tiles of 256 x 256
+            (3800, 4112, 256),                              # 255 tiles of 256 x 256
+            (16, 1040, 8192), (3, 272, 8320)]               # 16 tokens, K split in 8 parts
 
 
 @pytest.mark.parametrize("m,n,k", PRODUCTS)
@@ -125,7 +126,7 @@ def test_dequant_gemm_grouped(gpu_lib):
 
 
 @pytest.mark.parametrize("m,n,k", [(257, 272, 384), (17, 272, 384), (15, 272, 256), (5, 12816, 256),
-                                   (3800, 4112, 256)])
+                                   (3800, 4112, 256), (7, 272, 8192)])
 def test_lowrank_fused_gemm(gpu_lib, m, n, k):
     r = 24
     _case(f"guards: lowrank_fused_gemm (workspace and no-allocation) m={m} n={n} k={k} r={r}")

@@ -406,14 +406,41 @@ def test_gemm_streamk(gpu_lib, m, n, k, bits):
     assert np.max(np.abs(y1 - y_plain)) <= 1e-5 * np.max(np.abs(y_plain)) + 1e-6
 
 
+# ------------------------------------------------------------------ M <= 16: K split across workgroups
+@pytest.mark.parametrize("m,n,k,bits", [(16, 5120, 13824, 5), (7, 1040, 8192, 3), (1, 48, 8320, 7),
+                                        (16, 2048, 8192, 4), (13, 3184, 8192, 6), (16, 48, 40960, 6)])
+def test_gemm_small_m_split_k(gpu_lib, m, n, k, bits):
+    """16-token products with long K split K into 8 parts across workgroups
+    when given a workspace (odd column-block counts, parts of unequal group
+    counts): against the oracle, bit-identical on a second call, and within
+    float32 summation order of the call without a workspace."""
+    _case(f"dequant_gemm 16-token split K m={m} n={n} k={k} bits={bits}")
+    c = synth.random_case(m * 31 + n + k, m, n, k)
+    qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)
+    need = gpu_lib.workspace_bytes(m, n, k, 0)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    xd = dev_bf16(c["x"])
+    y_ref = O.gemm_ref(c["x"], _oracle_w16(c["w"], bits))
+    y1 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=ws))
+    y2 = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "split results differ between calls"
+    check_product(y1, y_ref, False, "split f32")
+    yb = host(gpu_lib.dequant_gemm(xd, qw, torch.bfloat16, workspace=ws))
+    check_product(yb, y_ref, True, "split bf16")
+    y_plain = host(gpu_lib.dequant_gemm(xd, qw, torch.float32, workspace=torch.empty(16, dtype=torch.uint8, device="cuda")))
+    assert np.max(np.abs(y1 - y_plain)) <= 1e-5 * np.max(np.abs(y_plain)) + 1e-6
+
+
 # ------------------------------------------------------------------ M <= 16: repeatability
 @pytest.mark.parametrize("m,n,k,bits", [
-    (16, 3072, 3072, 4), (1, 16, 128, 3), (5, 272, 384, 5), (16, 5120, 5120, 4), (11, 5120, 13824, 5),
-    (16, 15360, 5120, 6), (3, 1040, 1024, 7), (16, 48, 40960, 6), (2, 12816, 640, 3)])
+    (16, 3072, 3072, 4), (1, 16, 128, 3), (5, 272, 384, 5), (16, 5120, 5120, 4), (11, 5120, 6144, 5),
+    (16, 15360, 5120, 6), (3, 1040, 1024, 7), (16, 12800, 40960, 6), (2, 12816, 640, 3)])
 def test_gemm_small_m_repeatable(gpu_lib, m, n, k, bits):
-    """The M <= 16 kernels (K split inside a workgroup, partial tiles added in
-    wave order) against the oracle, equal to themselves bit for bit on a
-    second call, with and without a workspace (they use none)."""
+    """The M <= 16 kernels that keep K inside a workgroup (K < 8192, or
+    12800 columns and more; partial tiles added in wave order) against the
+    oracle, equal to themselves bit for bit on a second call, with and
+    without a workspace (they use none)."""
     _case(f"dequant_gemm M<=16 repeatability m={m} n={n} k={k} bits={bits}")
     c = synth.random_case(m * 31 + n + k, m, n, k)
     qw = gpu_lib.quantize_pack(dev_bf16(c["w"]), bits)

@@ -1,6 +1,6 @@
 """The fused low-rank product without a workspace (for callers that cannot
 allocate): through the C ABI, against the entry point that takes a
-workspace (same kernels: equal bit for bit) and against the oracle (the
+workspace, given one of T's bytes alone (same kernels: equal bit for bit) and against the oracle (the
 product's tolerance), on consecutive calls that share the library's device
 array, the second one smaller."""
 import ctypes
@@ -51,7 +51,9 @@ def test_noalloc_matches_workspace_call(gpu_lib, first, second):
     for i, (m, n, k, r, bits, dt) in enumerate((first, second)):
         _case(f"lowrank_fused_gemm_noalloc call {i}: m={m} n={n} k={k} r={r} bits={bits}")
         xh, x, qr, ld, lu, ref = _prepare(gpu_lib, 900 + 17 * i + m, m, n, k, r, bits)
-        y_ws = gpu_lib.lowrank_fused_gemm(x, qr, ld, lu, out_dtype=dt)
+        # a workspace of T's bytes alone: whole tiles, as the call without one
+        t_ws = torch.empty(max(256, -(-m * r * 2 // 256) * 256), dtype=torch.uint8, device="cuda")
+        y_ws = gpu_lib.lowrank_fused_gemm(x, qr, ld, lu, out_dtype=dt, workspace=t_ws)
         y_na = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
         cases.append((xh, x, qr, ld, lu, ref, y_ws, y_na, dt))
     torch.cuda.synchronize()
