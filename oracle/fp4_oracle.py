@@ -53,6 +53,15 @@ R23  Power-of-two scale mode (the scale format the matrix instructions apply
      themselves, E8M0): s = the smallest power of two >= fl32(amax / vmax), and at
      least 2^-126; then as R19 with that s.  Every code stays within the format's
      range, at the cost of up to one bit of it.
+R27  FP6 weights (a width the article names for activations only: §3.3's FP6
+     saves memory over FP8, §4.1's W4A6; this implementation also offers it for
+     weights): R25's formats E2M3 / E3M2 per group of 128 along the input
+     dimension, scale and rounding as R19 with 7.5 or 28 as vmax (R23 with
+     pow2); code = sign << 5 | magnitude index.  Storage: the codes in R26's
+     layout with the weight's rows (output channels) in place of tokens, the
+     scales tiled as R24's (32 per (column block, group)).
+R28  W6A8: Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k],
+     q_x the E4M3 activations of R20, v_w the FP6 weight values.
 """
 from __future__ import annotations
 
@@ -61,7 +70,8 @@ import numpy as np
 __all__ = ["FP4_FORMATS", "fp4_values", "minifloat_value", "quantize_fp4_groups", "pack_fp4",
            "unpack_fp4", "fp4_decode", "e4m3_values", "e4m3_round", "e4m3_decode",
            "quantize_rows_e4m3", "w4a8_ref", "tile_fp4", "untile_fp4", "FP6_FORMATS", "fp6_values",
-           "quantize_rows_fp6", "fp6_decode", "pack_fp6_tiled", "unpack_fp6_tiled", "w4a6_ref"]
+           "quantize_rows_fp6", "fp6_decode", "pack_fp6_tiled", "unpack_fp6_tiled", "w4a6_ref",
+           "quantize_fp6_groups", "tile_group_scales", "untile_group_scales", "w6a8_ref"]
 
 FP4_FORMATS = {"e2m1": (2, 1, 1), "e3m0": (3, 0, 3), "e1m2": (1, 2, 1)}   # ebits, mbits, bias
 FP6_FORMATS = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}
@@ -277,6 +287,58 @@ def w4a6_ref(xcodes, xscales, wcodes, wscales, wfmt: str, afmt: str) -> np.ndarr
     """R22 with FP6 activations, in float64."""
     qx = fp6_decode(xcodes, afmt)
     vw = fp4_decode(wcodes, wfmt)
+    m, k = qx.shape
+    y = np.zeros((m, vw.shape[0]), dtype=np.float64)
+    sw = np.asarray(wscales, dtype=np.float64)
+    for g in range(k // GROUP):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        y += (qx[:, sl] @ vw[:, sl].T) * sw[None, :, g]
+    return y * np.asarray(xscales, dtype=np.float64)[:, None]
+
+
+def quantize_fp6_groups(w, fmt: str, pow2: bool = False):
+    """(codes n x k uint8 in 0..63, scales n x k/128 float32) per R27: R19's
+    group quantizer with the FP6 levels (R23's scales with pow2)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    levels = fp6_values(fmt)
+    vmax = np.float32(levels[-1])
+    g = w.reshape(n, k // GROUP, GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = (amax / vmax).astype(np.float32)
+        if pow2:
+            s = np.where(s > 0, _pow2_at_least(np.where(s > 0, s, 1.0)), np.float32(0)).astype(np.float32)
+        r = (g / s[:, :, None]).astype(np.float32)
+    r = np.where(s[:, :, None] == 0, np.float32(0), r)
+    idx = _nearest_index(np.abs(r), levels)
+    codes = np.where((idx > 0) & (r < 0), idx | 32, idx).astype(np.uint8)
+    return codes.reshape(n, k), s
+
+
+def tile_group_scales(scales) -> np.ndarray:
+    """n x G group scales -> R24's tiled order: 32 per (column block, group),
+    column 32 b + j at position j, blocks padded with zeros (flat floats)."""
+    sc = np.asarray(scales, dtype=np.float32)
+    n, g = sc.shape
+    nb = -(-n // 32)
+    ss = np.zeros((nb * 32, g), dtype=np.float32)
+    ss[:n] = sc
+    return ss.reshape(nb, 32, g).transpose(0, 2, 1).reshape(-1).copy()
+
+
+def untile_group_scales(tscales, n: int, k: int) -> np.ndarray:
+    """Inverse of tile_group_scales (padding dropped)."""
+    g = k // GROUP
+    nb = -(-n // 32)
+    s = np.asarray(tscales, dtype=np.float32).reshape(nb, g, 32).transpose(0, 2, 1)
+    return s.reshape(nb * 32, g)[:n].copy()
+
+
+def w6a8_ref(xcodes, xscales, wcodes, wscales, wfmt: str) -> np.ndarray:
+    """R28 in float64: s_x[m] * sum_g s_w[n, g] (Q_x,g @ V_w,g^T)."""
+    qx = e4m3_decode(xcodes)
+    vw = fp6_decode(wcodes, wfmt)
     m, k = qx.shape
     y = np.zeros((m, vw.shape[0]), dtype=np.float64)
     sw = np.asarray(wscales, dtype=np.float64)

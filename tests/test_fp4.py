@@ -249,3 +249,90 @@ def test_w4a6_reference_against_loops():
             for j in range(n):
                 acc = sum(float(sw[j, kk // 128]) * qx[i, kk] * vw[j, kk] for kk in range(k))
                 assert abs(y[i, j] - float(sx[i]) * acc) <= 1e-9 * max(1.0, abs(y[i, j]))
+
+
+# ------------------------------------------------------------------ FP6 weights (R27, R28)
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+def test_fp6_group_quantizer(fmt):
+    lv = F.fp6_values(fmt)
+    rng = np.random.default_rng(11)
+    w = (rng.standard_t(4, size=(8, 512)) * 0.02).astype(np.float32)
+    w[0, :128] = 0.0                                          # a zero group
+    codes, s = F.quantize_fp6_groups(w, fmt)
+    assert s[0, 0] == 0.0 and np.all(codes[0, :128] == 0)
+    for r in range(8):
+        for g in range(4):
+            sl = slice(128 * g, 128 * g + 128)
+            if s[r, g] == 0:
+                continue
+            assert codes[r, sl][np.argmax(np.abs(w[r, sl]))] & 31 == 31   # the group's amax takes the top code
+            q = (w[r, sl] / s[r, g]).astype(np.float32)
+            assert np.array_equal(codes[r, sl] & 31, _brute_nearest(np.minimum(np.abs(q), lv[-1]), lv))
+    assert np.all(((codes & 32) != 0) <= (w < 0))
+    assert codes.max() < 64
+
+
+def test_fp6_group_quantizer_worked_examples():
+    """Groups whose scale is a power of two, so every quotient is exact and the
+    codes can be read off the level tables by hand (ties to the even code)."""
+    # E2M3: amax 0.9375 -> s = 0.125; r = 7.5, -3.75, 0.9375 (tie 0.875 | 1.0),
+    # 0.0625 (tie 0 | 0.125), -0.1875 (tie 0.125 | 0.25)
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, :5] = [0.9375, -0.46875, 0.1171875, 0.0078125, -0.0234375]
+    c, s = F.quantize_fp6_groups(w, "e2m3")
+    assert s[0, 0] == np.float32(0.125)
+    assert list(c[0, :5]) == [31, 32 | 23, 8, 0, 32 | 2]
+    # E3M2: amax 0.875 -> s = 0.03125; r = 28, 18 (tie 16 | 20), 1.125 (tie 1 | 1.25), -0.09375 (tie .0625 | .125)
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, :4] = [0.875, 0.5625, 0.03515625, -0.0029296875]
+    c, s = F.quantize_fp6_groups(w, "e3m2")
+    assert s[0, 0] == np.float32(0.03125)
+    assert list(c[0, :4]) == [31, 28, 12, 32 | 2]
+
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+def test_fp6_group_power_of_two_scales(fmt):
+    lv = F.fp6_values(fmt)
+    rng = np.random.default_rng(12)
+    w = rng.normal(0, 0.02, size=(6, 384)).astype(np.float32)
+    w[1, :128] = 0.0
+    codes, s = F.quantize_fp6_groups(w, fmt, pow2=True)
+    _, s_plain = F.quantize_fp6_groups(w, fmt)
+    nz = s > 0
+    m, _ = np.frexp(s[nz].astype(np.float64))
+    assert np.all(m == 0.5) and np.all(s[nz] >= s_plain[nz]) and np.all(s[nz] < 2 * s_plain[nz])
+    assert s[1, 0] == 0 and np.all(codes[1, :128] == 0)
+    q = (w.reshape(6, 3, 128) / np.where(s > 0, s, 1)[:, :, None]).astype(np.float32).reshape(6, 384)
+    assert np.all(np.abs(q) <= lv[-1])                         # nothing saturates
+    want = _brute_nearest(np.abs(q.reshape(-1)), lv).reshape(6, 384)
+    live = np.repeat(s, 128, axis=1) > 0
+    assert np.array_equal(np.where(live, codes & 31, 0), np.where(live, want, 0))
+
+
+def test_tiled_group_scales_by_hand():
+    n, k = 40, 256                                             # two column blocks (second padded), G = 2
+    scales = np.arange(1, n * 2 + 1, dtype=np.float32).reshape(n, 2)
+    ts = F.tile_group_scales(scales)
+    assert ts.shape == (2 * 2 * 32,)
+    assert ts[(1 * 2 + 1) * 32 + 1] == scales[33, 1]           # block 1, group 1, column 33
+    assert ts[0 * 32 + 31] == scales[31, 0] and ts[(0 * 2 + 1) * 32 + 0] == scales[0, 1]
+    assert ts[(1 * 2 + 0) * 32 + 13] == 0                       # column 45: padding
+    assert np.array_equal(F.untile_group_scales(ts, n, k), scales)
+    assert np.count_nonzero(ts) == scales.size
+
+
+def test_w6a8_reference_against_loops():
+    rng = np.random.default_rng(13)
+    m, n, k = 3, 4, 256
+    xc = rng.integers(0, 255, size=(m, k)).astype(np.uint8)
+    xc[(xc & 0x7F) == 0x7F] = 0x38                             # no NaN codes
+    wc = rng.integers(0, 64, size=(n, k)).astype(np.uint8)
+    sx = rng.uniform(0.01, 2, m).astype(np.float32)
+    sw = rng.uniform(0.01, 2, (n, 2)).astype(np.float32)
+    for wfmt in F.FP6_FORMATS:
+        y = F.w6a8_ref(xc, sx, wc, sw, wfmt)
+        qx, vw = F.e4m3_decode(xc), F.fp6_decode(wc, wfmt)
+        for i in range(m):
+            for j in range(n):
+                acc = sum(float(sw[j, kk // 128]) * qx[i, kk] * vw[j, kk] for kk in range(k))
+                assert abs(y[i, j] - float(sx[i]) * acc) <= 1e-9 * max(1.0, abs(y[i, j]))
