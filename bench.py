@@ -549,6 +549,10 @@ def w4a8_suite(args):
         ms_a6[f6] = (burst(lambda: api.w4a6_gemm(x6, s6, f6, qt, out=y), args.steps),
                      burst(lambda: api.w4a6_gemm(x6, s6, f6, qtp, out=y), args.steps))
     ms_q6 = burst(lambda: api.fp6_quantize_rows(x, "e2m3"), args.steps)
+    # W6A8: FP6 weights (tiled 6-bit storage) x E4M3 activations
+    q6w = {f6: (api.fp6_quantize_pack(w, f6), api.fp6_quantize_pack(w, f6, pow2=True)) for f6 in ("e2m3", "e3m2")}
+    ms_w6 = {f6: (burst(lambda: api.w6a8_gemm(xq, xs, q6w[f6][0], out=y), args.steps),
+                  burst(lambda: api.w6a8_gemm(xq, xs, q6w[f6][1], out=y), args.steps)) for f6 in ("e2m3", "e3m2")}
     qi = api.quantize_pack(w, 4)
     ms_i = burst(lambda: api.dequant_gemm(x, qi, out=y), args.steps)
     del xcs, xqs, xss
@@ -565,6 +569,7 @@ def w4a8_suite(args):
     for f6 in ("e2m3", "e3m2"):
         x6, s6 = api.fp6_quantize_rows(xr, f6)
         e_a6[f6] = rel(api.w4a6_gemm(x6, s6, f6, qt, torch.float32))
+    e_w6 = {f6: rel(api.w6a8_gemm(xq[:1024], xs[:1024], q6w[f6][0], torch.float32)) for f6 in ("e2m3", "e3m2")}
     e_int4 = rel(api.dequant_gemm(xr, qi, torch.float32))
     flops = 2.0 * m * n * k
     print(json.dumps({
@@ -581,9 +586,14 @@ def w4a8_suite(args):
         "w4a6_e2m3_pow2_us": round(ms_a6["e2m3"][1] * 1e3, 2),
         "w4a6_e2m3_pow2_TFLOPs": round(flops / ms_a6["e2m3"][1] / 1e9, 1),
         "w4a6_e3m2_us": round(ms_a6["e3m2"][0] * 1e3, 2), "w4a6_e3m2_pow2_us": round(ms_a6["e3m2"][1] * 1e3, 2),
+        "w6a8_e2m3_us": round(ms_w6["e2m3"][0] * 1e3, 2), "w6a8_e2m3_TFLOPs": round(flops / ms_w6["e2m3"][0] / 1e9, 1),
+        "w6a8_e2m3_frac_of_fp8_peak": round(flops / ms_w6["e2m3"][0] / 1e9 / 5000.0, 4),
+        "w6a8_e2m3_pow2_us": round(ms_w6["e2m3"][1] * 1e3, 2),
+        "w6a8_e3m2_us": round(ms_w6["e3m2"][0] * 1e3, 2), "w6a8_e3m2_pow2_us": round(ms_w6["e3m2"][1] * 1e3, 2),
         "int4_bf16_gemm_us": round(ms_i * 1e3, 2), "int4_bf16_TFLOPs": round(flops / ms_i / 1e9, 1),
         "w4a8_rel_err_vs_f32": round(e_w4a8, 5), "w4a8_pow2_rel_err_vs_f32": round(e_pow2, 5),
         "w4a6_e2m3_rel_err_vs_f32": round(e_a6["e2m3"], 5), "w4a6_e3m2_rel_err_vs_f32": round(e_a6["e3m2"], 5),
+        "w6a8_e2m3_rel_err_vs_f32": round(e_w6["e2m3"], 5), "w6a8_e3m2_rel_err_vs_f32": round(e_w6["e3m2"], 5),
         "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
     }), flush=True)
 

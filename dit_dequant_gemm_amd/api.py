@@ -60,6 +60,8 @@ SIGNATURES = {
     "ddg_w4a8_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
     "ddg_fp6_quantize_rows": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
     "ddg_w4a6_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_int, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
+    "ddg_fp6_quantize_pack": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
+    "ddg_w6a8_gemm": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp]),
 }
 
 FP4_FORMATS = {"e2m1": 0, "e3m0": 1, "e1m2": 2}
@@ -561,4 +563,60 @@ def w4a6_gemm(xq: torch.Tensor, xs: torch.Tensor, fmt: str, qw: QWeightFP4, out_
                                         FP6_FORMATS[fmt], qw.packed.data_ptr(), qw.scales.data_ptr(), qw.fmt_code,
                                         qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
                                         _stream_ptr(xq.device)), "ddg_w4a6_gemm")
+    return y
+
+
+class QWeightFP6:
+    """A weight in a 6-bit floating-point format (fmt "e2m3" or "e3m2") per
+    group of 128: packed, the tiled 6-bit storage with the weight's rows in
+    place of tokens (flat, ceil(n/32) * k/128 * 3072 bytes); scales, tiled 32
+    per (column block, group) (flat, ceil(n/32) * k/128 * 32 floats); pow2:
+    the scales are powers of two, applied by the matrix instructions."""
+
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, fmt: str, n: int, k: int,
+                 pow2: bool = False):
+        self.packed, self.scales, self.fmt, self.n, self.k, self.pow2 = packed, scales, fmt, n, k, pow2
+
+    @property
+    def fmt_code(self) -> int:
+        return FP6_FORMATS[self.fmt] | (FP4_POW2 if self.pow2 else 0)
+
+
+def fp6_quantize_pack(w: torch.Tensor, fmt: str = "e2m3", pow2: bool = False) -> QWeightFP6:
+    """Per-group(128) 6-bit float quantization of an (out x in) GPU weight
+    into the tiled 6-bit storage; pow2 rounds each group scale up to a power
+    of two."""
+    _require_cuda(w, "w")
+    if fmt not in FP6_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP6_FORMATS)}")
+    if w.dim() != 2 or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be a 2-D bf16 or float32 tensor")
+    w = w.contiguous()
+    n, k = w.shape
+    g, nb = max(k // GROUP, 0), -(-n // 32)
+    packed = torch.empty((nb * g * 3072,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((nb * g * 32,), dtype=torch.float32, device=w.device)
+    q = QWeightFP6(packed, scales, fmt, n, k, pow2)
+    _check(load_library().ddg_fp6_quantize_pack(w.data_ptr(), DDG_F32 if w.dtype == torch.float32 else DDG_BF16,
+                                                n, k, q.fmt_code, packed.data_ptr(), scales.data_ptr(),
+                                                _stream_ptr(w.device)), "ddg_fp6_quantize_pack")
+    return q
+
+
+def w6a8_gemm(xq: torch.Tensor, xs: torch.Tensor, qw: QWeightFP6, out_dtype=torch.bfloat16,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = s_x[m] * sum_g s_w[n, g] (X_q W_q^T)_g on the FP8 x FP6 matrix cores
+    (X from fp8_quantize_rows, W from fp6_quantize_pack)."""
+    for t, name in ((xq, "xq"), (xs, "xs")):
+        _require_cuda(t, name)
+    if xq.dtype != torch.uint8 or xq.dim() != 2 or xq.shape[1] != qw.k or xs.shape != (xq.shape[0],):
+        raise ValueError("xq must be m x k uint8 codes with m float32 scales")
+    m = xq.shape[0]
+    y = out if out is not None else torch.empty((m, qw.n), dtype=out_dtype, device=xq.device)
+    if y.shape != (m, qw.n) or y.dtype not in (torch.bfloat16, torch.float32) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous m x n bf16 or float32 tensor")
+    _check(load_library().ddg_w6a8_gemm(xq.contiguous().data_ptr(), xs.contiguous().data_ptr(), m, qw.k,
+                                        qw.packed.data_ptr(), qw.scales.data_ptr(), qw.fmt_code,
+                                        qw.n, y.data_ptr(), DDG_F32 if y.dtype == torch.float32 else DDG_BF16,
+                                        _stream_ptr(xq.device)), "ddg_w6a8_gemm")
     return y

@@ -693,6 +693,47 @@ int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
   return hip_status(ddg::launch_w4a6_gemm(a, fmt6, (fmt & DDG_FP4_POW2) != 0, stream));
 }
 
+int ddg_fp6_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt6, uint8_t* packed,
+                          float* scales, hipStream_t stream) {
+  const int f = fmt6 & ~DDG_FP4_POW2;
+  if ((f != DDG_FP6_E2M3 && f != DDG_FP6_E3M2) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
+    return DDG_ERR_ARG;
+  if (n < 0 || n > kMaxDim || !k_ok(k) || !mul_ok(n + 31, k) || !mul_ok((n + 31) * k, 4)) return DDG_ERR_SHAPE;
+  if (n == 0) return DDG_OK;
+  if (!w || !packed || !scales) return DDG_ERR_ARG;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(ddg::launch_fp6w_quantize_pack(w, w_dtype == DDG_F32, n, (int)k, f,
+                                                   (fmt6 & DDG_FP4_POW2) != 0, packed, scales, stream));
+}
+
+int ddg_w6a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, const uint8_t* packed,
+                  const float* wscales, int fmt6, int64_t n, void* y, int y_dtype, hipStream_t stream) {
+  const int f = fmt6 & ~DDG_FP4_POW2;
+  if ((f != DDG_FP6_E2M3 && f != DDG_FP6_E3M2) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))
+    return DDG_ERR_ARG;
+  if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || !mul_ok(m, n) ||
+      !mul_ok(m * n, 4) || !mul_ok(n + 31, k))
+    return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!xq || !xscales || !packed || !wscales || !y) return DDG_ERR_ARG;
+  if (!aligned(xq, 16) || !aligned(packed, 16) || !aligned(xscales, 4) || !aligned(wscales, 4) ||
+      !aligned(y, y_dtype == DDG_F32 ? 4 : 2))
+    return DDG_ERR_ALIGN;
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  ddg::W4A8Args a{};
+  a.xq = xq;
+  a.xscales = xscales;
+  a.packed = packed;
+  a.wscales = wscales;
+  a.y = y;
+  a.m = (int)m; a.n = (int)n; a.k = (int)k;
+  a.out_bf16 = y_dtype == DDG_BF16;
+  return hip_status(ddg::launch_w6a8_gemm(a, f, (fmt6 & DDG_FP4_POW2) != 0, stream));
+}
+
 int ddg_w4a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, const uint8_t* packed,
                   const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
   if (!fp4_fmt_ok(fmt) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32))

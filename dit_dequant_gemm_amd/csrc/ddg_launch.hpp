@@ -86,6 +86,13 @@ constexpr int kFp6E2M3 = 0, kFp6E3M2 = 1;
 hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt6, uint8_t* q, float* sx,
                                     hipStream_t stream);
 hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream);
+// FP6 weights (kFp6E2M3, kFp6E3M2) per group of 128 in the tiled 6-bit
+// storage (weight rows in place of tokens) with tiled scales, and their
+// product with E4M3 activations (xq, xscales of W4A8Args)
+constexpr int kFp6wE2M3 = 3, kFp6wE3M2 = 4;   // weight formats of the product kernel
+hipError_t launch_fp6w_quantize_pack(const void* w, bool f32_in, int64_t n, int k, int fmt6, bool pow2,
+                                     uint8_t* packed, float* scales, hipStream_t stream);
+hipError_t launch_w6a8_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream);
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);

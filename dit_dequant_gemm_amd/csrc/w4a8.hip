@@ -307,6 +307,17 @@ constexpr int kX6Record = 3072;
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x6v __attribute__((ext_vector_type(6)));
 
+// Keeps both sources of a packed FP6 conversion live past its result w.  The
+// compiler may otherwise give the conversion's six result registers to a
+// source that ends there, and the instruction writes its first result dwords
+// before it has read all of its first source: with the result in registers
+// 4..9 of the first source, code 8 came out wrong.  Sources still live where
+// the result is defined cannot share registers with it (the empty asm takes
+// the result too, so it stays after the conversion).
+__device__ __forceinline__ void fp6_keep_sources(u32x6v& w, const f32x16v& ev, const f32x16v& od) {
+  asm volatile("" : "+v"(w) : "v"(ev), "v"(od));
+}
+
 // The three 8-byte pieces of one 32-value unit (bf16 values in t) at rec.
 // r = x / s (correctly rounded) goes through the packed FP6 conversion
 // instruction (unit scale; round to nearest even, saturating at the largest
@@ -334,6 +345,7 @@ __device__ __forceinline__ void fp6_unit(const u32x4 (&t)[4], bool zero, bool fa
     w = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f));
   else
     w = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f));
+  fp6_keep_sources(w, ev, od);
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
     const u32x2 piece = {w[2 * u], w[2 * u + 1]};
@@ -405,6 +417,84 @@ __global__ __launch_bounds__(1024) void fp6_quantize_rows_kernel(const uint16_t*
   }
 }
 
+// FP6 weights: one lane per 32-weight chunk (the 4 lanes of a 128-group are
+// adjacent: the group abs-max is a 2-step butterfly inside the quad), scale
+// fl32(amax / vmax) (the smallest power of two at least that with POW2),
+// r = w / s correctly rounded, codes by the packed FP6 conversion (as
+// fp6_unit).  Chunk j of a row's group g is its unit (step j / 2, half
+// j % 2); it goes to record (row / 32, g) of the tiled 6-bit storage with
+// the weight rows in place of tokens; the scales go 32 per (row block,
+// group), row 32 b + r at position r.  Chunks n_in .. n_out - 1 (padding
+// rows) read no input and write zero codes and scales.
+template <int EB, int MB, int BIAS, bool F32_IN, bool POW2>
+__global__ __launch_bounds__(256) void fp6w_quantize_pack_kernel(const void* __restrict__ w, int64_t n_in,
+                                                                int64_t n_out, int cpr, uint8_t* __restrict__ q,
+                                                                float* __restrict__ scales) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = c < n_out;
+  const bool has_src = c < n_in;
+  const int64_t cc = has_src ? c : 0;
+  float v[32];
+  if (!has_src) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  } else if constexpr (F32_IN) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(w) + cc * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 t = src[i];
+      v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+    }
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + cc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 t = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_bits_to_f32(t[j] & 0xFFFFu);
+        v[8 * i + 2 * j + 1] = bf16_bits_to_f32(t[j] >> 16);
+      }
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+  a = __builtin_fmaxf(a, __shfl_xor(a, 1));
+  a = __builtin_fmaxf(a, __shfl_xor(a, 2));
+  float s = a / Fp6Fmt<EB, MB, BIAS>::vmax;
+  if constexpr (POW2) s = pow2_at_least(s);
+  const bool zero = !(s != 0.0f);
+  f32x16v ev, od;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float r = zero ? 0.0f : v[j] / s;
+    const float rv = __builtin_fabsf(r) <= Fp6Fmt<EB, MB, BIAS>::zero_below ? 0.0f : r;
+    if (j & 1) od[j >> 1] = rv; else ev[j >> 1] = rv;
+  }
+  u32x6v wd;
+  if constexpr (EB == 2)
+    wd = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f));
+  else
+    wd = __builtin_bit_cast(u32x6v, __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f));
+  fp6_keep_sources(wd, ev, od);
+  if (valid) {
+    const int64_t row = c / cpr;
+    const int j = (int)(c - row * cpr);
+    const int64_t G = cpr / 4, g = j >> 2;
+    const int un = j & 3;
+    const int64_t blk = (row >> 5) * G + g;
+    const int lr = (int)(row & 31);
+    uint8_t* rec = q + blk * kX6Record + lr * 8;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const u32x2 piece = {wd[2 * u], wd[2 * u + 1]};
+      *reinterpret_cast<u32x2*>(rec + (un * 3 + u) * 256) = piece;
+    }
+    if (un == 0) scales[blk * 32 + lr] = zero ? 0.0f : s;
+  }
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16e __attribute__((ext_vector_type(16)));
 
@@ -443,6 +533,13 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   constexpr int TN = 32 * CB * (8 / WM);
   constexpr bool kA6 = AF != 0;
   static_assert(!kA6 || (FMT == kFp4E2M1 && TILED), "6-bit activations pair with tiled E2M1 weights");
+  // FP6 weights (tiled 6-bit storage, a record of 3 KB per column block and
+  // group) run as the B operand against E4M3 activations
+  constexpr bool kW6 = FMT == kFp6wE2M3 || FMT == kFp6wE3M2;
+  static_assert(!kW6 || (TILED && AF == 0), "FP6 weights: tiled storage, E4M3 activations");
+  constexpr uint32_t kWRec = kW6 ? (uint32_t)kX6Record : 2048u;   // weight bytes per (block, group)
+  constexpr int kWPieces = (int)kWRec / 1024;
+  using BReg = std::conditional_t<kW6, u32x6v, u32x4>;
   constexpr int kStage = kA6 ? 8 * kX6Record : kW8Stage;
   constexpr int kXDma = kA6 ? 3 : 4;                     // X DMAs per wave and group
   // Several waves along M share each weight column: then the tile's weight
@@ -450,8 +547,8 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   // ahead and once per workgroup, and every wave reads its B operands there.
   constexpr bool kBLds = TILED && WM > 1;
   constexpr int kNBlk = (8 / WM) * CB;                   // 32-column blocks per tile
-  constexpr int kBStage = kBLds ? kNBlk * 2048 : 0;
-  constexpr int kBDma = kBLds ? (2 * kNBlk + 7) / 8 : 0; // per wave; the surplus repeats the first records
+  constexpr int kBStage = kBLds ? kNBlk * (int)kWRec : 0;
+  constexpr int kBDma = kBLds ? (kWPieces * kNBlk + 7) / 8 : 0;  // per wave; the surplus repeats the first pieces
   // one array per stage, every stage index a compile-time constant: the
   // compiler can then tell the stage being read from the one being filled
   // and keeps the fill in flight across the barrier
@@ -481,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   // weights and scales of this tile's columns (tiled: its whole 32-column
   // blocks, 2048 bytes and 32 scales per block and group)
   const int nblk = (n_valid + 31) / 32;
-  const rsrc_t rw = TILED ? make_rsrc(args.packed + (int64_t)(n0 / 32) * G * 2048, (uint32_t)(nblk * G) * 2048u)
+  const rsrc_t rw = TILED ? make_rsrc(args.packed + (int64_t)(n0 / 32) * G * kWRec, (uint32_t)(nblk * G) * kWRec)
                           : make_rsrc(args.packed + (int64_t)n0 * wrow, (uint32_t)n_valid * wrow);
   const rsrc_t rs = TILED ? make_rsrc(args.wscales + (int64_t)(n0 / 32) * G * 32, (uint32_t)(nblk * G) * 128u)
                           : make_rsrc(args.wscales + (int64_t)n0 * G, (uint32_t)n_valid * G * 4);
@@ -525,13 +622,18 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   //    so B is FP8 (converted in registers through a byte lookup), which
   //    pairs like A: lane half h holds k 32 h .. 32 h + 31; A takes chunks
   //    2h and 2h + 1.
-  constexpr bool kNative = FMT == kFp4E2M1;
+  //  * FP6 weights run as FP6 B operands: lane half h of step ks reads the
+  //    three 8-byte pieces of its column's unit (ks, h) in the record (codes
+  //    32 h .. 32 h + 31 of the step).  FP6 and FP4 operands share one lane
+  //    layout (the W4A6 pairing), so A takes chunks h, h + 2 as for E2M1.
+  constexpr bool kNative = FMT == kFp4E2M1 || kW6;
   uint32_t woff[CB], soff[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     if constexpr (TILED) {
       const uint32_t blk = (uint32_t)(wn * CB + cb);
-      woff[cb] = blk * (uint32_t)G * 2048u + 512u * (uint32_t)lh + 16u * (uint32_t)lr;
+      woff[cb] = blk * (uint32_t)G * kWRec +
+                 (kW6 ? 768u * (uint32_t)lh + 8u * (uint32_t)lr : 512u * (uint32_t)lh + 16u * (uint32_t)lr);
       soff[cb] = blk * (uint32_t)G * 128u + 4u * (uint32_t)lr;
     } else {
       const uint32_t ncol = (uint32_t)(wn * 32 * CB + cb * 32 + lr);
@@ -539,32 +641,45 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
       soff[cb] = ncol * (uint32_t)G * 4;
     }
   }
-  constexpr uint32_t kStepOff = TILED ? 1024u : 32u;           // ks = 1
-  constexpr uint32_t kGroupW = TILED ? 2048u : 64u, kGroupS = TILED ? 128u : 4u;
-  auto load_w = [&](int g, u32x4 (&b)[CB][2], float (&sc)[CB]) __attribute__((always_inline)) {
+  constexpr uint32_t kStepOff = TILED ? (kW6 ? 1536u : 1024u) : 32u;   // ks = 1
+  constexpr uint32_t kGroupW = TILED ? kWRec : 64u, kGroupS = TILED ? 128u : 4u;
+  auto load_w = [&](int g, BReg (&b)[CB][2], float (&sc)[CB]) __attribute__((always_inline)) {
     if constexpr (!kBLds) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          b[cb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rw, woff[cb] + kStepOff * ks, (uint32_t)g * kGroupW, 0));
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (kW6) {
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+              const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                            rw, woff[cb] + kStepOff * ks + 256u * u,
+                                                            (uint32_t)g * kGroupW, 0));
+              b[cb][ks][2 * u] = t[0];
+              b[cb][ks][2 * u + 1] = t[1];
+            }
+          } else {
+            b[cb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rw, woff[cb] + kStepOff * ks, (uint32_t)g * kGroupW, 0));
+          }
+        }
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       sc[cb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff[cb], (uint32_t)g * kGroupS, 0));
   };
   // the tile's weight records of group g -> LDS after the X stage: DMA d
-  // (0 .. 2 kNBlk - 1) copies half d % 2 of block d / 2
+  // (0 .. kWPieces kNBlk - 1) copies 1 KB piece d % kWPieces of block
+  // d / kWPieces
   auto issue_b = [&](int g, uint8_t* stage) __attribute__((always_inline)) {
     if constexpr (kBLds) {
 #pragma unroll
       for (int i = 0; i < kBDma; ++i) {
-        const int d = (kBDma * wave + i) % (2 * kNBlk);
+        const int d = (kBDma * wave + i) % (kWPieces * kNBlk);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rw, (lds_ptr_t)(stage + d * 1024), 16,
-            (uint32_t)(d >> 1) * (uint32_t)G * 2048u + (uint32_t)(d & 1) * 1024u + (uint32_t)lane * 16u,
-            (uint32_t)g * 2048u, 0, 0);
+            (uint32_t)(d / kWPieces) * (uint32_t)G * kWRec + (uint32_t)(d % kWPieces) * 1024u + (uint32_t)lane * 16u,
+            (uint32_t)g * kWRec, 0, 0);
       }
     }
   };
@@ -602,7 +717,7 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
 
-  u32x4 bc[CB][2], bn[CB][2];
+  BReg bc[CB][2], bn[CB][2];
   float sc[CB], sn[CB];
   // Group g: fetch group g + 1's weights into (bn, sn) and group g + 2's X
   // into the stage read in g - 1 (fill), multiply stage st with (bc, sc).
@@ -619,12 +734,26 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4 braw;
-        if constexpr (kBLds)
+        BReg braw;
+        if constexpr (kBLds && kW6) {
+          const uint8_t* p = stb + (wn * CB + cb) * (int)kWRec + ks * 1536 + lh * 768 + lr * 8;
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            const u32x2 t = *reinterpret_cast<const u32x2*>(p + 256 * u);
+            braw[2 * u] = t[0];
+            braw[2 * u + 1] = t[1];
+          }
+        } else if constexpr (kBLds) {
           braw = *reinterpret_cast<const u32x4*>(stb + (wn * CB + cb) * 2048 + ks * 1024 + lh * 512 + lr * 16);
-        else
+        } else {
           braw = bc[cb][ks];
-        if constexpr (kNative) {
+        }
+        if constexpr (kW6) {
+#pragma unroll
+          for (int j = 0; j < 6; ++j) bop[cb][ks][j] = (int)braw[j];
+          bop[cb][ks][6] = 0;
+          bop[cb][ks][7] = 0;
+        } else if constexpr (kNative) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             bop[cb][ks][j] = (int)braw[j];
@@ -642,7 +771,8 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
     int sb[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) sb[cb] = (int)((__builtin_bit_cast(uint32_t, sc[cb]) >> 23) & 0xFFu);
-    constexpr int kBFmt = kNative ? 4 : 0;                // B as FP4 (E2M1) or FP8 (E4M3)
+    // B as FP6 (E2M3 2, E3M2 3), FP4 (E2M1) or FP8 (E4M3)
+    constexpr int kBFmt = kW6 ? (FMT == kFp6wE2M3 ? 2 : 3) : (kNative ? 4 : 0);
     // with power-of-two scales row block rb's A reads are issued one row
     // block earlier; with float32 scales (16 more registers live for the
     // rescale) at the top of the row block, behind the previous MFMAs
@@ -851,6 +981,43 @@ hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t 
   if (fmt6 == kFp6E3M2)
     return pow2 ? launch_w4a8_cfg<kFp4E2M1, true, true, 4, 3, 3>(a, stream)
                 : launch_w4a8_cfg<kFp4E2M1, false, true, 4, 3, 3>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+template <int EB, int MB, int BIAS>
+hipError_t launch_fp6w_quant(const void* w, bool f32_in, bool pow2, int64_t n, int k, uint8_t* packed,
+                             float* scales, hipStream_t stream) {
+  const int cpr = k / 32;
+  const int64_t n_in = n * cpr, n_out = (n + 31) / 32 * 32 * cpr;
+  const dim3 grid((unsigned)((n_out + 255) / 256)), block(256);
+  if (f32_in) {
+    if (pow2) fp6w_quantize_pack_kernel<EB, MB, BIAS, true, true><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
+    else fp6w_quantize_pack_kernel<EB, MB, BIAS, true, false><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
+  } else {
+    if (pow2) fp6w_quantize_pack_kernel<EB, MB, BIAS, false, true><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
+    else fp6w_quantize_pack_kernel<EB, MB, BIAS, false, false><<<grid, block, 0, stream>>>(w, n_in, n_out, cpr, packed, scales);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fp6w_quantize_pack(const void* w, bool f32_in, int64_t n, int k, int fmt6, bool pow2,
+                                     uint8_t* packed, float* scales, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (fmt6 == kFp6E2M3) return launch_fp6w_quant<2, 3, 1>(w, f32_in, pow2, n, k, packed, scales, stream);
+  if (fmt6 == kFp6E3M2) return launch_fp6w_quant<3, 2, 3>(w, f32_in, pow2, n, k, packed, scales, stream);
+  return hipErrorInvalidValue;
+}
+
+// FP6 weights take the tiled E2M1 tile shape (256 x 192, weights through LDS).
+hipError_t launch_w6a8_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream) {
+  if (fmt6 == kFp6E2M3)
+    return pow2 ? launch_w4a8_cfg<kFp6wE2M3, true, true, 4, 3>(a, stream)
+                : launch_w4a8_cfg<kFp6wE2M3, false, true, 4, 3>(a, stream);
+  if (fmt6 == kFp6E3M2)
+    return pow2 ? launch_w4a8_cfg<kFp6wE3M2, true, true, 4, 3>(a, stream)
+                : launch_w4a8_cfg<kFp6wE3M2, false, true, 4, 3>(a, stream);
   return hipErrorInvalidValue;
 }
 

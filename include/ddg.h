@@ -443,6 +443,45 @@ int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
                   const uint8_t* packed, const float* wscales, int fmt, int64_t n, void* y,
                   int y_dtype, hipStream_t stream);
 
+/*
+ * FP6 weights (W6A8).  The FP4DiT article quantizes weights to 4 bits and
+ * names FP6 for activations (§3.2.3, §4.1 W4A6), arguing that FP6 saves
+ * memory over FP8 (§3.3); this library also offers the two FP6 formats for
+ * weights, multiplied with the E4M3 activations of ddg_fp8_quantize_rows on
+ * the FP8 x FP6 matrix instructions.
+ *
+ * Quantizer: per group of 128 weights along K, as ddg_fp4_quantize_pack
+ * with the FP6 levels: s = fl32(amax / vmax) (vmax 7.5 or 28; with
+ * DDG_FP4_POW2 OR-ed into fmt6 the smallest power of two at least that, and
+ * at least 2^-126), r = fl32(w / s) correctly rounded, code = the level
+ * nearest |r| (ties to the even code), sign in bit 5; an all-zero group gets
+ * s = 0 and codes 0.  packed: the tiled 6-bit storage of
+ * ddg_fp6_quantize_rows with the weight's rows (output channels) in place of
+ * tokens, ceil(n/32) * (k/128) * 3072 bytes; scales: the tiled order of
+ * DDG_FP4_TILED, ceil(n/32) * (k/128) * 32 floats (padding rows: zero codes
+ * and scales).
+ *   w       device, n x k bf16 or float32 (w_dtype), finite, 16-byte aligned.
+ *   packed  device, 16-byte aligned.   scales  device, 4-byte aligned.
+ * n == 0 is a no-op.  Errors: DDG_ERR_ARG (fmt6, dtype, null), DDG_ERR_SHAPE
+ * (k not a positive multiple of 128, n above 2^31 - 1), DDG_ERR_ALIGN,
+ * DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ */
+int ddg_fp6_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt6,
+                          uint8_t* packed, float* scales, hipStream_t stream);
+
+/*
+ * Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k] with q_x
+ * the E4M3 values of ddg_fp8_quantize_rows and v_w the FP6 weights of
+ * ddg_fp6_quantize_pack (fmt6, with DDG_FP4_POW2 exactly when the weights
+ * were quantized with it: the product then applies each scale's exponent
+ * field as the instruction's block scale); float32 accumulation, y (m x n)
+ * in bf16 (rounded once) or float32.  Other arguments and errors as
+ * ddg_w4a8_gemm.
+ */
+int ddg_w6a8_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
+                  const uint8_t* packed, const float* wscales, int fmt6, int64_t n, void* y,
+                  int y_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -296,6 +296,35 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     assert call(ws=FAKE + 2) == E_ALIGN and call(y=FAKE + 1) == E_ALIGN
     assert call(m=0, xq=None, xs=None, packed=None, ws=None, y=None) == OK
 
+    # FP6 weights: quantizer and W6A8 product
+    q6 = lib.ddg_fp6_quantize_pack
+    assert q6(FAKE, 0, 4, 128, 2, FAKE, FAKE, None) == E_ARG                # fp6 format
+    assert q6(FAKE, 0, 4, 128, 0x200, FAKE, FAKE, None) == E_ARG            # no tiled flag: always tiled
+    assert q6(FAKE, 2, 4, 128, 0, FAKE, FAKE, None) == E_ARG                # dtype
+    assert q6(FAKE, 0, 4, 100, 0, FAKE, FAKE, None) == E_SHAPE
+    assert q6(FAKE, 0, -1, 128, 1, FAKE, FAKE, None) == E_SHAPE
+    assert q6(FAKE, 0, 4, 128, 0x101, None, FAKE, None) == E_ARG
+    assert q6(MISALIGNED, 0, 4, 128, 0, FAKE, FAKE, None) == E_ALIGN
+    assert q6(FAKE, 1, 4, 128, 0, FAKE + 8, FAKE, None) == E_ALIGN
+    assert q6(None, 0, 0, 128, 0x100, None, None, None) == OK
+    g8 = lib.ddg_w6a8_gemm
+    base8 = [FAKE, FAKE, 4, 128, FAKE, FAKE, 0, 32, FAKE, 0, None]
+
+    def call8(**kw):
+        a = list(base8)
+        idx = {"xq": 0, "xs": 1, "m": 2, "k": 3, "packed": 4, "ws": 5, "f6": 6, "n": 7, "y": 8, "ydt": 9}
+        for key, v in kw.items():
+            a[idx[key]] = v
+        return g8(*a)
+
+    assert call8(f6=2) == E_ARG and call8(f6=0x200) == E_ARG and call8(ydt=3) == E_ARG
+    assert call8(k=130) == E_SHAPE and call8(k=2 ** 20 + 128) == E_SHAPE and call8(n=0) == E_SHAPE
+    assert call8(m=-1) == E_SHAPE
+    assert call8(xq=None) == E_ARG and call8(packed=None) == E_ARG and call8(y=None) == E_ARG
+    assert call8(xq=MISALIGNED) == E_ALIGN and call8(packed=FAKE + 8) == E_ALIGN and call8(y=FAKE + 1) == E_ALIGN
+    assert call8(m=0, xq=None, xs=None, packed=None, ws=None, y=None) == OK
+    assert call8(m=0, f6=0x101, xq=None) == OK
+
 
 def test_noalloc_lowrank_host_checks(lib):
     """The workspace-free low-rank product refuses, on the host and before

@@ -355,3 +355,89 @@ def test_rows_quantizers_extreme_scales(gpu_lib, fmt):
         cq, cs = F.quantize_rows_fp6(x, fmt)
         assert np.array_equal(host(xq), F.pack_fp6_tiled(cq))
     assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
+
+
+# ---- W6A8: FP6 weights ----
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+@pytest.mark.parametrize("n,k,f32,pow2", [(16, 128, False, False), (33, 384, True, True), (100, 5120, False, False),
+                                          (64, 256, True, False), (7, 1024, False, True), (300, 640, False, True)])
+def test_fp6_weight_quantize_bit_exact(gpu_lib, fmt, n, k, f32, pow2):
+    _case(f"fp6_quantize_pack {fmt} n={n} k={k} f32={f32} pow2={pow2}")
+    rng = np.random.default_rng(n * k + 5)
+    w = (rng.standard_t(4, size=(n, k)) * 0.02).astype(np.float32)
+    w[n // 2, :128] = 0.0                                      # a zero group
+    if not f32:
+        w = synth.to_bf16(w)
+    qw = gpu_lib.fp6_quantize_pack(dev_f32(w) if f32 else dev_bf16(w), fmt, pow2=pow2)
+    codes, s = F.quantize_fp6_groups(w, fmt, pow2=pow2)
+    # layout-free: back in row order, the codes and scales are the oracle's
+    assert np.array_equal(F.unpack_fp6_tiled(host(qw.packed), n, k), codes)
+    bs = F.untile_group_scales(host(qw.scales), n, k)
+    assert np.array_equal(bs.view(np.uint32), s.view(np.uint32))
+    # the stored bytes, padding rows included (zero codes and scales)
+    assert np.array_equal(host(qw.packed), F.pack_fp6_tiled(codes))
+    assert np.array_equal(host(qw.scales).view(np.uint32), F.tile_group_scales(s).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", list(F.FP6_FORMATS))
+def test_fp6_weight_quantize_ties_and_tiny_groups(gpu_lib, fmt):
+    """Hand-made groups with power-of-two scales whose quotients land on every
+    midpoint between levels (ties to the even code) and on the levels, a
+    group of subnormal weights and a zero group."""
+    _case(f"fp6_quantize_pack ties {fmt}")
+    lv = F.fp6_values(fmt).astype(np.float32)
+    mids = np.concatenate([(lv[1:] + lv[:-1]) / 2, lv, -(lv[1:] + lv[:-1]) / 2]).astype(np.float32)
+    w = np.zeros((4, 256), dtype=np.float32)
+    w[0, :mids.size] = mids * np.float32(0.125)                # group amax = top level -> s = 0.125
+    w[1, :128] = np.linspace(-1, 1, 128, dtype=np.float32) * np.float32(1e-39)
+    w[2, 128:] = rng_vals = np.random.default_rng(14).normal(0, 3, 128).astype(np.float32)
+    qw = gpu_lib.fp6_quantize_pack(dev_f32(w), fmt)
+    codes, s = F.quantize_fp6_groups(w, fmt)
+    assert s[0, 0] == np.float32(0.125) and s[3, 0] == 0 and s[3, 1] == 0 and rng_vals.size == 128
+    assert np.array_equal(F.unpack_fp6_tiled(host(qw.packed), 4, 256), codes)
+    assert np.array_equal(F.untile_group_scales(host(qw.scales), 4, 256).view(np.uint32), s.view(np.uint32))
+
+
+def _check_w6a8_f32(y, xc, xs, wc, ws, ref, wfmt):
+    absref = F.w6a8_ref(xc & 0x7F, xs, wc & 31, ws, wfmt)       # the same sum over magnitudes
+    assert np.all(np.abs(y - ref) <= 2.0 ** -14 * absref + 1e-37), \
+        float(np.max(np.abs(y - ref) / (absref + 1e-37)))
+    check_product(y, ref, False, f"w6a8 f32 {wfmt} k={xc.shape[1]}")
+
+
+@pytest.mark.parametrize("wfmt", list(F.FP6_FORMATS))
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (300, 272, 640), (513, 300, 2048), (64, 1000, 128),
+                                   (257, 33, 384)])
+def test_w6a8_gemm(gpu_lib, m, n, k, wfmt, pow2):
+    """The product on the oracle's FP6 weight codes (stored by the oracle) and
+    E4M3 activation codes."""
+    _case(f"w6a8_gemm {wfmt} pow2={pow2} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 13 + n + k)
+    w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
+    x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
+    wc, ws = F.quantize_fp6_groups(w, wfmt, pow2=pow2)
+    xc, xs = F.quantize_rows_e4m3(x)
+    qw = gpu_lib.QWeightFP6(_cuda_u8(F.pack_fp6_tiled(wc)), _cuda_f32(F.tile_group_scales(ws)), wfmt, n, k, pow2=pow2)
+    ref = F.w6a8_ref(xc, xs, wc, ws, wfmt)
+    y = host(gpu_lib.w6a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, torch.float32))
+    _check_w6a8_f32(y, xc, xs, wc, ws, ref, wfmt)
+    yb = host(gpu_lib.w6a8_gemm(_cuda_u8(xc), _cuda_f32(xs), qw, torch.bfloat16))
+    check_product(yb, ref, True, f"w6a8 bf16 {wfmt} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("wfmt", list(F.FP6_FORMATS))
+def test_w6a8_chain_attention_projection_sampled(gpu_lib, wfmt):
+    """GPU quantizers feeding the W6A8 product at 4096 x 3072 x 3072; m = 0 is a no-op."""
+    _case(f"w6a8 chain {wfmt} 4096 x 3072 x 3072 (sampled rows)")
+    c = synth.config2()
+    qw = gpu_lib.fp6_quantize_pack(dev_bf16(c["w"]), wfmt)
+    xq, xs = gpu_lib.fp8_quantize_rows(dev_bf16(c["x"]))
+    y = host(gpu_lib.w6a8_gemm(xq, xs, qw, torch.float32))
+    wc, ws = F.quantize_fp6_groups(c["w"], wfmt)
+    rows = np.r_[0:32, 2048:2080, 4064:4096]
+    xc, xsc = F.quantize_rows_e4m3(c["x"][rows])
+    _check_w6a8_f32(y[rows], xc, xsc, wc, ws, F.w6a8_ref(xc, xsc, wc, ws, wfmt), wfmt)
+    empty = gpu_lib.w6a8_gemm(xq[:0], xs[:0], qw, torch.float32)
+    assert empty.shape == (0, 3072)
