@@ -548,6 +548,11 @@ def w4a8_suite(args):
         x6, s6 = api.fp6_quantize_rows(x, f6)
         ms_a6[f6] = (burst(lambda: api.w4a6_gemm(x6, s6, f6, qt, out=y), args.steps),
                      burst(lambda: api.w4a6_gemm(x6, s6, f6, qtp, out=y), args.steps))
+    x6, s6 = api.fp6_quantize_rows(x, "e2m3")
+    # W4A6 with the lookup weight formats (FP8 B operands)
+    ms_a6_lut = {f: burst(lambda: api.w4a6_gemm(x6, s6, "e2m3", q, out=y), args.steps)
+                 for f, q in (("e3m0", api.fp4_quantize_pack(w, "e3m0", tiled=True)),
+                              ("e1m2", api.fp4_quantize_pack(w, "e1m2", tiled=True)))}
     ms_q6 = burst(lambda: api.fp6_quantize_rows(x, "e2m3"), args.steps)
     # W6A8: FP6 weights (tiled 6-bit storage) x E4M3 activations
     q6w = {f6: (api.fp6_quantize_pack(w, f6), api.fp6_quantize_pack(w, f6, pow2=True)) for f6 in ("e2m3", "e3m2")}
@@ -586,6 +591,7 @@ def w4a8_suite(args):
         "w4a6_e2m3_pow2_us": round(ms_a6["e2m3"][1] * 1e3, 2),
         "w4a6_e2m3_pow2_TFLOPs": round(flops / ms_a6["e2m3"][1] / 1e9, 1),
         "w4a6_e3m2_us": round(ms_a6["e3m2"][0] * 1e3, 2), "w4a6_e3m2_pow2_us": round(ms_a6["e3m2"][1] * 1e3, 2),
+        "w4a6_e3m0_weights_us": round(ms_a6_lut["e3m0"] * 1e3, 2), "w4a6_e1m2_weights_us": round(ms_a6_lut["e1m2"] * 1e3, 2),
         "w6a8_e2m3_us": round(ms_w6["e2m3"][0] * 1e3, 2), "w6a8_e2m3_TFLOPs": round(flops / ms_w6["e2m3"][0] / 1e9, 1),
         "w6a8_e2m3_frac_of_fp8_peak": round(flops / ms_w6["e2m3"][0] / 1e9 / 5000.0, 4),
         "w6a8_e2m3_pow2_us": round(ms_w6["e2m3"][1] * 1e3, 2),

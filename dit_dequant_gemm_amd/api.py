@@ -548,7 +548,7 @@ def fp6_quantize_rows(x: torch.Tensor, fmt: str = "e2m3"):
 def w4a6_gemm(xq: torch.Tensor, xs: torch.Tensor, fmt: str, qw: QWeightFP4, out_dtype=torch.bfloat16,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = s_x[m] * sum_g s_w[n, g] (X_q W_q^T)_g on the FP6 x FP4 matrix cores
-    (X from fp6_quantize_rows in format fmt; tiled E2M1 weights)."""
+    (X from fp6_quantize_rows in format fmt; tiled FP4 weights of any format)."""
     for t, name in ((xq, "xq"), (xs, "xs")):
         _require_cuda(t, name)
     if fmt not in FP6_FORMATS:

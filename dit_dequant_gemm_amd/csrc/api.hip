@@ -671,7 +671,7 @@ int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
                   const float* wscales, int fmt, int64_t n, void* y, int y_dtype, hipStream_t stream) {
   if (fmt6 != DDG_FP6_E2M3 && fmt6 != DDG_FP6_E3M2) return DDG_ERR_ARG;
   if (!fp4_fmt_ok(fmt) || (y_dtype != DDG_BF16 && y_dtype != DDG_F32)) return DDG_ERR_ARG;
-  if ((fmt & ~kFp4Flags) != DDG_FP4_E2M1 || !(fmt & DDG_FP4_TILED)) return DDG_ERR_ARG;   // tiled E2M1 only
+  if (!(fmt & DDG_FP4_TILED)) return DDG_ERR_ARG;                                       // tiled storage only
   if (m < 0 || m > kMaxDim || !k_ok(k) || k > kMaxK || n <= 0 || n > kMaxDim || !mul_ok(m, n) ||
       !mul_ok(m * n, 4) || !mul_ok(n, k))
     return DDG_ERR_SHAPE;
@@ -690,7 +690,7 @@ int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
   a.y = y;
   a.m = (int)m; a.n = (int)n; a.k = (int)k;
   a.out_bf16 = y_dtype == DDG_BF16;
-  return hip_status(ddg::launch_w4a6_gemm(a, fmt6, (fmt & DDG_FP4_POW2) != 0, stream));
+  return hip_status(ddg::launch_w4a6_gemm(a, fmt & ~kFp4Flags, fmt6, (fmt & DDG_FP4_POW2) != 0, stream));
 }
 
 int ddg_fp6_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt6, uint8_t* packed,

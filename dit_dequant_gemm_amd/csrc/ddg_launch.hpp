@@ -81,11 +81,12 @@ hipError_t launch_fp8_quantize_rows(const uint16_t* x, int64_t m, int k, uint8_t
                                     hipStream_t stream);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, int fmt, bool pow2, bool tiled, hipStream_t stream);
 // 6-bit activations (formats kFp6E2M3, kFp6E3M2) in the tiled 6-bit storage;
-// the product takes tiled E2M1 weights (xq of W4A8Args: the 6-bit storage)
+// the product takes tiled FP4 weights of format fmt (xq of W4A8Args: the
+// 6-bit storage)
 constexpr int kFp6E2M3 = 0, kFp6E3M2 = 1;
 hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt6, uint8_t* q, float* sx,
                                     hipStream_t stream);
-hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream);
+hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt, int fmt6, bool pow2, hipStream_t stream);
 // FP6 weights (kFp6E2M3, kFp6E3M2) per group of 128 in the tiled 6-bit
 // storage (weight rows in place of tokens) with tiled scales, and their
 // product with E4M3 activations (xq, xscales of W4A8Args)

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
   constexpr int RB = 8 / WM;
   constexpr int TN = 32 * CB * (8 / WM);
   constexpr bool kA6 = AF != 0;
-  static_assert(!kA6 || (FMT == kFp4E2M1 && TILED), "6-bit activations pair with tiled E2M1 weights");
+  static_assert(!kA6 || (FMT <= kFp4E1M2 && TILED), "6-bit activations pair with tiled FP4 weights");
   // FP6 weights (tiled 6-bit storage, a record of 3 KB per column block and
   // group) run as the B operand against E4M3 activations
   constexpr bool kW6 = FMT == kFp6wE2M3 || FMT == kFp6wE3M2;
@@ -743,6 +743,14 @@ __global__ __launch_bounds__(512, 1) void w4a8_gemm_kernel(W4A8Args args) {
             braw[2 * u] = t[0];
             braw[2 * u + 1] = t[1];
           }
+        } else if constexpr (kBLds && kA6 && !kNative) {
+          // FP6 A against FP8 B: A's lane half h element j is k = 16 h + j (j < 16) or
+          // 32 + 16 h + j - 16, B's is k = 32 h + j; so B's half h takes codes
+          // 16 h .. 16 h + 15 of both 32-code units (8 bytes of each half's slice)
+          const uint8_t* p = stb + (wn * CB + cb) * 2048 + ks * 1024 + lr * 16 + lh * 8;
+          const u32x2 u0 = *reinterpret_cast<const u32x2*>(p);
+          const u32x2 u1 = *reinterpret_cast<const u32x2*>(p + 512);
+          braw = u32x4{u0[0], u0[1], u1[0], u1[1]};
         } else if constexpr (kBLds) {
           braw = *reinterpret_cast<const u32x4*>(stb + (wn * CB + cb) * 2048 + ks * 1024 + lh * 512 + lr * 16);
         } else {
@@ -974,13 +982,26 @@ hipError_t launch_fp6_quantize_rows(const uint16_t* x, int64_t m, int k, int fmt
   return hipGetLastError();
 }
 
-hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream) {
+namespace {
+template <int FMT>
+hipError_t launch_w4a6_fmt(const W4A8Args& a, int fmt6, bool pow2, hipStream_t stream) {
   if (fmt6 == kFp6E2M3)
-    return pow2 ? launch_w4a8_cfg<kFp4E2M1, true, true, 4, 3, 2>(a, stream)
-                : launch_w4a8_cfg<kFp4E2M1, false, true, 4, 3, 2>(a, stream);
+    return pow2 ? launch_w4a8_cfg<FMT, true, true, 4, 3, 2>(a, stream)
+                : launch_w4a8_cfg<FMT, false, true, 4, 3, 2>(a, stream);
   if (fmt6 == kFp6E3M2)
-    return pow2 ? launch_w4a8_cfg<kFp4E2M1, true, true, 4, 3, 3>(a, stream)
-                : launch_w4a8_cfg<kFp4E2M1, false, true, 4, 3, 3>(a, stream);
+    return pow2 ? launch_w4a8_cfg<FMT, true, true, 4, 3, 3>(a, stream)
+                : launch_w4a8_cfg<FMT, false, true, 4, 3, 3>(a, stream);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+// Tiled FP4 weights of every format (E3M0 and E1M2 as FP8 B operands).
+hipError_t launch_w4a6_gemm(const W4A8Args& a, int fmt, int fmt6, bool pow2, hipStream_t stream) {
+  switch (fmt) {
+    case kFp4E2M1: return launch_w4a6_fmt<kFp4E2M1>(a, fmt6, pow2, stream);
+    case kFp4E3M0: return launch_w4a6_fmt<kFp4E3M0>(a, fmt6, pow2, stream);
+    case kFp4E1M2: return launch_w4a6_fmt<kFp4E1M2>(a, fmt6, pow2, stream);
+  }
   return hipErrorInvalidValue;
 }
 

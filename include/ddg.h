@@ -433,11 +433,11 @@ int ddg_fp6_quantize_rows(const void* x, int64_t m, int64_t k, int fmt6, uint8_t
 
 /*
  * Y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] v_w[n, k] with q_x
- * the FP6 values of ddg_fp6_quantize_rows (format fmt6) and v_w E2M1 weights
- * in tiled storage (fmt = DDG_FP4_E2M1 | DDG_FP4_TILED, optionally
- * | DDG_FP4_POW2), on the FP6 x FP4 matrix instructions; float32 accumulation.
- * Other weight formats or row storage: DDG_ERR_ARG.  Other arguments and
- * errors as ddg_w4a8_gemm.
+ * the FP6 values of ddg_fp6_quantize_rows (format fmt6) and v_w FP4 weights
+ * in tiled storage (fmt = a format | DDG_FP4_TILED, optionally
+ * | DDG_FP4_POW2): E2M1 on the FP6 x FP4 matrix instructions, E3M0 and E1M2
+ * as FP8 operands (FP6 x FP8); float32 accumulation.  Row storage:
+ * DDG_ERR_ARG.  Other arguments and errors as ddg_w4a8_gemm.
  */
 int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k, int fmt6,
                   const uint8_t* packed, const float* wscales, int fmt, int64_t n, void* y,

@@ -284,7 +284,8 @@ def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
         return g6(*a)
 
     assert call6(f6=2) == E_ARG and call6(fmt=5) == E_ARG and call6(ydt=3) == E_ARG
-    assert call6(fmt=0) == E_ARG and call6(fmt=0x201) == E_ARG and call6(fmt=0x101) == E_ARG   # tiled E2M1 only
+    assert call6(fmt=0) == E_ARG and call6(fmt=0x101) == E_ARG and call6(fmt=0x203) == E_ARG   # tiled storage only
+    assert call6(fmt=0x201, m=0, xq=None) == OK and call6(fmt=0x302, m=0, xq=None) == OK
     assert call6(k=130) == E_SHAPE and call6(n=0) == E_SHAPE and call6(m=-1) == E_SHAPE
     assert call6(xq=None) == E_ARG and call6(y=None) == E_ARG
     assert call6(xq=MISALIGNED) == E_ALIGN

@@ -290,33 +290,35 @@ def test_fp6_rows_ties_and_subnormals(gpu_lib, fmt):
     assert np.array_equal(host(xs).view(np.uint32), cs.view(np.uint32))
 
 
-def _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt):
-    absref = F.w4a6_ref(xc & 31, xs, wc & 7, ws, "e2m1", afmt)
+def _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt, wfmt="e2m1"):
+    absref = F.w4a6_ref(xc & 31, xs, wc & 7, ws, wfmt, afmt)
     assert np.all(np.abs(y - ref) <= 2.0 ** -14 * absref + 1e-37), \
         float(np.max(np.abs(y - ref) / (absref + 1e-37)))
     check_product(y, ref, False, f"w4a6 f32 {afmt} k={xc.shape[1]}")
 
 
+@pytest.mark.parametrize("wfmt", list(F.FP4_FORMATS))
 @pytest.mark.parametrize("afmt", list(F.FP6_FORMATS))
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (300, 272, 640), (513, 300, 2048), (64, 1000, 128),
                                    (257, 33, 384)])
-def test_w4a6_gemm(gpu_lib, m, n, k, afmt, pow2):
-    """The product on the oracle's FP6 codes (tiled by the oracle) and tiled E2M1 weights."""
-    _case(f"w4a6_gemm {afmt} pow2={pow2} m={m} n={n} k={k}")
+def test_w4a6_gemm(gpu_lib, m, n, k, afmt, pow2, wfmt):
+    """The product on the oracle's FP6 codes (tiled by the oracle) and tiled
+    FP4 weights of every format (E3M0 and E1M2 as FP8 operands)."""
+    _case(f"w4a6_gemm {wfmt} x {afmt} pow2={pow2} m={m} n={n} k={k}")
     rng = np.random.default_rng(m * 11 + n + k)
     w = synth.to_bf16(rng.standard_t(4, size=(n, k)) * 0.02)
     x = synth.to_bf16(rng.normal(0, 1, size=(m, k)))
-    wc, ws = F.quantize_fp4_groups(w, "e2m1", pow2=pow2)
+    wc, ws = F.quantize_fp4_groups(w, wfmt, pow2=pow2)
     xc, xs = F.quantize_rows_fp6(x, afmt)
     t, ts = F.tile_fp4(F.pack_fp4(wc), ws)
-    qw = gpu_lib.QWeightFP4(_cuda_u8(t), _cuda_f32(ts), "e2m1", n, k, pow2=pow2, tiled=True)
-    ref = F.w4a6_ref(xc, xs, wc, ws, "e2m1", afmt)
+    qw = gpu_lib.QWeightFP4(_cuda_u8(t), _cuda_f32(ts), wfmt, n, k, pow2=pow2, tiled=True)
+    ref = F.w4a6_ref(xc, xs, wc, ws, wfmt, afmt)
     xq = _cuda_u8(F.pack_fp6_tiled(xc))
     y = host(gpu_lib.w4a6_gemm(xq, _cuda_f32(xs), afmt, qw, torch.float32))
-    _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt)
+    _check_w4a6_f32(y, xc, xs, wc, ws, ref, afmt, wfmt)
     yb = host(gpu_lib.w4a6_gemm(xq, _cuda_f32(xs), afmt, qw, torch.bfloat16))
-    check_product(yb, ref, True, f"w4a6 bf16 {afmt} m={m} n={n} k={k}")
+    check_product(yb, ref, True, f"w4a6 bf16 {wfmt} x {afmt} m={m} n={n} k={k}")
 
 
 @pytest.mark.parametrize("afmt", list(F.FP6_FORMATS))
