@@ -163,7 +163,9 @@ typedef struct ddg_gemm_desc {
  * Products go into one launch per 16 products (mixed bit widths and shapes)
  * of the same class: M <= 16; 16 < M <= 32; 32 < M <= 64; M > 64 (the
  * large-M kernel's 256 x 256 tiles, deepest K first; these results equal
- * those of separate calls bit for bit).  All launches are on `stream`.
+ * bit for bit those of a separate call that takes the same whole tiles, i.e.
+ * one without K split and without 256 x 192 tiles).  All launches are on
+ * `stream`.
  *   descs   host array of `count` descriptors, read during the call only.
  *   count   0 .. DDG_MAX_GROUPED (0 is a no-op).
  * No y may overlap another product's inputs or output.  Results equal those
