@@ -283,7 +283,7 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
     }
     return by_bits<SmallF>(bits, a, rb, nc, nk, stream);
   }
-  // large kernels: 256 x 256 tiles (whole, split-K or stream-K) or 256 x 192
+  // large kernel: 256 x 256 tiles
   a.tiles_m = (a.m + ddg::kBM - 1) / ddg::kBM;
   a.tiles_n = (a.n + ddg::kBN - 1) / ddg::kBN;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
