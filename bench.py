@@ -62,14 +62,18 @@ def parse():
                          "dominant kernel (used only while the kernel sources are unchanged)")
     ap.add_argument("--tokens", type=int, default=1024,
                     help="block: tokens per product (M > 64: the large-M kernel)")
-    ap.add_argument("--suite", choices=["block16", "block", "alloc", "rotate", "w4a8"], default=None,
+    ap.add_argument("--ways", type=int, default=8,
+                    help="shard: the number of GPUs the block's linears are split over along N")
+    ap.add_argument("--suite", choices=["block16", "block", "alloc", "rotate", "w4a8", "shard"], default=None,
                     help="block16: instead of the bench line, time the four linears of a "
                          "Wan-14B block (qkv, o, up, down, their drawn bit widths) at 16 tokens, "
                          "one by one and grouped, one JSON line each; alloc: error tables of a "
                          "synthetic 4-block model on the GPU and the PD-guided bit allocation; "
                          "rotate: the block-Hadamard activation pre-pass against HBM, its cost next "
                          "to the product, and its accuracy on the outlier workload; w4a8: FP4 "
-                         "weights x FP8 per-token activations on the scaled matrix cores")
+                         "weights x FP8 per-token activations on the scaled matrix cores; shard: "
+                         "one GPU's share of the block's linears split --ways ways along N, at "
+                         "16 and 32760 tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -236,6 +240,80 @@ def block16_suite(steps, warmup):
     qkv = [resident(w[5120 * i:5120 * (i + 1)], x, b) for i, b in enumerate((5, 6, 4))]
     line("q,k,v (5,6,4 bits) one by one", qkv, timed(seq(qkv)))
     line("q,k,v (5,6,4 bits) grouped", qkv, timed(grouped(qkv)))
+
+
+def shard_suite(ways, steps, warmup):
+    """One GPU's share of the block's four linears when each is split `ways`
+    ways along N (column-parallel, no exchange: every GPU holds N/ways rows of
+    the packed weight and scales and computes those columns of Y): the first
+    N/ways rows of each drawn weight, at 16 tokens (packed-weight GB/s, >= 1 GiB
+    of weight copies rotated) and at 32760 tokens (TFLOP/s), each product
+    alone, the four one by one, and the four grouped."""
+    import torch
+
+    from dit_dequant_gemm_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    bits_of = synth.config5_bits()
+    shares = {}
+    for name in ("qkv", "o", "up", "down"):
+        n, k = synth.C5_SHAPES[name]
+        if n % (16 * ways):
+            raise SystemExit(f"{name}: {n} rows do not split into {ways} shares of whole 16-row blocks")
+        w = torch.from_numpy(synth.config5_weights(name, rows=n // ways)).to(dev, torch.bfloat16)
+        shares[name] = api.quantize_pack(w, bits_of[name])
+        del w
+
+    def line(tokens, name, ls, ms):
+        nbytes = sum(L["bytes"] for L in ls)
+        flops = sum(2.0 * tokens * L["q"].n * L["q"].k for L in ls)
+        rec = {"suite": "dit-block-shard", "ways": ways, "tokens": tokens, "linear": name,
+               "shapes": [f"{L['q'].n}x{L['q'].k}@{L['q'].bits}b" for L in ls], "us": round(ms * 1e3, 2)}
+        if tokens <= 16:
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            rec.update(packed_weight_GBps=round(gbps, 1), frac_of_hbm_peak=round(gbps / PEAK_HBM_GBPS, 4))
+        else:
+            tf = flops / (ms * 1e-3) / 1e12
+            rec.update(TFLOPs=round(tf, 1), frac_of_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        rec["steps"] = steps
+        print(json.dumps(rec), flush=True)
+
+    for tokens in (16, 32760):
+        lins = []
+        for name, q0 in shares.items():
+            nbytes = q0.packed.numel() + q0.scales.numel() * 4
+            copies = max(2, -(-ROTATE_BYTES // nbytes)) if tokens <= 16 else 1
+            qs = [q0] + [dataclasses.replace(q0, packed=q0.packed.clone(), scales=q0.scales.clone())
+                         for _ in range(copies - 1)]
+            x = torch.from_numpy(synth.config5_x(name, tokens)).to(dev, torch.bfloat16)
+            y = torch.empty((tokens, q0.n), dtype=torch.bfloat16, device=dev)
+            lins.append({"name": name, "q": q0, "qs": qs, "x": x, "y": y, "bytes": nbytes})
+
+        def seq(ls):
+            return lambda i: [api.dequant_gemm(L["x"], L["qs"][i % len(L["qs"])], out=L["y"]) for L in ls]
+
+        for L in lins:
+            line(tokens, L["name"], [L], timed(seq([L])))
+        line(tokens, "qkv+o+up+down one by one", lins, timed(seq(lins)))
+        line(tokens, "qkv+o+up+down grouped", lins,
+             timed(lambda i: api.dequant_gemm_grouped([(L["x"], L["qs"][i % len(L["qs"])], L["y"])
+                                                       for L in lins])))
+        del lins
+        torch.cuda.empty_cache()
 
 
 def _greedy_allocation(mse, nparams, target, candidates):
@@ -920,6 +998,9 @@ def main():
         return
     if args.suite == "w4a8":
         w4a8_suite(args)
+        return
+    if args.suite == "shard":
+        shard_suite(args.ways, args.steps, args.warmup)
         return
 
     c = synth.config2(m=M_BIG)

@@ -408,6 +408,39 @@ int ddg_dequant_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
   return hip_status(launch_product(a, bits, stream, sk, cus));
 }
 
+// Column blocks of 16 per workgroup (4, 2 or 1) of a grouped launch of
+// 16-token products: the choice with the least estimated time, taken as the
+// larger of the costliest workgroup and the launch's total cost per compute
+// unit; a workgroup costs its packed weight and scale bytes plus half its X
+// bytes (16 K bf16, read from L2 by every workgroup).  Fewer columns per
+// workgroup spread products with few columns or long K over more compute
+// units, at the price of more X reads.  Grouped timings at 16 tokens, bf16 Y
+// (4, 2, 1 column blocks): the four block linears 63.6 / 76.4 / 116.8 us, their
+// 2-way N shares 47.7 / 43.1 / 63.7, their 8-way shares 45.3 / 31.0 / 24.5,
+// q, k, v as three 5120 x 5120 tensors 23.0 / 28.0 / 44.5; the estimate picks
+// 4, 2, 1 and 4 of them.
+int grouped_ncb(const ddg_gemm_desc* descs, const int* list, int count, int cus) {
+  int best = 4;
+  double best_t = 0.0;
+  for (int ncb : {4, 2, 1}) {
+    double worst = 0.0, total = 0.0;
+    for (int j = 0; j < count; ++j) {
+      const ddg_gemm_desc& d = descs[list[j]];
+      const double wg_bytes = 16.0 * ncb * (double)d.k * (d.bits / 8.0 + 1.0 / DDG_GROUP * 4.0)
+                              + 0.5 * 32.0 * (double)d.k;
+      const double wgs = (double)((d.n + 16 * ncb - 1) / (16 * ncb));
+      worst = std::max(worst, wg_bytes);
+      total += wgs * wg_bytes;
+    }
+    const double t = std::max(worst, total / std::max(cus, 1));
+    if (ncb == 4 || t < best_t) {
+      best = ncb;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t stream) {
   if (count < 0 || count > DDG_MAX_GROUPED) return DDG_ERR_SHAPE;
   if (count == 0) return DDG_OK;
@@ -494,13 +527,14 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
   for (int s0 = 0; s0 < n_small; s0 += ddg::kMaxGroup) {
     ddg::GroupArgs ga{};
     ga.count = std::min(ddg::kMaxGroup, n_small - s0);
+    ga.ncb = grouped_ncb(descs, small + s0, ga.count, cus);
     ga.wg_start[0] = 0;
     for (int j = 0; j < ga.count; ++j) {
       const ddg_gemm_desc& d = descs[small[s0 + j]];
       ga.g[j] = args_of(d);
       ga.bits[j] = d.bits;
       ga.kc[j] = skinny_chunk(d.k / DDG_GROUP);
-      const int64_t wgs = (d.n + 16 * ddg::kGroupedNcb - 1) / (16 * ddg::kGroupedNcb);
+      const int64_t wgs = (d.n + 16 * ga.ncb - 1) / (16 * ga.ncb);
       if (ga.wg_start[j] + wgs > kMaxDim) return DDG_ERR_SHAPE;
       ga.wg_start[j + 1] = ga.wg_start[j] + (int)wgs;
     }

@@ -1538,7 +1538,6 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs args) {
 // by bit width and chunk size.  The LDS arrays are sized for the widest case.
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroup = 16;
-constexpr int kGroupedNcb = 4;
 
 struct GroupArgs {
   GemmArgs g[kMaxGroup];
@@ -1546,6 +1545,7 @@ struct GroupArgs {
   int bits[kMaxGroup];
   int kc[kMaxGroup];
   int count;
+  int ncb;          // M <= 16 launch: column blocks of 16 per workgroup (1, 2 or 4)
 };
 
 // Up to kMaxGroup products with M > 64 in one launch of K2 tiles:

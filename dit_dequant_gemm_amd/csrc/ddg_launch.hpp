@@ -39,8 +39,9 @@ hipError_t launch_gemm_small_split(const GemmArgs& a, int nc, const SmallSplit& 
 template <int B>
 hipError_t launch_gemm_skinny(const GemmArgs& a, int kc, int ncb, hipStream_t stream);
 
-// up to kMaxGroup products with M <= 16 in one launch (ga.wg_start is the
-// prefix sum of ceil(n / (16 kGroupedNcb)) over the products)
+// up to kMaxGroup products with M <= 16 in one launch of ga.ncb (1, 2 or 4)
+// column blocks of 16 per workgroup (ga.wg_start is the prefix sum of
+// ceil(n / (16 ga.ncb)) over the products)
 hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream);
 // up to kMaxGroup products with M > 64 in one launch of 256 x 256 tiles
 // (ga.tile_start is the prefix sum of the products' tile counts)

@@ -3,8 +3,8 @@
 
 namespace ddg {
 
+template <int NCB>
 __global__ __launch_bounds__(512) void gemm_grouped_skinny_kernel(GroupArgs ga) {
-  constexpr int NCB = kGroupedNcb;
   using L = SkinnyLds<7, 5, NCB>;
   __shared__ __attribute__((aligned(1024))) uint8_t wl0[L::W0];
   __shared__ __attribute__((aligned(1024))) uint8_t wl1[L::W1];
@@ -94,7 +94,14 @@ hipError_t launch_gemm_grouped(const GroupArgs& ga, hipStream_t stream) {
   if (ga.count < 1 || ga.count > kMaxGroup) return hipErrorInvalidValue;
   const int wgs = ga.wg_start[ga.count];
   if (wgs <= 0) return hipSuccess;
-  gemm_grouped_skinny_kernel<<<dim3((unsigned)wgs), dim3(512), 0, stream>>>(ga);
+  if (ga.ncb == 4)
+    gemm_grouped_skinny_kernel<4><<<dim3((unsigned)wgs), dim3(512), 0, stream>>>(ga);
+  else if (ga.ncb == 2)
+    gemm_grouped_skinny_kernel<2><<<dim3((unsigned)wgs), dim3(512), 0, stream>>>(ga);
+  else if (ga.ncb == 1)
+    gemm_grouped_skinny_kernel<1><<<dim3((unsigned)wgs), dim3(512), 0, stream>>>(ga);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

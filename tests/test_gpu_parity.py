@@ -294,6 +294,47 @@ def test_gemm_grouped_matches_single_calls(gpu_lib):
         check_product(host(a), b.astype(np.float64), False, "grouped vs single")
 
 
+# The grouped 16-token launch takes 4, 2 or 1 column blocks of 16 per
+# workgroup, whichever has the least estimated time: the larger of the
+# costliest workgroup and the total cost per compute unit, a workgroup costing
+# its packed and scale bytes plus half its X bytes.  _grouped_ncb restates that
+# choice so that each set below is known to run the form it is meant to cover
+# (mixed widths and dtypes, ragged N: partial last workgroups).
+_GROUP_NCB_CASES = {
+    1: [(16, 1952, 384, 4, torch.bfloat16), (5, 1040, 256, 6, torch.float32),
+        (16, 272, 640, 3, torch.bfloat16), (1, 64, 128, 7, torch.float32)],
+    2: [(16, 4112, 256, 5, torch.float32), (16, 3088, 128, 4, torch.bfloat16),
+        (7, 2064, 256, 6, torch.float32), (16, 1008, 384, 3, torch.bfloat16)],
+    4: [(16, 12304, 128, 4, torch.bfloat16), (11, 8208, 128, 5, torch.float32),
+        (16, 4096, 256, 3, torch.bfloat16), (2, 1040, 128, 7, torch.float32)],
+}
+
+
+def _grouped_ncb(cases, cus):
+    est = {}
+    for ncb in (4, 2, 1):
+        worst = total = 0.0
+        for _m, n, k, bits, _dt in cases:
+            wg = 16.0 * ncb * k * (bits / 8.0 + 4.0 / 128) + 0.5 * 32.0 * k
+            worst = max(worst, wg)
+            total += -(-n // (16 * ncb)) * wg
+        est[ncb] = max(worst, total / cus)
+    best = 4
+    for ncb in (2, 1):
+        if est[ncb] < est[best]:
+            best = ncb
+    return best
+
+
+@pytest.mark.parametrize("ncb", sorted(_GROUP_NCB_CASES))
+def test_gemm_grouped_column_blocks(gpu_lib, ncb):
+    _case(f"dequant_gemm_grouped 16-token launch with {ncb} column blocks per workgroup")
+    cases = _GROUP_NCB_CASES[ncb]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert _grouped_ncb(cases, cus) == ncb, "the set no longer selects the form it covers"
+    _run_group(gpu_lib, cases, 11 + ncb)
+
+
 def test_gemm_empty_batch_leaves_output(gpu_lib):
     _case("dequant_gemm m=0")
     c = synth.random_case(1, 4, 32, 128)
