@@ -564,7 +564,8 @@ def w4a8_suite(args):
     activation quantizers against HBM, the products (row and tiled weight
     storage, float32 and power-of-two scales) against the dense matrix peaks,
     the 4-bit bf16 product beside them, and each path's error against the
-    float32 product of the unquantized weight."""
+    float32 product of the unquantized weight; then the main products at
+    32760 x 5120 x 5120 (a second JSON line)."""
     import torch
 
     from dit_dequant_gemm_amd import api, synth
@@ -680,6 +681,40 @@ def w4a8_suite(args):
         "w6a8_e2m3_rel_err_vs_f32": round(e_w6["e2m3"], 5), "w6a8_e3m2_rel_err_vs_f32": round(e_w6["e3m2"], 5),
         "int4_w4a16_rel_err_vs_f32": round(e_int4, 5),
     }), flush=True)
+    del x, w, xq, xs, y, qf, qp, qt, qtp, qi, q6w, x6, s6, xr, yref
+    torch.cuda.empty_cache()
+
+    # The same products at a Wan-14B block shape with many tile rounds (the o
+    # projection, 32760 x 5120 x 5120), where a single wave of tiles no longer
+    # bounds them: tiled E2M1 weights with E4M3 and E2M3 activations, E2M3
+    # weights with E4M3 activations, and the 4-bit bf16 product.
+    m, (n, k) = 32760, synth.C5_SHAPES["o"]
+    x = torch.from_numpy(synth.config5_x("o", m)).to(dev, torch.bfloat16)
+    w = torch.from_numpy(synth.config5_weights("o")).to(dev, torch.bfloat16)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    xq, xs = api.fp8_quantize_rows(x)
+    x6, s6 = api.fp6_quantize_rows(x, "e2m3")
+    qt = api.fp4_quantize_pack(w, "e2m1", tiled=True)
+    qtp = api.fp4_quantize_pack(w, "e2m1", pow2=True, tiled=True)
+    q6 = api.fp6_quantize_pack(w, "e2m3")
+    q6p = api.fp6_quantize_pack(w, "e2m3", pow2=True)
+    qi = api.quantize_pack(w, 4)
+    steps = max(1, args.steps // 4)
+    big = {"w4a8_tiled": burst(lambda: api.w4a8_gemm(xq, xs, qt, out=y), steps),
+           "w4a8_tiled_pow2": burst(lambda: api.w4a8_gemm(xq, xs, qtp, out=y), steps),
+           "w4a6_e2m3": burst(lambda: api.w4a6_gemm(x6, s6, "e2m3", qt, out=y), steps),
+           "w4a6_e2m3_pow2": burst(lambda: api.w4a6_gemm(x6, s6, "e2m3", qtp, out=y), steps),
+           "w6a8_e2m3": burst(lambda: api.w6a8_gemm(xq, xs, q6, out=y), steps),
+           "w6a8_e2m3_pow2": burst(lambda: api.w6a8_gemm(xq, xs, q6p, out=y), steps),
+           "int4_bf16": burst(lambda: api.dequant_gemm(x, qi, out=y), steps)}
+    peak = {"w4a8_tiled": 5000.0, "w4a8_tiled_pow2": 5000.0, "w4a6_e2m3": 10100.0, "w4a6_e2m3_pow2": 10100.0,
+            "w6a8_e2m3": 5000.0, "w6a8_e2m3_pow2": 5000.0, "int4_bf16": PEAK_BF16_TFLOPS}
+    flops = 2.0 * m * n * k
+    rec = {"suite": "w4a8-fp4", "shape": [m, n, k], "steps": steps}
+    for key, ms in big.items():
+        tf = flops / ms / 1e9
+        rec[key] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / peak[key], 4)}
+    print(json.dumps(rec), flush=True)
 
 
 def _sysfs_clock_power():
