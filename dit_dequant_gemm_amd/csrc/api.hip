@@ -24,6 +24,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool bits_ok(int bits) { return bits >= 3 && bits <= 7; }
 
 bool k_ok(int64_t k) { return k > 0 && k <= kMaxDim && k % DDG_GROUP == 0; }
+// rows x k weights at one lane per 32 stay within DDG_CHUNK_WEIGHTS_MAX (k
+// already checked; rows may be padded)
+bool chunks_ok(int64_t rows, int64_t k) { return rows <= DDG_CHUNK_WEIGHTS_MAX / k; }
 
 // a * b without overflow past 2^62 (byte counts stay well inside int64).
 bool mul_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && (a == 0 || b <= (INT64_C(1) << 62) / a); }
@@ -363,7 +366,7 @@ int ddg_packed_bytes(int64_t n, int64_t k, int bits, int64_t* packed_bytes, int6
 int ddg_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int bits, uint8_t* packed,
                       float* scales, hipStream_t stream) {
   if (!bits_ok(bits) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32)) return DDG_ERR_ARG;
-  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4)) return DDG_ERR_SHAPE;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4) || !chunks_ok(n, k)) return DDG_ERR_SHAPE;
   if (n == 0) return DDG_OK;
   if (!w || !packed || !scales) return DDG_ERR_ARG;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
@@ -377,7 +380,7 @@ int ddg_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int bits
 int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t n, int64_t k,
                    void* w_out, hipStream_t stream) {
   if (!bits_ok(bits)) return DDG_ERR_ARG;
-  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 2)) return DDG_ERR_SHAPE;
+  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 2) || !chunks_ok(n, k)) return DDG_ERR_SHAPE;
   if (n == 0) return DDG_OK;
   if (!packed || !scales || !w_out) return DDG_ERR_ARG;
   if (!aligned(packed, 16) || !aligned(w_out, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
@@ -664,7 +667,9 @@ int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
                           float* scales, hipStream_t stream) {
   if (!fp4_fmt_ok(fmt) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
     return DDG_ERR_ARG;
-  if (n < 0 || !k_ok(k) || !mul_ok(n, k) || !mul_ok(n * k, 4)) return DDG_ERR_SHAPE;
+  if (n < 0 || n > kMaxDim || !k_ok(k) || !mul_ok(n + 31, k) || !mul_ok((n + 31) * k, 4) ||
+      !chunks_ok((n + 31) / 32 * 32, k))
+    return DDG_ERR_SHAPE;
   if (n == 0) return DDG_OK;
   if (!w || !packed || !scales) return DDG_ERR_ARG;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;
@@ -732,7 +737,9 @@ int ddg_fp6_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
   const int f = fmt6 & ~DDG_FP4_POW2;
   if ((f != DDG_FP6_E2M3 && f != DDG_FP6_E3M2) || (w_dtype != DDG_BF16 && w_dtype != DDG_F32))
     return DDG_ERR_ARG;
-  if (n < 0 || n > kMaxDim || !k_ok(k) || !mul_ok(n + 31, k) || !mul_ok((n + 31) * k, 4)) return DDG_ERR_SHAPE;
+  if (n < 0 || n > kMaxDim || !k_ok(k) || !mul_ok(n + 31, k) || !mul_ok((n + 31) * k, 4) ||
+      !chunks_ok((n + 31) / 32 * 32, k))
+    return DDG_ERR_SHAPE;
   if (n == 0) return DDG_OK;
   if (!w || !packed || !scales) return DDG_ERR_ARG;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return DDG_ERR_ALIGN;

@@ -60,6 +60,10 @@ extern "C" {
 #endif
 
 #define DDG_GROUP 128      /* weights per scale ([WDQ] §3.1) */
+/* Most weights (n * k; for the FP4/FP6 quantizers with n padded to a
+ * multiple of 32) that a weight quantizer or ddg_dequantize takes in one
+ * call: one lane per 32 weights keeps the launch below 2^32 work-items. */
+#define DDG_CHUNK_WEIGHTS_MAX ((INT64_C(1) << 37) - 8192)
 #define DDG_VERSION 1
 
 typedef enum ddg_dtype {
@@ -103,7 +107,7 @@ int ddg_packed_bytes(int64_t n, int64_t k, int bits, int64_t* packed_bytes,
  * (correctly rounded multiply and divide, no fused operations, subnormals
  * kept).  n == 0 is a no-op.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE (n < 0; k not a positive multiple of
- * 128), DDG_ERR_ALIGN, DDG_ERR_HIP.
+ * 128; n * k above DDG_CHUNK_WEIGHTS_MAX), DDG_ERR_ALIGN, DDG_ERR_HIP.
  */
 int ddg_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
                       uint8_t* packed, float* scales, hipStream_t stream);
@@ -368,7 +372,8 @@ int ddg_rpbh_rotate(const void* x, int x_dtype, int64_t n, int64_t d, const int3
  *   w       device, n x k bf16 or float32 (w_dtype), finite, 16-byte aligned.
  *   packed  device, 16-byte aligned.   scales  device, 4-byte aligned.
  * n == 0 is a no-op.  Errors: DDG_ERR_ARG (fmt, dtype, null), DDG_ERR_SHAPE
- * (k not a positive multiple of 128), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ * (k not a positive multiple of 128; ceil(n/32) * 32 * k above
+ * DDG_CHUNK_WEIGHTS_MAX), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
  */
 int ddg_fp4_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt,
                           uint8_t* packed, float* scales, hipStream_t stream);
@@ -465,8 +470,8 @@ int ddg_w4a6_gemm(const uint8_t* xq, const float* xscales, int64_t m, int64_t k,
  *   w       device, n x k bf16 or float32 (w_dtype), finite, 16-byte aligned.
  *   packed  device, 16-byte aligned.   scales  device, 4-byte aligned.
  * n == 0 is a no-op.  Errors: DDG_ERR_ARG (fmt6, dtype, null), DDG_ERR_SHAPE
- * (k not a positive multiple of 128, n above 2^31 - 1), DDG_ERR_ALIGN,
- * DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
+ * (k not a positive multiple of 128, n above 2^31 - 1, ceil(n/32) * 32 * k
+ * above DDG_CHUNK_WEIGHTS_MAX), DDG_ERR_ALIGN, DDG_ERR_HIP, DDG_ERR_UNSUPPORTED.
  */
 int ddg_fp6_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int fmt6,
                           uint8_t* packed, float* scales, hipStream_t stream);

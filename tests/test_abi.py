@@ -230,6 +230,31 @@ def test_rpbh_rotate_rejects_bad_arguments(lib):
     assert call(n=0, x=None, perm=None, signs=None, out=None) == OK
 
 
+def test_weight_quantizers_bound_the_launch(lib):
+    """One lane per 32 weights: the quantizers and the dequantizer take at
+    most DDG_CHUNK_WEIGHTS_MAX weights (rows padded to 32 for FP4/FP6), so the
+    launch stays below 2^32 work-items.  At the bound the shape passes and the
+    null pointer is what is rejected; one row more is a shape error."""
+    assert re.search(r"#define DDG_CHUNK_WEIGHTS_MAX \(\(INT64_C\(1\) << 37\) - 8192\)", open(HEADER).read())
+    cap = (1 << 37) - 8192
+    assert (cap // 32 + 255) // 256 * 256 < 1 << 32
+    k = 128
+    n_max = cap // k                                  # a multiple of 32
+    assert n_max % 32 == 0
+    q, d = lib.ddg_quantize_pack, lib.ddg_dequantize
+    q4, q6 = lib.ddg_fp4_quantize_pack, lib.ddg_fp6_quantize_pack
+    assert q(None, 0, n_max, k, 4, FAKE, FAKE, None) == E_ARG
+    assert q(FAKE, 0, n_max + 1, k, 4, FAKE, FAKE, None) == E_SHAPE
+    assert d(None, FAKE, 4, n_max, k, FAKE, None) == E_ARG
+    assert d(FAKE, FAKE, 4, n_max + 1, k, FAKE, None) == E_SHAPE
+    for f in (0, 0x200):                              # row and tiled storage
+        assert q4(None, 0, n_max, k, f, FAKE, FAKE, None) == E_ARG
+        assert q4(FAKE, 0, n_max + 1, k, f, FAKE, FAKE, None) == E_SHAPE
+    assert q6(None, 0, n_max, k, 0, FAKE, FAKE, None) == E_ARG
+    assert q6(FAKE, 0, n_max + 1, k, 0, FAKE, FAKE, None) == E_SHAPE
+    assert q(FAKE, 0, n_max // 2, 2 * k + 128, 4, FAKE, FAKE, None) == E_SHAPE   # the product counts
+
+
 def test_fp4_and_w4a8_calls_reject_bad_arguments(lib):
     q = lib.ddg_fp4_quantize_pack
     assert q(FAKE, 0, 4, 128, 3, FAKE, FAKE, None) == E_ARG           # fmt
