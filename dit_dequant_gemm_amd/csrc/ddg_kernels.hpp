@@ -712,7 +712,7 @@ __device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, 
                        (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
         __bf16* dst = static_cast<__bf16*>(args.y) + base;
         if (vec && gc + 8 <= args.n) {
-          *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
+          store_out16(dst, __builtin_bit_cast(u32x4, v));
         } else {
           for (int e = 0; e < 8 && gc + e < args.n; ++e) dst[e] = v[e];
         }
@@ -720,7 +720,7 @@ __device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, 
         const f32x4 t = *reinterpret_cast<const f32x4*>(src);
         float* dst = static_cast<float*>(args.y) + base;
         if (vec && gc + 4 <= args.n) {
-          *reinterpret_cast<f32x4*>(dst) = t;
+          store_out16(dst, __builtin_bit_cast(u32x4, t));
         } else {
           for (int e = 0; e < 4 && gc + e < args.n; ++e) dst[e] = t[e];
         }
