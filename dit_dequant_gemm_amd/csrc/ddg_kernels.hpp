@@ -292,26 +292,6 @@ __device__ __forceinline__ void large_accumulate(const GemmArgs& args, int tm, i
                                             aoff[u >> 3]);
   };
 
-  if (lowrank && args.t != nullptr) {
-    // acc = T * lora_up^T over the rank dimension, 16 at a time (zero-padded).
-    const int R = args.r;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    const int n = min(nw0 + wave * 32 + lr, args.n - 1);
-    for (int j0 = 0; j0 < R; j0 += 16) {
-      const int kk = j0 + 8 * lh;
-      const bool kok = kk < R;
-      const int kc = min(kk, R - 8);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
-      const bf16x8 bl = kok ? v : zero;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int m = min(m0 + rb * 32 + lr, args.m - 1);
-        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
-        acc[rb] = mfma32x32x16(kok ? tv : zero, bl, acc[rb]);
-      }
-    }
-  }
-
   uint32_t wc[CW], wn[CW], be[CW];
   float sc = 0.f, sn = 0.f, ns64 = 0.f;
   bf16x8 ring[RING];
@@ -343,6 +323,28 @@ __device__ __forceinline__ void large_accumulate(const GemmArgs& args, int tm, i
 #pragma unroll
   for (int i = 0; i < 8; ++i) issue_x_one(g0, st0, i);
   load_w(g0, wn, sn);
+  // the low-rank branch's loads go out behind the first group's, so that
+  // their latencies overlap (32760 x 5120 x 5120, r = 32: 1558 -> 1504 us for
+  // the fused call); it still adds into acc before the K loop
+  if (lowrank && args.t != nullptr) {
+    // acc = T * lora_up^T over the rank dimension, 16 at a time (zero-padded).
+    const int R = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    const int n = min(nw0 + wave * 32 + lr, args.n - 1);
+    for (int j0 = 0; j0 < R; j0 += 16) {
+      const int kk = j0 + 8 * lh;
+      const bool kok = kk < R;
+      const int kc = min(kk, R - 8);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
+      const bf16x8 bl = kok ? v : zero;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int m = min(m0 + rb * 32 + lr, args.m - 1);
+        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
+        acc[rb] = mfma32x32x16(kok ? tv : zero, bl, acc[rb]);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   take_next_weights();
@@ -540,32 +542,6 @@ __device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, 
 #pragma unroll
     for (int c = 0; c < CB; ++c) acc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (args.t != nullptr) {
-    // acc = T * lora_up^T over the rank dimension, 32 at a time (zero-padded).
-    const int R = args.r;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    for (int j0 = 0; j0 < R; j0 += 32) {
-      const int kk = j0 + 8 * lq;
-      const bool kok = kk < R;
-      const int kc = min(kk, R - 8);
-      bf16x8 bl[CB];
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int n = min(nw0 + (int)ncol + 16 * c, args.n - 1);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
-        bl[c] = kok ? v : zero;
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int m = min(m0 + rb * 16 + lr, args.m - 1);
-        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
-        const bf16x8 a = kok ? tv : zero;
-#pragma unroll
-        for (int c = 0; c < CB; ++c) acc[rb][c] = mfma16x16x32(a, bl[c], acc[rb][c]);
-      }
-    }
-  }
-
   uint32_t wc[CB][B], wn[CB][B], be1[CB][B];
   float sc[CB], sn[CB], nsh[CB];
   uint32_t ev[CB], od[CB];              // 4-bit: the chunk dword's codes plus one, as bytes
@@ -607,6 +583,33 @@ __device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, 
 #pragma unroll
   for (int i = 0; i < 16; ++i) issue_x_one(0, 0, i);
   load_w(0, wn, sn);
+  // the low-rank branch behind the first group's loads, as in K2
+  // (4096 x 3072 x 3072, r = 32: 87.6 -> 84.3 us for the fused call)
+  if (args.t != nullptr) {
+    // acc = T * lora_up^T over the rank dimension, 32 at a time (zero-padded).
+    const int R = args.r;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int j0 = 0; j0 < R; j0 += 32) {
+      const int kk = j0 + 8 * lq;
+      const bool kok = kk < R;
+      const int kc = min(kk, R - 8);
+      bf16x8 bl[CB];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int n = min(nw0 + (int)ncol + 16 * c, args.n - 1);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(args.lora_up + (int64_t)n * R + kc);
+        bl[c] = kok ? v : zero;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int m = min(m0 + rb * 16 + lr, args.m - 1);
+        const bf16x8 tv = *reinterpret_cast<const bf16x8*>(args.t + (int64_t)m * R + kc);
+        const bf16x8 a = kok ? tv : zero;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[rb][c] = mfma16x16x32(a, bl[c], acc[rb][c]);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   take_next_weights();
@@ -1564,15 +1567,20 @@ struct GroupLargeArgs {
 // ---------------------------------------------------------------------------
 // K4: T = bf16(X * L1), with L1^T = lora_down (R x K) -- computed as
 // T^T = lora_down * X^T so both MFMA operands are contiguous 16-byte reads.
-// Workgroup = 4 waves over 16 token rows; waves split K in 32-wide steps;
-// the 4 partials are summed through LDS, then rounded to bf16 once.
+// Workgroup = 8 waves over 16 token rows; waves split K in 32-wide steps;
+// the 8 partials are summed through LDS in wave order, then rounded to bf16
+// once.  (Eight waves rather than four keep more loads in flight: the fused
+// 4096 x 3072 x 3072 call, r = 32, 84.3 -> 82.2 us.)
 // ---------------------------------------------------------------------------
+constexpr int kLowrankWaves = 8;
+
 template <int RBLK>
-__global__ __launch_bounds__(256) void lowrank_t_kernel(const __bf16* __restrict__ x,
-                                                        const __bf16* __restrict__ lora_down,
-                                                        __bf16* __restrict__ t, int m, int k,
-                                                        int r) {
-  __shared__ f32x4 red[4][RBLK][64];
+__global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_kernel(const __bf16* __restrict__ x,
+                                                                       const __bf16* __restrict__ lora_down,
+                                                                       __bf16* __restrict__ t, int m, int k,
+                                                                       int r) {
+  constexpr int NW = kLowrankWaves;
+  __shared__ f32x4 red[NW][RBLK][64];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lq = lane >> 4;
@@ -1585,13 +1593,13 @@ __global__ __launch_bounds__(256) void lowrank_t_kernel(const __bf16* __restrict
   // U steps of this wave's K range per trip, their loads issued before the
   // first MFMA (the loop is bound by load latency otherwise)
   constexpr int U = RBLK <= 2 ? 8 : (RBLK <= 4 ? 4 : 2);
-  const int steps = (k - wave * 32 + 127) / 128;
+  const int steps = (k - wave * 32 + 32 * NW - 1) / (32 * NW);
   int st = 0;
   for (; st + U <= steps; st += U) {
     bf16x8 bv[U], av[U][RBLK];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k0 = wave * 32 + 128 * (st + u);
+      const int k0 = wave * 32 + 32 * NW * (st + u);
       bv[u] = *reinterpret_cast<const bf16x8*>(xrow + k0);
 #pragma unroll
       for (int j = 0; j < RBLK; ++j) {
@@ -1605,7 +1613,7 @@ __global__ __launch_bounds__(256) void lowrank_t_kernel(const __bf16* __restrict
       for (int j = 0; j < RBLK; ++j) acc[j] = mfma16x16x32(av[u][j], bv[u], acc[j]);
   }
   for (; st < steps; ++st) {
-    const int k0 = wave * 32 + 128 * st;
+    const int k0 = wave * 32 + 32 * NW * st;
     const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow + k0);
 #pragma unroll
     for (int j = 0; j < RBLK; ++j) {
@@ -1624,7 +1632,7 @@ __global__ __launch_bounds__(256) void lowrank_t_kernel(const __bf16* __restrict
     for (int j = 0; j < RBLK; ++j) {
       f32x4 s = red[0][j][lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
+      for (int w = 1; w < NW; ++w) {
         const f32x4 v = red[w][j][lane];
         s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
       }

@@ -5,7 +5,7 @@ namespace ddg {
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream) {
-  const dim3 grid((unsigned)((m + 15) / 16)), block(256);
+  const dim3 grid((unsigned)((m + 15) / 16)), block(64 * kLowrankWaves);
   switch ((r + 15) / 16) {
     case 1: lowrank_t_kernel<1><<<grid, block, 0, stream>>>(x, lora_down, t, m, k, r); break;
     case 2: lowrank_t_kernel<2><<<grid, block, 0, stream>>>(x, lora_down, t, m, k, r); break;
