@@ -1567,12 +1567,10 @@ struct GroupLargeArgs {
 // ---------------------------------------------------------------------------
 // K4: T = bf16(X * L1), with L1^T = lora_down (R x K) -- computed as
 // T^T = lora_down * X^T so both MFMA operands are contiguous 16-byte reads.
-// Workgroup = 8 waves over 16 token rows; waves split K in 32-wide steps;
-// the 8 partials are summed through LDS in wave order, then rounded to bf16
-// once.  (Eight waves rather than four keep more loads in flight: the fused
-// 4096 x 3072 x 3072 call, r = 32, 84.3 -> 82.2 us.)
+// Workgroup = 4 waves over 16 token rows; waves split K in 32-wide steps;
+// the 4 partials are summed through LDS, then rounded to bf16 once.
 // ---------------------------------------------------------------------------
-constexpr int kLowrankWaves = 8;
+constexpr int kLowrankWaves = 4;
 
 template <int RBLK>
 __global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_kernel(const __bf16* __restrict__ x,
