@@ -44,6 +44,19 @@ PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 M_BIG, M_SMALL, N, K, BITS = 4096, 16, 3072, 3072, 4
 REPEATS = 5
 ROTATE_BYTES = 1 << 30
+# a burst of back-to-back launches holds at least this many launches, or at
+# least this long a stretch of them, whichever is reached first
+BURST_MIN_LAUNCHES = 100
+BURST_MIN_MS = 200.0
+
+
+def burst_count(ms_one, steps):
+    """Launches per timed burst for a kernel of about ms_one per launch:
+    --steps, raised to BURST_MIN_LAUNCHES or to BURST_MIN_MS of launches
+    (whichever needs fewer)."""
+    import math
+    need = min(BURST_MIN_LAUNCHES, math.ceil(BURST_MIN_MS / max(ms_one, 1e-6)))
+    return max(steps, need)
 
 
 def parse():
@@ -915,7 +928,8 @@ def workload_lines(api, synth, torch, steps, warmup):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        return _median_burst_ms(torch, fn, steps)
+        one = _median_burst_ms(torch, fn, 1, repeats=1)
+        return _median_burst_ms(torch, fn, burst_count(one, steps))
 
     # workload 3: Student-t(4) weights, std 0.02
     t4 = torch.distributions.StudentT(torch.tensor(4.0, device=dev))
@@ -1104,14 +1118,17 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # per-kernel averages: median over REPEATS bursts of `steps` launches each
+    # per-kernel averages: median over REPEATS bursts of at least
+    # BURST_MIN_LAUNCHES launches each (all three kernels take well under
+    # BURST_MIN_MS / BURST_MIN_LAUNCHES per launch)
     base = args.warmup + args.steps
+    n_burst = max(args.steps, BURST_MIN_LAUNCHES)
     reps = {"q": [], "g": [], "s": []}
     for r in range(REPEATS):
-        off = base + r * args.steps
-        reps["q"].append(burst_ms(quantize_into, args.steps, off))
-        reps["g"].append(burst_ms(gemm_big, args.steps, off))
-        reps["s"].append(burst_ms(gemm_small, args.steps, off))
+        off = base + r * n_burst
+        reps["q"].append(burst_ms(quantize_into, n_burst, off))
+        reps["g"].append(burst_ms(gemm_big, n_burst, off))
+        reps["s"].append(burst_ms(gemm_small, n_burst, off))
     t_q, t_g, t_s = (float(np.median(reps[k])) for k in ("q", "g", "s"))
 
     # context, not a target: torch's dense bf16 product of the same shape on
@@ -1160,6 +1177,7 @@ def main():
         "kernels_ms_repeats": {k: [round(v, 5) for v in reps[k2]]
                                for k, k2 in (("quantize_pack", "q"), ("dequant_gemm_m4096", "g"),
                                              ("dequant_gemm_m16", "s"))},
+        "launches_per_burst": n_burst,
         "context_torch_matmul_bf16_dense_TFLOPs": round(flops / (t_dense * 1e-3) / 1e12, 1),
         "system": system_info(torch),
         "clock_power_under_load": dict(under_load, kernel="dequant_gemm_m4096"),
