@@ -127,11 +127,25 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------------------
 // Epilogue store of one 16x16 MFMA accumulator tile.  Lane (lr = lane%16,
-// lq = lane/16) holds rows 4*lq .. 4*lq+3 of column lr.
+// lq = lane/16) holds rows 4*lq .. 4*lq+3 of column lr; row0 = 16 rb + 4 lq
+// and col = 16 cb + lr for a tile (rb, cb) that is the same for all lanes.
 // ---------------------------------------------------------------------------
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(void* __restrict__ y, int64_t ldy, int row0, int col,
                                            int m_rows, int n_cols, f32x4 v) {
+  // a 16 x 16 tile wholly inside Y: no per-lane checks (one uniform branch;
+  // 16 x 3072 x 3072: 6.29 -> 6.17 us, 16 x 640 x 5120: 7.68 -> 6.29 us)
+  if (__builtin_amdgcn_readfirstlane(row0 & ~15) + 16 <= m_rows &&
+      __builtin_amdgcn_readfirstlane(col & ~15) + 16 <= n_cols) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (OUT_BF16)
+        static_cast<__bf16*>(y)[(int64_t)(row0 + i) * ldy + col] = (__bf16)v[i];
+      else
+        static_cast<float*>(y)[(int64_t)(row0 + i) * ldy + col] = v[i];
+    }
+    return;
+  }
   if (col >= n_cols) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
