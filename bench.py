@@ -1094,7 +1094,12 @@ def main():
         gemm_small(i)
 
     def burst_ms(fn, count, offset):
-        """Average duration of `count` back-to-back launches of fn."""
+        """Average duration of `count` back-to-back launches of fn, after
+        --warmup untimed launches of the same kernel (the first launches
+        after another kernel's burst run slower while the clock settles)."""
+        for i in range(args.warmup):
+            fn(offset + i)
+        offset += args.warmup
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -1120,12 +1125,13 @@ def main():
 
     # per-kernel averages: median over REPEATS bursts of at least
     # BURST_MIN_LAUNCHES launches each (all three kernels take well under
-    # BURST_MIN_MS / BURST_MIN_LAUNCHES per launch)
+    # BURST_MIN_MS / BURST_MIN_LAUNCHES per launch), each burst after its own
+    # warm-up launches
     base = args.warmup + args.steps
     n_burst = max(args.steps, BURST_MIN_LAUNCHES)
     reps = {"q": [], "g": [], "s": []}
     for r in range(REPEATS):
-        off = base + r * n_burst
+        off = base + r * (n_burst + args.warmup)
         reps["q"].append(burst_ms(quantize_into, n_burst, off))
         reps["g"].append(burst_ms(gemm_big, n_burst, off))
         reps["s"].append(burst_ms(gemm_small, n_burst, off))
