@@ -1,6 +1,9 @@
 """The C ABI on the host (CPU only): the library loads, exports every entry
 point declared in include/ddg.h, and rejects bad arguments before any HIP
-call.  No compute call is made here."""
+call.  No compute call is made here: every call either expects an error that
+the host checks return before any launch, or is an empty (M == 0) no-op, so
+the file is safe to run where a GPU is present (the fake addresses below are
+never handed to a kernel)."""
 import ctypes
 import os
 import re
@@ -198,7 +201,25 @@ def test_lowrank_fused_gemm_rejects_bad_arguments(lib):
     assert call(wsb=64 * 64 - 1) == E_WS
     assert call(bits=1) == E_ARG
     assert call(k=100) == E_SHAPE
+    # the T pre-pass launches 16 work-items per row: at most 2^28 - 16 rows
+    assert call(m=(1 << 28) - 15, wsb=1 << 40) == E_SHAPE
     assert call(m=0, x=None, down=None, up=None, ws=None, y=None) == OK
+
+
+def test_lowrank_down_rejects_bad_arguments(lib):
+    """T = bf16(X L1) alone: shapes, null and misaligned pointers are refused
+    on the host before any launch; M == 0 is a no-op."""
+    f = lib.ddg_lowrank_down
+
+    def call(x=FAKE, m=64, k=256, down=FAKE, r=32, t=FAKE):
+        return f(x, m, k, down, r, t, None)
+
+    assert call(r=12) == E_SHAPE and call(r=0) == E_SHAPE and call(r=136) == E_SHAPE
+    assert call(k=100) == E_SHAPE and call(k=0) == E_SHAPE and call(k=2 ** 20 + 128) == E_SHAPE
+    assert call(m=-1) == E_SHAPE and call(m=(1 << 28) - 15) == E_SHAPE
+    assert call(x=None) == E_ARG and call(down=None) == E_ARG and call(t=None) == E_ARG
+    assert call(x=MISALIGNED) == E_ALIGN and call(down=MISALIGNED) == E_ALIGN and call(t=FAKE + 8) == E_ALIGN
+    assert call(m=0, x=None, down=None, t=None) == OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -371,11 +392,13 @@ def test_row_quantizers_and_error_tables_bound_their_rows(lib):
     """One workgroup per row (or per 16 rows): row counts whose launch would
     pass 2^32 work-items are refused on the host before anything is launched."""
     FAKE = 1 << 20
-    assert lib.ddg_fp8_quantize_rows(FAKE, (1 << 24) - 1, 128, FAKE, FAKE, None) != E_SHAPE
+    # at the largest accepted count the shape check passes and the null output
+    # is refused next (E_ARG): nothing is launched, with or without a GPU
+    assert lib.ddg_fp8_quantize_rows(FAKE, (1 << 24) - 1, 128, None, FAKE, None) == E_ARG
     assert lib.ddg_fp8_quantize_rows(FAKE, 1 << 24, 128, FAKE, FAKE, None) == E_SHAPE
-    assert lib.ddg_fp6_quantize_rows(FAKE, (1 << 26) - 32, 128, 0, FAKE, FAKE, None) != E_SHAPE
+    assert lib.ddg_fp6_quantize_rows(FAKE, (1 << 26) - 32, 128, 0, None, FAKE, None) == E_ARG
     assert lib.ddg_fp6_quantize_rows(FAKE, (1 << 26) - 31, 128, 0, FAKE, FAKE, None) == E_SHAPE
-    assert lib.ddg_quant_sse(FAKE, 0, (1 << 24) - 1, 128, FAKE, FAKE, None) != E_SHAPE
+    assert lib.ddg_quant_sse(FAKE, 0, (1 << 24) - 1, 128, FAKE, None, None) == E_ARG
     assert lib.ddg_quant_sse(FAKE, 0, 1 << 24, 128, FAKE, FAKE, None) == E_SHAPE
 
 
