@@ -902,7 +902,9 @@ def workload_lines(api, synth, torch, steps, warmup):
       workload4_lowrank the rank-32 branch + 4-bit residual of a 3072x3072
                         weight at 4096 tokens: the fused call, and the residual's
                         product alone beside it (their difference is the branch:
-                        the T pre-pass and the epilogue term);
+                        the T pre-pass and the epilogue term), and the T pre-pass
+                        alone (ddg_lowrank_down; X rotated over >= 1 GiB of copies):
+                        GB/s of X, lora_down and T;
       workload5_m32760  the four Wan-14B block linears at their drawn widths,
                         32760 tokens (one by one and grouped): TFLOP/s;
       workload5_m16     the same at 16 tokens: packed-weight GB/s (one by one and
@@ -966,13 +968,23 @@ def workload_lines(api, synth, torch, steps, warmup):
     ms_f = burst(lambda i: api.lowrank_fused_gemm(x4, qs[i % len(qs)], lora_down, lora_up,
                                                   out=y4, workspace=wsp))
     ms_m = burst(lambda i: api.dequant_gemm(x4, qs[i % len(qs)], out=y4))
+    # the T pre-pass alone (ddg_lowrank_down), over copies of X totalling
+    # >= 1 GiB so that every launch reads X from HBM: HBM-bound, X's bytes
+    xs4 = [x4] + [x4.clone() for _ in range(max(1, -(-ROTATE_BYTES // (x4.numel() * 2)) - 1))]
+    t4 = torch.empty((4096, 32), dtype=torch.bfloat16, device=dev)
+    ms_t = burst(lambda i: api.lowrank_down(xs4[i % len(xs4)], lora_down, out=t4))
+    t_bytes = x4.numel() * 2 + lora_down.numel() * 2 + t4.numel() * 2
     fl_lr = 2.0 * 4096 * 32 * (3072 + 3072)
     out["workload4_lowrank_m4096"] = {
         "fused": dict(tflops(4096, 3072, 3072, ms_f),
                       TFLOPs_with_branch=round((2.0 * 4096 * 3072 * 3072 + fl_lr) / (ms_f * 1e-3) / 1e12, 1)),
         "residual_product_alone": tflops(4096, 3072, 3072, ms_m),
-        "branch_us": round((ms_f - ms_m) * 1e3, 2), "rank": 32}
-    del qs, q0, w4, resid, x4, y4, wsp
+        "branch_us": round((ms_f - ms_m) * 1e3, 2), "rank": 32,
+        "t_prepass_alone": {"us": round(ms_t * 1e3, 2),
+                            "GBps": round(t_bytes / (ms_t * 1e-3) / 1e9, 1),
+                            "frac_of_hbm_peak": round(t_bytes / (ms_t * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                            "x_copies_rotated": len(xs4)}}
+    del qs, q0, w4, resid, x4, y4, wsp, xs4, t4
     torch.cuda.empty_cache()
 
     # workload 5: the block's linears at their drawn widths

@@ -50,6 +50,7 @@ SIGNATURES = {
                                  ctypes.POINTER(_c_int), _c_int, ctypes.c_double,
                                  ctypes.POINTER(ctypes.c_double), _c_int, _c_int,
                                  ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_double)]),
+    "ddg_lowrank_down": (_c_int, [_vp, _c_i64, _c_i64, _vp, _c_int, _vp, _vp]),
     "ddg_lowrank_fused_gemm": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
                                         _c_int, _vp, _c_int, _vp, _sz, _vp]),
     "ddg_lowrank_fused_gemm_noalloc": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _c_int, _c_i64, _vp, _vp,
@@ -412,6 +413,28 @@ def workspace_bytes(m: int, n: int, k: int, r: int) -> int:
     b = ctypes.c_size_t()
     _check(load_library().ddg_workspace_bytes(m, n, k, r, ctypes.byref(b)), "ddg_workspace_bytes")
     return b.value
+
+
+def lowrank_down(x: torch.Tensor, lora_down: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """T = bf16(X @ L1) alone (lora_down = L1^T, r x in, bf16): the pre-pass of
+    lowrank_fused_gemm.  x: (m x in) bf16 with in a multiple of 128."""
+    for t, name in ((x, "x"), (lora_down, "lora_down")):
+        _require_cuda(t, name)
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D bf16 tensor")
+    m, k = x.shape
+    r = lora_down.shape[0]
+    if lora_down.shape[1] != k:
+        raise ValueError("lora_down has the wrong input dimension")
+    if out is None:
+        out = torch.empty(m, r, dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (m, r) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (m x r) bf16 tensor")
+    _check(load_library().ddg_lowrank_down(x.data_ptr(), m, k, lora_down.data_ptr(), r,
+                                           out.data_ptr(), _stream_ptr(x.device)),
+           "ddg_lowrank_down")
+    return out
 
 
 def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,

@@ -13,6 +13,9 @@ namespace {
 
 constexpr int64_t kMaxDim = 2147483647;     // M, N fit a signed 32-bit int
 constexpr int64_t kMaxK = INT64_C(1) << 20; // per-tile buffer ranges stay below 4 GiB
+// The low-rank pre-pass gives 16 rows of X to each workgroup of 256 lanes, so
+// a launch stays below 2^32 work-items up to this many rows.
+constexpr int64_t kLowrankMaxM = (INT64_C(1) << 28) - 16;
 constexpr int kMaxDevices = 64;
 
 // Per-device facts cached on first use: 0 unknown, 1 gfx950, -1 other.
@@ -554,12 +557,24 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
   return DDG_OK;
 }
 
+int ddg_lowrank_down(const void* x, int64_t m, int64_t k, const void* lora_down, int r, void* t,
+                     hipStream_t stream) {
+  if (m < 0 || m > kLowrankMaxM || !k_ok(k) || k > kMaxK || !mul_ok(m, k)) return DDG_ERR_SHAPE;
+  if (r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  if (m == 0) return DDG_OK;
+  if (!x || !lora_down || !t) return DDG_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(lora_down, 16) || !aligned(t, 16)) return DDG_ERR_ALIGN;
+  return hip_status(ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
+                                          static_cast<const __bf16*>(lora_down),
+                                          static_cast<__bf16*>(t), (int)m, (int)k, r, stream));
+}
+
 int ddg_lowrank_fused_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                            const float* scales, int bits, int64_t n, const void* lora_down,
                            const void* lora_up, int r, void* y, int y_dtype, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
-  if (r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  if (r < 8 || r > 128 || r % 8 || m > kLowrankMaxM) return DDG_ERR_SHAPE;
   if (m == 0) return DDG_OK;
   if (!lora_down || !lora_up || !workspace) return DDG_ERR_ARG;
   if (!aligned(lora_down, 16) || !aligned(lora_up, 16) || !aligned(workspace, 16))
@@ -617,7 +632,7 @@ extern "C" int ddg_lowrank_fused_gemm_noalloc(const void* x, int64_t m, int64_t 
                                               const void* lora_up, int r, void* y, int y_dtype,
                                               hipStream_t stream) {
   if (int st = check_gemm(x, m, k, packed, scales, bits, n, y, y_dtype)) return st;
-  if (r < 8 || r > 128 || r % 8) return DDG_ERR_SHAPE;
+  if (r < 8 || r > 128 || r % 8 || m > kLowrankMaxM) return DDG_ERR_SHAPE;
   if (m == 0) return DDG_OK;
   if (!lora_down || !lora_up) return DDG_ERR_ARG;
   if (!aligned(lora_down, 16) || !aligned(lora_up, 16)) return DDG_ERR_ALIGN;

@@ -195,6 +195,27 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
 int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
 
 /*
+ * T = bf16(X * L1) on its own: the down projection of the 16-bit low-rank
+ * branch ([SVDQ] 技术原理详解: the branch is a product with the two factors
+ * of the SVD, kept in 16 bits).  ddg_lowrank_fused_gemm runs this same pre-pass
+ * into its workspace before its product.  This call is for callers that keep
+ * T, for example to check or time it.
+ *   x          device, M x K bf16, row-major
+ *   lora_down  device, r x K bf16 = L1^T (row j: the j-th input projection)
+ *   t          device, M x r bf16, row-major (output, fully overwritten; the
+ *              caller owns it)
+ * Each element is summed in float32 and rounded to bf16 once.
+ * Requirements: K a positive multiple of 128, at most 2^20; 8 <= r <= 128,
+ * r % 8 == 0; M at most 2^28 - 16 (16 rows per workgroup of 256 lanes keeps
+ * the launch below 2^32 work-items); x, lora_down and t 16-byte aligned.
+ * M == 0 is a no-op.
+ * Errors: DDG_ERR_SHAPE (M negative or above 2^28 - 16, K or r out of range),
+ * DDG_ERR_ARG (null pointer), DDG_ERR_ALIGN, DDG_ERR_HIP.
+ */
+int ddg_lowrank_down(const void* x, int64_t m, int64_t k, const void* lora_down, int r, void* t,
+                     hipStream_t stream);
+
+/*
  * Y = X * w_hat^T + T * L2 with T = bf16(X * L1)  ([SVDQ] 技术原理详解: a
  * 16-bit low-rank branch beside the quantized residual; the residual's record
  * is packed/scales).  The low-rank factors are passed in the layout of linear
@@ -208,7 +229,9 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
  *              required), then optionally the split-K area of
  *              ddg_dequant_gemm; ddg_workspace_bytes(M, N, K, r) bytes hold
  *              both.  Its contents are scratch (no initial state needed).
- * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0.
+ * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0, and
+ * M at most 2^28 - 16 (the T pre-pass gives 16 rows to each workgroup of
+ * 256 lanes, and a launch stays below 2^32 work-items).
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_WORKSPACE,
  * DDG_ERR_HIP.
  */

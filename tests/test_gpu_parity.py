@@ -510,6 +510,47 @@ def _lowrank_case(api, x, w, bits, r, rows=None, out=torch.float32):
     return check_product(y[rows], y_ref, out == torch.bfloat16)
 
 
+def _check_t(api, x, l1, what):
+    """T = bf16(X L1) from ddg_lowrank_down against the oracle's
+    bf16(fl32(X L1)) summed in float64.  The kernel sums the exact bf16
+    products in float32, so its sum is within (K - 1) 2^-24 sum|x l1| of the
+    exact one, and the two bf16 roundings can then land one bf16 step apart
+    (2^-7 of the value at most).  Every element is held to that bound, and at
+    least 99% must be equal bit for bit."""
+    t_ref = O.lowrank_t_ref(x, l1)
+    t = host(api.lowrank_down(dev_bf16(x), dev_bf16(np.ascontiguousarray(l1.T)))).astype(np.float64)
+    tr = t_ref.astype(np.float64)
+    absdot = np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(l1, np.float64))
+    bound = 2.0 ** -7 * np.maximum(np.abs(t), np.abs(tr)) + (x.shape[1] - 1) * 2.0 ** -24 * absdot
+    err = np.abs(t - tr)
+    assert np.all(err <= bound), f"{what}: T off by {np.max(err - bound):.3e} beyond the bound"
+    same = np.mean(t == tr)
+    assert same >= 0.99, f"{what}: only {same:.4f} of T equal to the oracle"
+    return same
+
+
+@pytest.mark.parametrize("m,k,r", [(1, 128, 8), (17, 640, 24), (100, 256, 128), (33, 1024, 40),
+                                   (300, 3072, 32)])
+def test_lowrank_down_small_shapes(gpu_lib, m, k, r):
+    """The pre-pass alone at ragged row counts (the last 16-row block partly
+    filled) and every rank class."""
+    _case(f"lowrank_down m={m} k={k} r={r}")
+    rng = np.random.default_rng(m * 131 + r)
+    x = O.bf16_rne(rng.standard_normal((m, k)).astype(np.float32))
+    l1 = O.bf16_rne((rng.standard_normal((k, r)) / np.sqrt(k)).astype(np.float32))
+    _check_t(gpu_lib, x, l1, f"m={m} k={k} r={r}")
+
+
+def test_lowrank_down_config4(gpu_lib):
+    """Workload 4's T at full size: X 4096 x 3072 with its outlier channels and
+    the rank-32 factor of the SVD split of its weight, every element."""
+    _case("lowrank_down workload 4 (4096 x 3072, r = 32)")
+    c = synth.config4()
+    l1, _, _ = O.svd_split(c["w"], 32)
+    same = _check_t(gpu_lib, c["x"], l1, "workload 4")
+    print(f"[case] workload 4 T equal to the oracle: {same:.5f}", flush=True)
+
+
 @pytest.mark.parametrize("r", [8, 16, 40, 64, 128])
 @pytest.mark.parametrize("m", [5, 16, 48, 100])
 def test_lowrank_small_shapes(gpu_lib, r, m):
