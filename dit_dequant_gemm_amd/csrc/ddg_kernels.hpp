@@ -1611,38 +1611,49 @@ struct GroupLargeArgs {
 // ---------------------------------------------------------------------------
 // K4: T = bf16(X * L1), with L1^T = lora_down (R x K) -- computed as
 // T^T = lora_down * X^T so both MFMA operands are contiguous 16-byte reads.
-// Workgroup = 4 waves over 16 token rows; waves split K in 32-wide steps;
-// the 4 partials are summed through LDS, then rounded to bf16 once.
+// Workgroup = 4 waves over RR blocks of 16 token rows; waves split K in
+// 32-wide steps; the 4 partials are summed through LDS in wave order, then
+// rounded to bf16 once.
 // ---------------------------------------------------------------------------
 constexpr int kLowrankWaves = 4;
 
-template <int RBLK>
+template <int RBLK, int RR>
 __global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_kernel(const __bf16* __restrict__ x,
                                                                        const __bf16* __restrict__ lora_down,
                                                                        __bf16* __restrict__ t, int m, int k,
                                                                        int r) {
+  // RR blocks of 16 token rows per workgroup: every lora_down fragment a wave
+  // loads feeds RR MFMAs, so lora_down (r x K, read whole by every workgroup)
+  // costs 1/RR of its bytes per token row
+  static_assert(RR * RBLK <= 8, "partial tiles in LDS: at most 32 KB");
   constexpr int NW = kLowrankWaves;
-  __shared__ f32x4 red[NW][RBLK][64];
+  __shared__ f32x4 red[NW][RR][RBLK][64];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int m0 = blockIdx.x * 16;
-  const int mrow = min(m0 + lr, m - 1);
-  const __bf16* xrow = x + (int64_t)mrow * k + 8 * lq;
-  f32x4 acc[RBLK];
+  const int m0 = blockIdx.x * 16 * RR;
+  const __bf16* xrow[RR];
 #pragma unroll
-  for (int j = 0; j < RBLK; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RR; ++i) xrow[i] = x + (int64_t)min(m0 + 16 * i + lr, m - 1) * k + 8 * lq;
+  f32x4 acc[RR][RBLK];
+#pragma unroll
+  for (int i = 0; i < RR; ++i)
+#pragma unroll
+    for (int j = 0; j < RBLK; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // U steps of this wave's K range per trip, their loads issued before the
-  // first MFMA (the loop is bound by load latency otherwise)
-  constexpr int U = RBLK <= 2 ? 8 : (RBLK <= 4 ? 4 : 2);
+  // first MFMA (the loop is bound by load latency otherwise); U by the loads
+  // of one step
+  constexpr int LPS = RR + RBLK;
+  constexpr int U = LPS <= 3 ? 8 : (LPS <= 5 ? 4 : 2);
   const int steps = (k - wave * 32 + 32 * NW - 1) / (32 * NW);
   int st = 0;
   for (; st + U <= steps; st += U) {
-    bf16x8 bv[U], av[U][RBLK];
+    bf16x8 bv[U][RR], av[U][RBLK];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k0 = wave * 32 + 32 * NW * (st + u);
-      bv[u] = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) bv[u][i] = *reinterpret_cast<const bf16x8*>(xrow[i] + k0);
 #pragma unroll
       for (int j = 0; j < RBLK; ++j) {
         const int rr = j * 16 + lr;
@@ -1652,39 +1663,51 @@ __global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_kernel(const __b
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < RBLK; ++j) acc[j] = mfma16x16x32(av[u][j], bv[u], acc[j]);
+      for (int i = 0; i < RR; ++i)
+#pragma unroll
+        for (int j = 0; j < RBLK; ++j) acc[i][j] = mfma16x16x32(av[u][j], bv[u][i], acc[i][j]);
   }
   for (; st < steps; ++st) {
     const int k0 = wave * 32 + 32 * NW * st;
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow + k0);
+    bf16x8 b[RR];
+#pragma unroll
+    for (int i = 0; i < RR; ++i) b[i] = *reinterpret_cast<const bf16x8*>(xrow[i] + k0);
 #pragma unroll
     for (int j = 0; j < RBLK; ++j) {
       const int rr = j * 16 + lr;
       const bf16x8 a = load_bf16x8_or_zero(lora_down + (int64_t)min(rr, r - 1) * k + k0 + 8 * lq,
                                            rr < r);
-      acc[j] = mfma16x16x32(a, b, acc[j]);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) acc[i][j] = mfma16x16x32(a, b[i], acc[i][j]);
     }
   }
 #pragma unroll
-  for (int j = 0; j < RBLK; ++j) red[wave][j][lane] = acc[j];
+  for (int i = 0; i < RR; ++i)
+#pragma unroll
+    for (int j = 0; j < RBLK; ++j) red[wave][i][j][lane] = acc[i][j];
   __syncthreads();
-  if (wave == 0) {
-    const int mm = m0 + lr;
+  // wave i (< RR) sums and stores row block i, the partials in wave order
+  if (wave < RR) {
 #pragma unroll
-    for (int j = 0; j < RBLK; ++j) {
-      f32x4 s = red[0][j][lane];
+    for (int i = 0; i < RR; ++i) {
+      if (i != wave) continue;
+      const int mm = m0 + 16 * i + lr;
 #pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        const f32x4 v = red[w][j][lane];
-        s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
-      }
-      const int rr = j * 16 + 4 * lq;      // rows rr..rr+3 of T^T = columns of T
-      if (mm < m && rr < r) {
-        // r % 8 == 0 and rr % 4 == 0, so rr < r implies rr + 3 < r
-        uint32_t lo = pack_bf16x2(s[0], s[1]);
-        uint32_t hi = pack_bf16x2(s[2], s[3]);
-        u32x2 v = {lo, hi};
-        *reinterpret_cast<u32x2*>(t + (int64_t)mm * r + rr) = v;
+      for (int j = 0; j < RBLK; ++j) {
+        f32x4 s = red[0][i][j][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          const f32x4 v = red[w][i][j][lane];
+          s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+        }
+        const int rr = j * 16 + 4 * lq;      // rows rr..rr+3 of T^T = columns of T
+        if (mm < m && rr < r) {
+          // r % 8 == 0 and rr % 4 == 0, so rr < r implies rr + 3 < r
+          uint32_t lo = pack_bf16x2(s[0], s[1]);
+          uint32_t hi = pack_bf16x2(s[2], s[3]);
+          u32x2 v = {lo, hi};
+          *reinterpret_cast<u32x2*>(t + (int64_t)mm * r + rr) = v;
+        }
       }
     }
   }

@@ -530,10 +530,13 @@ def _check_t(api, x, l1, what):
 
 
 @pytest.mark.parametrize("m,k,r", [(1, 128, 8), (17, 640, 24), (100, 256, 128), (33, 1024, 40),
-                                   (300, 3072, 32)])
+                                   (300, 3072, 32),
+                                   (16400, 256, 48),     # two row blocks per workgroup
+                                   (32790, 128, 32)])    # four, the last workgroup 22 rows
 def test_lowrank_down_small_shapes(gpu_lib, m, k, r):
     """The pre-pass alone at ragged row counts (the last 16-row block partly
-    filled) and every rank class."""
+    filled), every rank class, and the grids that give a workgroup two or
+    four row blocks."""
     _case(f"lowrank_down m={m} k={k} r={r}")
     rng = np.random.default_rng(m * 131 + r)
     x = O.bf16_rne(rng.standard_normal((m, k)).astype(np.float32))
