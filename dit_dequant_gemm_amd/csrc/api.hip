@@ -319,14 +319,35 @@ hipError_t launch_product(ddg::GemmArgs& a, int bits, hipStream_t stream, Scratc
 // Bytes of the low-rank intermediate T (M x r bf16), rounded up to 256.
 size_t lowrank_t_bytes(int64_t m, int r) { return (size_t)((m * r * 2 + 255) / 256 * 256); }
 
+// Float32 partials of the pre-pass split over K (at most 64 rows, at least 8
+// groups; chunks x M x r floats), rounded up to 256; 0 where it does not split.
+size_t lowrank_part_bytes(int64_t m, int64_t k, int r) {
+  if (m <= 0 || m > 64 || k / DDG_GROUP < 8 || r <= 0) return 0;
+  int gpc = 1;
+  const int chunks = ddg::lowrank_split_chunks((int)k, &gpc);
+  return align256((size_t)chunks * (size_t)m * (size_t)r * 4);
+}
+
 // T = bf16(X L1) into t, then the product with the branch in its epilogue.
+// The scratch sk (after T) holds the product's split-K area first; where room
+// is left after it for the pre-pass's partials, the pre-pass splits K over
+// workgroups (they are read before the product starts, in stream order).
 hipError_t launch_lowrank(const void* x, int64_t m, int64_t k, const uint8_t* packed, const float* scales,
                           int bits, int64_t n, const void* lora_down, const void* lora_up, int r, void* y,
                           int y_dtype, __bf16* t, hipStream_t stream, Scratch sk = {}, int cus = 0) {
-  if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
-                                           static_cast<const __bf16*>(lora_down), t, (int)m,
-                                           (int)k, r, stream))
+  const size_t split_area = std::max(streamk_bytes(m, n), small_split_bytes(m, n, k));
+  const size_t part_bytes = lowrank_part_bytes(m, k, r);
+  if (part_bytes > 0 && sk.p != nullptr && sk.bytes >= split_area + part_bytes) {
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(sk.p) + split_area);
+    if (hipError_t e = ddg::launch_lowrank_t_split(static_cast<const __bf16*>(x),
+                                                   static_cast<const __bf16*>(lora_down), t, part,
+                                                   (int)m, (int)k, r, stream))
+      return e;
+  } else if (hipError_t e = ddg::launch_lowrank_t(static_cast<const __bf16*>(x),
+                                                  static_cast<const __bf16*>(lora_down), t, (int)m,
+                                                  (int)k, r, stream)) {
     return e;
+  }
   ddg::GemmArgs a{};
   a.x = static_cast<const __bf16*>(x);
   a.packed = packed;
@@ -553,7 +574,8 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes) {
   if (!bytes) return DDG_ERR_ARG;
   if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || k < 0 || (r != 0 && (r < 8 || r > 128 || r % 8)))
     return DDG_ERR_SHAPE;
-  *bytes = (r ? lowrank_t_bytes(m, r) : 0) + std::max(streamk_bytes(m, n), small_split_bytes(m, n, k));
+  *bytes = (r ? lowrank_t_bytes(m, r) + lowrank_part_bytes(m, k, r) : 0) +
+           std::max(streamk_bytes(m, n), small_split_bytes(m, n, k));
   return DDG_OK;
 }
 

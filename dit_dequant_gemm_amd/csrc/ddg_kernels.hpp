@@ -1713,4 +1713,97 @@ __global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_kernel(const __b
   }
 }
 
+// ---------------------------------------------------------------------------
+// The pre-pass for few token rows, K split over workgroups.  With one
+// workgroup per 16 rows, 16 tokens leave the whole pre-pass to one compute
+// unit, which cannot keep enough misses in flight to read lora_down quickly.
+// Workgroup (b, c) sums row block b over K chunk c (gpc whole groups) as the
+// kernel above does and writes its float32 partial tile to part[c][row][j];
+// lowrank_t_reduce_kernel then adds the chunks in chunk order and rounds to
+// bf16 once, so the result repeats bit for bit.
+// ---------------------------------------------------------------------------
+template <int RBLK>
+__global__ __launch_bounds__(64 * kLowrankWaves) void lowrank_t_part_kernel(const __bf16* __restrict__ x,
+                                                                            const __bf16* __restrict__ lora_down,
+                                                                            float* __restrict__ part, int m,
+                                                                            int k, int r, int gpc) {
+  constexpr int NW = kLowrankWaves;
+  __shared__ f32x4 red[NW][RBLK][64];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int c = blockIdx.y;
+  const int kb = c * gpc * kGroup;                      // chunk start (< k)
+  const int kl = min(gpc * kGroup, k - kb);             // chunk length, whole groups
+  const __bf16* xrow = x + (int64_t)min(m0 + lr, m - 1) * k + kb + 8 * lq;
+  const __bf16* lrow[RBLK];
+#pragma unroll
+  for (int j = 0; j < RBLK; ++j) lrow[j] = lora_down + (int64_t)min(j * 16 + lr, r - 1) * k + kb + 8 * lq;
+  f32x4 acc[RBLK];
+#pragma unroll
+  for (int j = 0; j < RBLK; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;                                  // steps per batch of loads
+  const int steps = (kl - wave * 32 + 32 * NW - 1) / (32 * NW);
+  int st = 0;
+  for (; st + U <= steps; st += U) {
+    bf16x8 bv[U], av[U][RBLK];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = wave * 32 + 32 * NW * (st + u);
+      bv[u] = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+      for (int j = 0; j < RBLK; ++j) av[u][j] = load_bf16x8_or_zero(lrow[j] + k0, j * 16 + lr < r);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < RBLK; ++j) acc[j] = mfma16x16x32(av[u][j], bv[u], acc[j]);
+  }
+  for (; st < steps; ++st) {
+    const int k0 = wave * 32 + 32 * NW * st;
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+    for (int j = 0; j < RBLK; ++j)
+      acc[j] = mfma16x16x32(load_bf16x8_or_zero(lrow[j] + k0, j * 16 + lr < r), b, acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < RBLK; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  if (wave == 0) {
+    const int mm = m0 + lr;
+#pragma unroll
+    for (int j = 0; j < RBLK; ++j) {
+      f32x4 s = red[0][j][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const f32x4 v = red[w][j][lane];
+        s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+      }
+      const int rr = j * 16 + 4 * lq;
+      if (mm < m && rr < r)
+        *reinterpret_cast<f32x4*>(part + ((int64_t)c * m + mm) * r + rr) = s;
+    }
+  }
+}
+
+// T[i] = bf16(sum over chunks c in order of part[c][i]), four outputs a lane.
+// (A template, as every kernel of this header, so that the units that
+// include it share one definition.)
+template <int V = 0>
+__global__ __launch_bounds__(256) void lowrank_t_reduce_kernel(const float* __restrict__ part,
+                                                               __bf16* __restrict__ t, int m, int r,
+                                                               int chunks) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = (int64_t)m * r / 4;
+  if (q >= n4) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + 4 * q);
+  for (int c = 1; c < chunks; ++c) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)c * m * r + 4 * q);
+    s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+  }
+  u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  *reinterpret_cast<u32x2*>(t + 4 * q) = o;
+}
+
 }  // namespace ddg

@@ -98,5 +98,11 @@ hipError_t launch_w6a8_gemm(const W4A8Args& a, int fmt6, bool pow2, hipStream_t 
 
 hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t, int m, int k,
                             int r, hipStream_t stream);
+// K chunks of the split pre-pass for k inputs (whole groups, at most 32
+// chunks): gpc groups per chunk; returns the chunk count.
+int lowrank_split_chunks(int k, int* gpc);
+// The split pre-pass: float32 partials (chunks x m x r) in part, then T.
+hipError_t launch_lowrank_t_split(const __bf16* x, const __bf16* lora_down, __bf16* t, float* part,
+                                  int m, int k, int r, hipStream_t stream);
 
 }  // namespace ddg

@@ -56,4 +56,42 @@ hipError_t launch_lowrank_t(const __bf16* x, const __bf16* lora_down, __bf16* t,
   }
 }
 
+int lowrank_split_chunks(int k, int* gpc) {
+  const int g = k / kGroup;
+  *gpc = (g + 31) / 32;
+  return (g + *gpc - 1) / *gpc;
+}
+
+namespace {
+template <int RBLK>
+hipError_t launch_part(const __bf16* x, const __bf16* lora_down, float* part, int m, int k, int r,
+                       int gpc, int chunks, hipStream_t stream) {
+  const dim3 grid((unsigned)((m + 15) / 16), (unsigned)chunks), block(64 * kLowrankWaves);
+  lowrank_t_part_kernel<RBLK><<<grid, block, 0, stream>>>(x, lora_down, part, m, k, r, gpc);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_lowrank_t_split(const __bf16* x, const __bf16* lora_down, __bf16* t, float* part,
+                                  int m, int k, int r, hipStream_t stream) {
+  int gpc = 1;
+  const int chunks = lowrank_split_chunks(k, &gpc);
+  hipError_t e = hipErrorInvalidValue;
+  switch ((r + 15) / 16) {
+    case 1: e = launch_part<1>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 2: e = launch_part<2>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 3: e = launch_part<3>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 4: e = launch_part<4>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 5: e = launch_part<5>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 6: e = launch_part<6>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 7: e = launch_part<7>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    case 8: e = launch_part<8>(x, lora_down, part, m, k, r, gpc, chunks, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t n4 = (int64_t)m * r / 4;
+  lowrank_t_reduce_kernel<0><<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(part, t, m, r, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace ddg

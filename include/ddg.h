@@ -187,7 +187,10 @@ int ddg_dequant_gemm_grouped(const ddg_gemm_desc* descs, int count, hipStream_t 
  * 256 x 256; M <= 16, K >= 8192, N < 12800: 8 KiB of partial sums and 64
  * bytes of flags per 16 output columns, padded to 64 columns; else 0); with
  * rank r, what ddg_lowrank_fused_gemm needs: the M x r bf16 intermediate T,
- * rounded up to 256 bytes, followed by that split-K area.
+ * rounded up to 256 bytes, followed by that split-K area and, for M <= 64
+ * and K >= 1024, the float32 partials of the T pre-pass split over K
+ * (ceil(G / c) chunks of c = ceil(G / 32) groups, G = K / 128, times M x r
+ * floats, rounded up to 256).
  * Host-only.
  * Errors: DDG_ERR_ARG (null), DDG_ERR_SHAPE (m, n or k negative or m, n above
  * 2^31 - 1, r not 0 and outside 8..128 or not a multiple of 8).
@@ -227,8 +230,13 @@ int ddg_lowrank_down(const void* x, int64_t m, int64_t k, const void* lora_down,
  * accumulator as the main product before y is written.
  *   workspace  device scratch: T first (M * r * 2 bytes rounded up to 256,
  *              required), then optionally the split-K area of
- *              ddg_dequant_gemm; ddg_workspace_bytes(M, N, K, r) bytes hold
- *              both.  Its contents are scratch (no initial state needed).
+ *              ddg_dequant_gemm and, for M <= 64 and K >= 1024, the T
+ *              pre-pass's partials; ddg_workspace_bytes(M, N, K, r) bytes
+ *              hold all three.  With room for the partials, the pre-pass
+ *              splits K over workgroups and adds the partials in a fixed
+ *              order (T may then differ from the unsplit pre-pass's in the
+ *              last bf16 place; either way it repeats bit for bit).  Its
+ *              contents are scratch (no initial state needed).
  * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0, and
  * M at most 2^28 - 16 (the T pre-pass gives 16 rows to each workgroup of
  * 256 lanes, and a launch stays below 2^32 work-items).

@@ -91,7 +91,19 @@ def test_workspace_bytes(lib):
     split16 = lambda n: 8 * 1024 * ((n // 16 + 3) // 4 * 4) + -(-8 * 8 * ((n // 16 + 3) // 4 * 4) // 256) * 256
     assert lib.ddg_workspace_bytes(16, 5120, 13824, 0, ctypes.byref(b)) == OK and b.value == split16(5120) == 2641920
     assert lib.ddg_workspace_bytes(1, 1040, 8192, 0, ctypes.byref(b)) == OK and b.value == split16(1040)
-    assert lib.ddg_workspace_bytes(16, 5120, 13824, 32, ctypes.byref(b)) == OK and b.value == 1024 + split16(5120)
+    # with a rank, at most 64 rows and at least 8 groups: the pre-pass's float32
+    # partials after the split-K area (chunks of ceil(G / 32) groups)
+    def part(m, k, r):
+        g = k // 128
+        gpc = -(-g // 32)
+        return -(-(-(-g // gpc) * m * r * 4) // 256) * 256 if m <= 64 and g >= 8 else 0
+    assert part(16, 13824, 32) == 27 * 16 * 32 * 4 and part(16, 5120, 32) == 20 * 16 * 32 * 4
+    assert lib.ddg_workspace_bytes(16, 5120, 13824, 32, ctypes.byref(b)) == OK and \
+        b.value == 1024 + split16(5120) + part(16, 13824, 32)
+    assert lib.ddg_workspace_bytes(16, 5120, 5120, 32, ctypes.byref(b)) == OK and b.value == 1024 + part(16, 5120, 32)
+    assert lib.ddg_workspace_bytes(64, 3072, 1024, 8, ctypes.byref(b)) == OK and b.value == 1024 + 8 * 64 * 8 * 4
+    assert lib.ddg_workspace_bytes(16, 5120, 896, 32, ctypes.byref(b)) == OK and b.value == 1024     # 7 groups
+    assert lib.ddg_workspace_bytes(65, 3072, 3072, 32, ctypes.byref(b)) == OK and b.value == 4352 + sk
     assert lib.ddg_workspace_bytes(16, 5120, 5120, 0, ctypes.byref(b)) == OK and b.value == 0       # K < 8192
     assert lib.ddg_workspace_bytes(16, 12800, 8192, 0, ctypes.byref(b)) == OK and b.value == 0      # skinny kernel
     assert lib.ddg_workspace_bytes(17, 5120, 13824, 0, ctypes.byref(b)) == OK and b.value == 0      # M > 16

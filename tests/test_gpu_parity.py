@@ -570,6 +570,38 @@ def test_lowrank_wide_small_m(gpu_lib):
     _lowrank_case(gpu_lib, c["x"][:3], c["w"], 4, 32, out=torch.bfloat16)
 
 
+@pytest.mark.parametrize("m,n,k,r", [(1, 272, 1024, 8), (16, 272, 5120, 32), (37, 144, 13824, 128),
+                                     (64, 272, 3072, 40), (16, 5120, 13824, 32)])
+def test_lowrank_split_prepass(gpu_lib, m, n, k, r):
+    """At most 64 token rows and at least 8 groups, with the workspace
+    ddg_workspace_bytes asks for: the pre-pass splits K over workgroups
+    (float32 partials after the product's own split-K area, added in chunk
+    order).  T (the workspace's first bytes) against the oracle's T, Y against
+    the oracle, and two calls equal bit for bit."""
+    _case(f"lowrank_fused_gemm split pre-pass m={m} n={n} k={k} r={r}")
+    c = synth.random_case(7000 + m + r, m, n, k, wstd=0.05)
+    l1, l2, res = O.svd_split(c["w"], r)
+    qr = gpu_lib.quantize_pack(torch.from_numpy(res).to("cuda"), 4)
+    w16 = O.dequant_bf16(*O.quantize_groups(res, 4), 4)
+    ld = dev_bf16(np.ascontiguousarray(l1.T))
+    lu = dev_bf16(np.ascontiguousarray(l2.T))
+    ws = torch.empty(gpu_lib.workspace_bytes(m, n, k, r), dtype=torch.uint8, device="cuda")
+    x = dev_bf16(c["x"])
+    y1 = host(gpu_lib.lowrank_fused_gemm(x, qr, ld, lu, torch.float32, workspace=ws))
+    t = ws[:m * r * 2].view(torch.bfloat16).view(m, r).float().cpu().numpy().astype(np.float64)
+    t_ref = O.lowrank_t_ref(c["x"], l1).astype(np.float64)
+    absdot = np.abs(np.asarray(c["x"], np.float64)) @ np.abs(np.asarray(l1, np.float64))
+    bound = 2.0 ** -7 * np.maximum(np.abs(t), np.abs(t_ref)) + (k - 1) * 2.0 ** -24 * absdot
+    assert np.all(np.abs(t - t_ref) <= bound), "T beyond the float32 summation bound"
+    assert np.mean(t == t_ref) >= 0.99, "T: fewer than 99% equal to the oracle"
+    y2 = host(gpu_lib.lowrank_fused_gemm(x, qr, ld, lu, torch.float32, workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "split pre-pass results differ between calls"
+    y_ref, _ = O.lowrank_fused_ref(c["x"], w16, l1, l2)
+    check_product(y1, y_ref, False, "split pre-pass f32")
+    yb = host(gpu_lib.lowrank_fused_gemm(x, qr, ld, lu, torch.bfloat16, workspace=ws))
+    check_product(yb, y_ref, True, "split pre-pass bf16")
+
+
 def test_lowrank_config4(gpu_lib):
     _case("lowrank_fused_gemm workload 4 (M=4096, r=32)")
     c = synth.config4()
