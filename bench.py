@@ -131,6 +131,40 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 3}), flush=True)
 
 
+def _steady_ms(torch, stream, fn, steps, warmup):
+    """Average duration of back-to-back calls fn(i), with i a running call
+    index (the suites that rotate weight copies pick copy i):
+    `warmup` calls, then more warm-up calls of the same products until 100 ms
+    of them have run (the first launches after set-up run slower while the
+    clock settles), then at least `steps` calls, or BURST_MIN_MS of them,
+    between two HIP events on `stream`.  Returns (ms per call, calls timed)."""
+    i = 0
+    for _ in range(warmup):
+        fn(i)
+        i += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < 0.1 or n < 3:
+        fn(i)
+        i += 1
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - t0) * 1e3 / n
+    count = max(steps, int(BURST_MIN_MS / max(one_ms, 1e-3)))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(count):
+        fn(i)
+        i += 1
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / count, count
+
+
 def block_suite(tokens, steps, warmup):
     """The four linears of one DiT block (Wan-14B shapes, drawn widths) at
     `tokens` > 64 tokens: each product alone, the four one by one, and the four
@@ -151,25 +185,16 @@ def block_suite(tokens, steps, warmup):
         lins.append({"name": name, "qw": qw, "x": x, "y": y})
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return _steady_ms(torch, stream, lambda i: fn(), steps, warmup)
 
-    def line(name, ls, ms):
+    def line(name, ls, timing):
+        ms, count = timing
         flops = sum(2.0 * tokens * L["qw"].n * L["qw"].k for L in ls)
         tf = flops / (ms * 1e-3) / 1e12
         print(json.dumps({"suite": "dit-block", "tokens": tokens, "linear": name,
                           "shapes": [f"{L['qw'].n}x{L['qw'].k}@{L['qw'].bits}b" for L in ls],
                           "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                          "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": steps}),
+                          "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": count}),
               flush=True)
 
     for L in lins:
@@ -182,7 +207,8 @@ def block_suite(tokens, steps, warmup):
 
 def block16_suite(steps, warmup):
     """The four linears of one DiT block at M = 16 tokens: packed-weight GB/s
-    of each product (K back-to-back launches over >= 1 GiB of weight copies),
+    of each product (at least K back-to-back launches, or 200 ms of them, after
+    100 ms of warm-up launches, over >= 1 GiB of weight copies),
     then the same four as one grouped call, and q, k, v as three 5120x5120
     tensors of different widths, one by one and grouped."""
     import torch
@@ -192,17 +218,7 @@ def block16_suite(steps, warmup):
     stream = torch.cuda.current_stream()
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            fn(warmup + i)
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return _steady_ms(torch, stream, fn, steps, warmup)[0]
 
     def resident(w_np, x_np, bits):
         """Weight copies totalling >= 1 GiB, X, Y for one linear."""
@@ -269,17 +285,7 @@ def shard_suite(ways, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            fn(warmup + i)
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return _steady_ms(torch, stream, fn, steps, warmup)[0]
 
     bits_of = synth.config5_bits()
     shares = {}
