@@ -200,9 +200,11 @@ int ddg_workspace_bytes(int64_t m, int64_t n, int64_t k, int r, size_t* bytes);
 /*
  * T = bf16(X * L1) on its own: the down projection of the 16-bit low-rank
  * branch ([SVDQ] 技术原理详解: the branch is a product with the two factors
- * of the SVD, kept in 16 bits).  ddg_lowrank_fused_gemm runs this same pre-pass
- * into its workspace before its product.  This call is for callers that keep
- * T, for example to check or time it.
+ * of the SVD, kept in 16 bits).  ddg_lowrank_fused_gemm runs this pre-pass
+ * into its workspace before its product (for M <= 64, given room for its
+ * partials, the same sums split over K, which may differ in the last bf16
+ * place).  This call is for callers that keep T, for example to check or
+ * time it.
  *   x          device, M x K bf16, row-major
  *   lora_down  device, r x K bf16 = L1^T (row j: the j-th input projection)
  *   t          device, M x r bf16, row-major (output, fully overwritten; the
