@@ -363,17 +363,28 @@ def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> Optiona
     return ws
 
 
+def _capturing() -> bool:
+    """True while the current stream is being captured into a graph."""
+    return torch.cuda.is_current_stream_capturing()
+
+
 def dequant_gemm(x: torch.Tensor, qw: QWeight, out_dtype=torch.bfloat16,
                  out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = X @ w_hat^T with on-the-fly dequantization.  workspace: optional
     scratch (uint8, at least workspace_bytes(m, n, k, 0) bytes) for the
-    stream-K form of products with few output tiles; by default one kept per
-    device and stream is used."""
+    split-K and stream-K forms; by default one kept per device and stream is
+    used.  Under graph capture no workspace is used (whole tiles): a call that
+    splits K tags its partial sums with a launch epoch that every replay of a
+    graph would repeat, so replays could read an earlier replay's sums; a
+    workspace passed under capture raises ValueError."""
     x = _prep_x(x, qw)
     y = _out(x, qw.n, out_dtype, out)
     sp = _stream_ptr(x.device)
-    if workspace is None:
+    if _capturing():
+        if workspace is not None:
+            raise ValueError("dequant_gemm: no workspace under graph capture (split K is launch-specific)")
+    elif workspace is None:
         workspace = _cached_workspace(x.device, sp, workspace_bytes(x.shape[0], qw.n, qw.k, 0))
     wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _check(load_library().ddg_dequant_gemm(
@@ -442,7 +453,9 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
                        out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = X @ w_hat^T + bf16(X @ L1) @ L2 with lora_down = L1^T (r x in) and
-    lora_up = L2^T (out x r), both bf16."""
+    lora_up = L2^T (out x r), both bf16.  Under graph capture only T's bytes
+    of the workspace are handed over (whole tiles, unsplit pre-pass: see
+    dequant_gemm)."""
     x = _prep_x(x, qw)
     for t, name in ((lora_down, "lora_down"), (lora_up, "lora_up")):
         _require_cuda(t, name)
@@ -459,11 +472,16 @@ def lowrank_fused_gemm(x: torch.Tensor, qw: QWeight, lora_down: torch.Tensor,
     need = workspace_bytes(x.shape[0], qw.n, qw.k, r)
     if workspace is None:
         workspace = _cached_workspace(x.device, _stream_ptr(x.device), max(need, 256))
+    wbytes = workspace.numel() * workspace.element_size()
+    if _capturing():
+        # T's bytes alone: whole tiles and the unsplit pre-pass, nothing that
+        # depends on the launch (see dequant_gemm)
+        wbytes = min(wbytes, -(-x.shape[0] * r * 2 // 256) * 256)
     _check(load_library().ddg_lowrank_fused_gemm(
         x.data_ptr(), x.shape[0], qw.k, qw.packed.data_ptr(), qw.scales.data_ptr(), qw.bits,
         qw.n, lora_down.data_ptr(), lora_up.data_ptr(), r, y.data_ptr(),
         DDG_F32 if y.dtype == torch.float32 else DDG_BF16, workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream_ptr(x.device)),
+        wbytes, _stream_ptr(x.device)),
         "ddg_lowrank_fused_gemm")
     return y
 

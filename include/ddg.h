@@ -136,6 +136,10 @@ int ddg_dequantize(const uint8_t* packed, const float* scales, int bits, int64_t
  *           calls that share a workspace must be ordered (one stream).
  *           Results then differ from the call without workspace only in
  *           float32 summation order (the same on every call).
+ *           Graph capture: the exchange is tagged with an epoch that the
+ *           host draws per call, so a captured call that splits K would
+ *           repeat its epoch on every replay and could read an earlier
+ *           replay's partial sums.  Under capture, pass no workspace.
  * Requirements: M >= 0 (M == 0 is a no-op), N a positive multiple of 16,
  * K a positive multiple of 128 and at most 2^20, M, N <= 2^31 - 1.
  * Errors: DDG_ERR_ARG, DDG_ERR_SHAPE, DDG_ERR_ALIGN, DDG_ERR_HIP.
@@ -238,7 +242,10 @@ int ddg_lowrank_down(const void* x, int64_t m, int64_t k, const void* lora_down,
  *              splits K over workgroups and adds the partials in a fixed
  *              order (T may then differ from the unsplit pre-pass's in the
  *              last bf16 place; either way it repeats bit for bit).  Its
- *              contents are scratch (no initial state needed).
+ *              contents are scratch (no initial state needed).  Under graph
+ *              capture, pass a workspace of T's bytes alone (whole tiles and
+ *              the unsplit pre-pass; see ddg_dequant_gemm), or call
+ *              ddg_lowrank_fused_gemm_noalloc.
  * Requirements: as ddg_dequant_gemm, plus 8 <= r <= 128, r % 8 == 0, and
  * M at most 2^28 - 16 (the T pre-pass gives 16 rows to each workgroup of
  * 256 lanes, and a launch stays below 2^32 work-items).
