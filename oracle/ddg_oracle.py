@@ -30,7 +30,7 @@ Sources (cited by title and section only):
   - section "技术原理详解": a 16-bit low-rank branch takes the outliers, the
     residual is quantized to 4 bit.
 
-Readings where the pages are silent or garbled (each is repeated in the design doc):
+Readings where the pages are silent or garbled:
 
 R1  n_half = 2^(bits-1) - 1 (the clamp bound, also the unsigned offset).
 R2  All arithmetic of the quantizer is IEEE float32: abs-max (exact),

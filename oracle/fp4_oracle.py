@@ -13,7 +13,7 @@ Source: [FP4] the FP4DiT article (aijishu.com).
   - §3.2.3 / §4.1: per-token online min-max activation quantization to 8 bits
     (W4A8) and 6 bits (W4A6); §3.3: FP6 saves memory over FP8.
 
-Readings where the article is silent (each is repeated in the design doc):
+Readings where the article is silent:
 
 R18  The 4-bit formats are sign + magnitude minifloats, subnormal when the
      exponent field is 0: E2M1 bias 1 (0, .5, 1, 1.5, 2, 3, 4, 6), E1M2 bias 1

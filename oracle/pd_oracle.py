@@ -14,7 +14,7 @@ that blends each tensor's error table, a Lagrange term plus a quadratic
 penalty 1e4 (bpw - target)^2 on the budget -- with random restarts, then
 rounding and keeping the best restart.  §4.4 and §4.6 report its results.
 
-Readings where the section is silent (each is repeated in the design doc):
+Readings where the section is silent:
 
 R7   Candidate widths are the packable ones, 3..7; b_min = 3, b_max = 7.
 R8   dist(b, c) = |b - c|; the soft weights are softmax_c(-|b - c| / temp),

@@ -13,7 +13,7 @@ Source: [ORQ] the OrbitQuant article (www.sumeiyu.com, news 221186).
     basis, W <- W Pi_d^T, and quantized; online every activation is rotated by
     Pi_d, so the rotations cancel inside the product.
 
-Readings where the section is silent (each is repeated in the design doc):
+Readings where the section is silent:
 
 R13  H_h is the Sylvester-ordered Walsh-Hadamard matrix of order h (a power of
      two), scaled by 1/sqrt(h) so that Pi_d is orthogonal (the variance 1/d of
